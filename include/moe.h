@@ -1,0 +1,228 @@
+/*
+ * moe.h -- C ABI of libmoe.so, a routed-expert MoE layer for AMD MI355X (gfx950).
+ *
+ * The layer (one call of moe_forward) computes, for T tokens x[T, H]:
+ *   1. top-k routing over E experts with renormalised softmax weights;
+ *   2. a stable expert permutation of the T*k (token, slot) pairs, each
+ *      expert's segment padded to a multiple of block_m rows;
+ *   3. dynamic activation quantisation (block FP8 1x128 or OCP MXFP4 1x32);
+ *   4. a grouped gate/up GEMM over separate gate and up halves of w13, fused
+ *      with the clamped SwiGLU silu(min(gate, L)) * clamp(up, -L, L) and the
+ *      re-quantisation of the intermediate;
+ *   5. a grouped down GEMM and the routing-weighted combine into bf16 out[T, H].
+ *
+ * Sources (page title and section):
+ *   - sglang PR #38546 "[AMD] [GLM-5.3-Flash Day 0] Enable FP8 and Quark MXFP4
+ *     MoE on gfx950": Summary (block FP8 [128,128] weights with dynamic FP8
+ *     activations; OCP MXFP4 1x32 weights and activations; gate and up loaded
+ *     as separate contiguous halves; clamped SwiGLU with swiglu_limit=10.0) and
+ *     the contract table (explicit gate mode, limit always forwarded,
+ *     preshuffle owned by the runner that consumes it, unsupported
+ *     configurations rejected at construction, hidden/intermediate padding
+ *     recorded and forwarded).
+ *   - FreeToken PR #270 "glm5_next: support GLM-5.3-Flash (hybrid KDA + DSA,
+ *     mHC, NVFP4 expert offload)": Summary (288-expert top-8 routing; the
+ *     clamped SwiGLU formula, an infinite limit giving plain SwiGLU; backends
+ *     that cannot apply the limit are rejected).
+ *
+ * Conventions for every entry point:
+ *   - Every pointer argument is DEVICE memory owned by the caller, except the
+ *     moe_cfg_t pointer, which is host memory read during the call only.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *     enqueued on it; no call synchronises, allocates device memory or reads
+ *     device memory back to the host, so moe_forward can be captured in a
+ *     HIP graph.  Scratch memory is caller-provided (moe_workspace_bytes).
+ *   - Every argument is validated before anything is enqueued: a call that
+ *     returns an error has launched nothing.  MOE_ERR_HIP reports a failed
+ *     launch; faults inside kernels surface at the caller's next sync.
+ *   - The library keeps no state; calls on different streams are independent
+ *     as long as their buffers do not overlap.
+ *   - T = 0 (no tokens) is valid and launches nothing.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  MOE_ERR_ALIGN = 3,       /* a padded size is not a multiple of 128 */
+  MOE_ERR_UNSUPPORTED = 4, /* quant mode, gate mode, block_m, limit or dtype not supported */
+  MOE_ERR_LAYOUT = 5,      /* weight layout tag is not the one this call consumes */
+  MOE_ERR_WORKSPACE = 6,   /* workspace smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = 7          /* a kernel launch failed */
+} moe_status_t;
+
+/* Weight/activation contracts (sglang PR #38546, Summary). */
+enum {
+  MOE_QUANT_FP8_BLOCK = 1, /* w: e4m3 + fp32 scale per [128,128] block; act: e4m3 + fp32 per 1x128 */
+  MOE_QUANT_MXFP4 = 2      /* w and act: E2M1 two per byte (low nibble = even index) + E8M0 per 1x32 */
+};
+
+/* Physical order of the gate and up projections inside w13.  Only separate
+ * contiguous halves (gate rows [0, Ip), up rows [Ip, 2Ip)) are accepted;
+ * interleaved is rejected with MOE_ERR_UNSUPPORTED (sglang PR #38546, contract
+ * table: gate mode is explicit, never inferred). */
+enum { MOE_GATE_SEPARATED = 0, MOE_GATE_INTERLEAVED = 1 };
+
+/* Weight layout tags.  CANONICAL is row-major [E, N, K] (what
+ * moe_quant_weights writes).  TILED_V1 is the GEMM kernels' layout, written
+ * only by moe_preshuffle_weights (the runner owns its preshuffle). */
+enum { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_TILED_V1 = 0x4D310001 };
+
+/* Element types accepted by moe_quant_act / moe_quant_weights. */
+enum { MOE_DTYPE_BF16 = 1, MOE_DTYPE_F32 = 2 };
+
+/* Hidden/intermediate padding metadata (sglang PR #38546, contract table:
+ * padding is recorded and forwarded).  `*_padded` must be multiples of 128 and
+ * not below the real size.  x and out have `hidden` columns; weights are
+ * stored padded with zeros: w13 [E, 2*inter_padded, hidden_padded] (each half
+ * padded separately) and w2 [E, hidden_padded, inter_padded]. */
+typedef struct {
+  int32_t hidden, hidden_padded, inter, inter_padded;
+} moe_pad_t;
+
+typedef struct {
+  int32_t num_experts;   /* E, 1..1024 */
+  int32_t top_k;         /* k, 1..min(16, E) */
+  int32_t quant_mode;    /* MOE_QUANT_* */
+  int32_t gate_mode;     /* must be MOE_GATE_SEPARATED */
+  int32_t weight_layout; /* must be MOE_LAYOUT_TILED_V1 for the GEMM entry points */
+  int32_t block_m;       /* rows per expert block: 16, 32, 64 or 128 */
+  float swiglu_limit;    /* L > 0; +inf gives plain SwiGLU; NaN rejected */
+  moe_pad_t pad;
+} moe_cfg_t;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status_t s);
+
+/* Validates a configuration without touching the GPU ("fails at
+ * construction, not later"). */
+moe_status_t moe_validate_cfg(const moe_cfg_t* cfg);
+
+/* Number of block_m-row blocks the padded permutation can need for
+ * num_pairs = T*k pairs: min(P, (P + E*(block_m-1)) / block_m).  Returns -1
+ * for invalid arguments. */
+int32_t moe_max_blocks(int32_t num_pairs, int32_t num_experts, int32_t block_m);
+
+/* Bytes of scratch that moe_forward needs for up to T_max tokens (0 if the
+ * configuration is invalid).  Also enough for moe_grouped_gemm2_combine. */
+size_t moe_workspace_bytes(const moe_cfg_t* cfg, int32_t T_max);
+
+/* Sizes in bytes of the intermediate aq / as buffers (rows = max_blocks *
+ * block_m; FP8: aq u8 [rows, Ip], as f32 [rows, Ip/128]; MXFP4: aq u8
+ * [rows, Ip/2], as u8 [rows, Ip/32]).  Returns MOE_ERR_* on a bad cfg. */
+moe_status_t moe_intermediate_bytes(const moe_cfg_t* cfg, int32_t T, size_t* aq_bytes,
+                                    size_t* as_bytes);
+
+/* Top-k routing (FreeToken PR #270, Summary: 288-expert top-8 routing).
+ * logits: f32 [T, E] row-major.  Selection is on the raw logits: descending
+ * value, ties to the lower expert id (-0.0 equals +0.0); slot j holds the j-th
+ * best.  weights[t, j] = exp(l_j - l_max) / sum over the k selected.
+ * Outputs: ids int32 [T, top_k], weights f32 [T, top_k].  NaN logits are not
+ * supported (the result is unspecified but in range). */
+moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t top_k,
+                            int32_t* ids, float* weights, void* stream);
+
+/* Stable counting sort of the P = T*top_k pairs (pair f = t*top_k + j) by
+ * expert ids[f].  With nb = moe_max_blocks(P, E, block_m):
+ *   sorted_ids   int32 [nb*block_m]: expert e's segment starts at
+ *                expert_offsets[e] and holds its pairs in increasing f, padded
+ *                with the sentinel P to a multiple of block_m; every entry past
+ *                the last segment is also P;
+ *   block_expert int32 [nb]: expert of each block, -1 past the last segment;
+ *   expert_offsets int32 [E+1]: exclusive scan of the padded segment sizes;
+ *   num_post_padded int32 [1]: expert_offsets[E], left on the device.
+ * Experts with no pairs get no block.  ids outside [0, E) are skipped. */
+moe_status_t moe_permute_align(const int32_t* ids, int32_t T, int32_t top_k, int32_t E,
+                               int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
+                               int32_t* expert_offsets, int32_t* num_post_padded,
+                               void* stream);
+
+/* Dynamic row quantisation (sglang PR #38546, Summary: dynamic FP8
+ * activations; OCP MXFP4 1x32).  in: `rows` rows of `cols` valid elements
+ * (bf16 or f32) with row stride ld_in elements; columns cols..cols_padded-1
+ * are taken as zero.  cols_padded % 128 == 0.
+ *   FP8:   q u8 [rows, cols_padded] e4m3; scales f32 [rows, cols_padded/128]:
+ *          s = amax/448 (fp32 division), q = RNE(clamp(v/s, +-448)); amax = 0
+ *          gives s = 0 and all-zero codes.
+ *   MXFP4: q u8 [rows, cols_padded/2]; scales u8 [rows, cols_padded/32]:
+ *          b = clamp(floor(log2 amax) - 2 + 127, 0, 254) (0 when amax = 0),
+ *          codes = RNE_E2M1(clamp(v / 2^(b-127), +-6)).
+ * Signs of zero are kept.  Results are bit-exact by definition. */
+moe_status_t moe_quant_act(const void* in, int32_t in_dtype, int32_t rows, int32_t cols,
+                           int64_t ld_in, int32_t cols_padded, int32_t quant_mode, void* q,
+                           void* scales, void* stream);
+
+/* Offline weight quantisation into the CANONICAL layout.  w: f32 [E, N, K]
+ * row-major (already zero-padded).
+ *   FP8:   N % 128 == 0, K % 128 == 0; q u8 [E, N, K]; scales f32
+ *          [E, N/128, K/128] (dequant multipliers), one per [128,128] block,
+ *          same arithmetic as moe_quant_act with the block as the group.
+ *   MXFP4: K % 32 == 0; q u8 [E, N, K/2]; scales u8 [E, N, K/32]. */
+moe_status_t moe_quant_weights(int32_t quant_mode, const float* w, int32_t E, int32_t N,
+                               int32_t K, void* q, void* scales, void* stream);
+
+/* Sizes of the TILED_V1 buffers for w13 (which = 13: N = 2*Ip, K = Hp) or
+ * w2 (which = 2: N = Hp, K = Ip). */
+moe_status_t moe_preshuffled_bytes(const moe_cfg_t* cfg, int32_t which, size_t* w_bytes,
+                                   size_t* s_bytes);
+
+/* Rewrites CANONICAL quantised weights (moe_quant_weights' output for the
+ * padded matrix of `which`) into TILED_V1, the only layout the GEMM entry
+ * points read (sglang PR #38546, contract table: the runner owns its
+ * preshuffle).  Ignores cfg->weight_layout.  Output sizes from
+ * moe_preshuffled_bytes.  In and out must not overlap. */
+moe_status_t moe_preshuffle_weights(const moe_cfg_t* cfg, int32_t which, const void* w,
+                                    const void* s, void* w_out, void* s_out, void* stream);
+
+/* Grouped gate/up GEMM + clamped SwiGLU + re-quantisation (sglang PR #38546,
+ * Summary; FreeToken PR #270, Summary).  For every row r of every block b <
+ * num_post_padded/block_m with pair f = sorted_ids[b*block_m + r] < T*k:
+ *   h = deq(xq[f / k]) . deq(w13[block_expert[b]])^T   (fp32, N = 2Ip, K = Hp)
+ *   a = silu(min(h[:Ip], L)) * clamp(h[Ip:], -L, L)
+ *   aq/as row (b*block_m + r) = quantise(a) per 1x128 (FP8) or 1x32 (MXFP4)
+ * Pad rows (f = T*k) get all-zero codes and zero scales.
+ * xq/xs: moe_quant_act output for x (FP8: u8 [T, Hp] + f32 [T, Hp/128];
+ * MXFP4: u8 [T, Hp/2] + u8 [T, Hp/32]).  w13/w13_scale: TILED_V1.
+ * aq/as: sizes from moe_intermediate_bytes, indexed by sorted position. */
+moe_status_t moe_grouped_gemm1_swiglu(const moe_cfg_t* cfg, int32_t T, const void* xq,
+                                      const void* xs, const int32_t* sorted_ids,
+                                      const int32_t* block_expert,
+                                      const int32_t* num_post_padded, const void* w13,
+                                      const void* w13_scale, void* aq, void* as, void* stream);
+
+/* Grouped down GEMM + routing-weighted combine.  For each pair f:
+ *   y_f = deq(aq row of f) . deq(w2[e])^T   (fp32, N = Hp, K = Ip)
+ *   out[t, :H] = bf16_rne( sum over j = 0..k-1 in slot order of
+ *                          fl32(topk_w[t, j] * y_{t*k+j}) ), fp32 accumulation.
+ * out: bf16 [T, ld_out]; columns >= H are not written.  ws: at least
+ * moe_workspace_bytes(cfg, T) bytes. */
+moe_status_t moe_grouped_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const void* aq,
+                                       const void* as, const int32_t* sorted_ids,
+                                       const int32_t* block_expert,
+                                       const int32_t* num_post_padded, const void* w2,
+                                       const void* w2_scale, const float* topk_w,
+                                       void* out_bf16, int64_t ld_out, void* ws,
+                                       size_t ws_bytes, void* stream);
+
+/* The whole layer: route, permute, quantise x, GEMM1+SwiGLU, GEMM2+combine,
+ * all on `stream` with no host synchronisation.  x: bf16 [T, ld_x] (H valid
+ * columns); router_logits f32 [T, E]; weights TILED_V1; out bf16 [T, ld_out].
+ * ws: at least moe_workspace_bytes(cfg, T) bytes. */
+moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, int64_t ld_x,
+                         const float* router_logits, const void* w13, const void* w13_scale,
+                         const void* w2, const void* w2_scale, void* out_bf16, int64_t ld_out,
+                         void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */
