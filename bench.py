@@ -1,0 +1,240 @@
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+One step = one moe_forward over one batch of synthetic tokens: top-k routing,
+permutation, activation quantisation, GEMM1 + clamped SwiGLU +
+re-quantisation, GEMM2 + weighted combine.  Inputs (router logits, bf16
+activations, quantised + preshuffled weights of all experts) are resident in
+HBM before the timed region starts.
+
+Prints one JSON line with tokens/s (whole job), effective TFLOP/s
+(6*T*k*H*I per step on the real sizes), the roofline of the dominant kernel
+(its average duration from HIP events recorded on the launch stream around
+the same kernels, called through the stage entry points) and the CPU
+oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "mxfp4": 10100.0}   # dense, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_fp8")
+    ap.add_argument("--T", type=int, default=0, help="override the token count")
+    ap.add_argument("--block-m", type=int, default=0)
+    ap.add_argument("--cpu-sample", type=int, default=4, help="tokens in the oracle's timed sample (0 = skip)")
+    ap.add_argument("--no-breakdown", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(wl, ids, M):
+    """Bytes the layer must move at least once: the weights and scales of
+    every expert with at least one pair, x, the logits and the output; plus,
+    per kernel, what it must read/write (documented next to the roofline)."""
+    import numpy as np
+    counts = np.bincount(ids.reshape(-1), minlength=wl.E)
+    active = int(np.count_nonzero(counts))
+    Hp, Ip = wl.Hp, wl.Ip
+    P = wl.T * wl.top_k
+    if wl.mode == "fp8":
+        w13 = 2 * Ip * Hp + (2 * Ip // 128) * (Hp // 128) * 4
+        w2 = Hp * Ip + (Hp // 128) * (Ip // 128) * 4
+        xq = wl.T * (Hp + Hp // 128 * 4)
+        aq = P * (Ip + Ip // 128 * 4)
+    else:
+        w13 = 2 * Ip * Hp // 2 + 2 * Ip * Hp // 32
+        w2 = Hp * Ip // 2 + Hp * Ip // 32
+        xq = wl.T * (Hp // 2 + Hp // 32)
+        aq = P * (Ip // 2 + Ip // 32)
+    layer = active * (w13 + w2) + wl.T * wl.H * 2 + wl.T * wl.E * 4 + wl.T * wl.H * 2
+    gemm1 = active * w13 + xq + aq
+    gemm2 = active * w2 + aq + P * Hp * 4
+    return dict(active_experts=active, layer=layer, gemm1=gemm1, gemm2=gemm2,
+                w13_per_expert=w13, w2_per_expert=w2)
+
+
+def cpu_baseline(wl, x, lg, sample_tokens: int):
+    """The oracle, as it stands, on the first `sample_tokens` tokens of the
+    same workload: timed from bf16 activations + quantised weights to the fp32
+    output (routing, activation quantisation, dequantisation, GEMMs, SwiGLU,
+    re-quantisation, combine).  Weight quantisation is done beforehand and
+    not timed."""
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    from oracle.from_workload import quantize_experts
+    toks = list(range(min(sample_tokens, wl.T)))
+    lg_h = lg.cpu().numpy()
+    x_h = x.float().cpu().numpy()
+    ids, _ = O.route_topk(lg_h[toks], wl.top_k)
+    Q = quantize_experts(wl, np.unique(ids), "cuda")
+    t0 = time.perf_counter()
+    O.moe_forward(x_h, lg_h, Q, wl.top_k, wl.swiglu_limit, wl.H, wl.I, tokens=toks)
+    dt = time.perf_counter() - t0
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {len(toks)} of {wl.T} tokens of {wl.name} ({len(np.unique(ids))} experts), "
+                      f"{dt:.2f} s wall; weight quantisation excluded; "
+                      f"host affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
+              "sharding is described, not built", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import workloads as W
+    import mxfp4_quantized_weights_amd as M
+
+    wl = W.WORKLOADS[args.workload]
+    if args.T:
+        wl = wl.with_(T=args.T)
+    bm = args.block_m or M.pick_block_m(wl.T, wl.E, wl.top_k)
+    cfg = M.make_cfg(wl.E, wl.top_k, wl.mode, wl.H, wl.I, wl.Hp, wl.Ip, block_m=bm,
+                     swiglu_limit=wl.swiglu_limit)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    # weights: drawn on the GPU, quantised and preshuffled by the library
+    ew = M.ExpertWeights(cfg, dev)
+    for e0 in range(0, wl.E, 16):
+        ex = range(e0, min(wl.E, e0 + 16))
+        ew.add_experts(e0, W.all_w13(wl, ex, "cuda"), W.all_w2(wl, ex, "cuda"))
+    ew.finalize()
+    ew.q13 = ew.s13 = ew.q2 = ew.s2 = None      # only the tiled copies stay resident
+    torch.cuda.empty_cache()
+    x = W.activations(wl, "cuda")
+    lg = W.router_logits(wl, "cuda")
+    out = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(M.workspace_bytes(cfg, wl.T), dtype=torch.uint8, device=dev)
+    w13, s13, w2, s2 = ew.tiled()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        M.moe_forward(cfg, x, lg, w13, s13, w2, s2, out=out, ws=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+
+    # per-kernel breakdown: the same kernels through the stage entry points,
+    # HIP events recorded on the launch stream between them
+    ids, wts = M.moe_route_topk(lg, wl.top_k)
+    ids_h = ids.cpu().numpy()
+    nbytes = algorithmic_bytes(wl, ids_h, M)
+    kern = {}
+    if not args.no_breakdown:
+        names = ["route_topk", "permute_align", "quant_act", "gemm1_swiglu", "gemm2_combine"]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        aq_b, as_b = M.intermediate_bytes(cfg, wl.T)
+        nb = M.max_blocks(wl.T * wl.top_k, wl.E, bm)
+        sid = torch.empty(nb * bm, dtype=torch.int32, device=dev)
+        bexp = torch.empty(nb, dtype=torch.int32, device=dev)
+        offs = torch.empty(wl.E + 1, dtype=torch.int32, device=dev)
+        npp = torch.empty(1, dtype=torch.int32, device=dev)
+        import ctypes
+        lib = M.lib()
+        cfgp = ctypes.byref(cfg)
+        sp = stream.cuda_stream
+        if wl.mode == "fp8":
+            xq = torch.empty(wl.T, wl.Hp, dtype=torch.uint8, device=dev)
+            xs = torch.empty(wl.T, wl.Hp // 128, dtype=torch.float32, device=dev)
+        else:
+            xq = torch.empty(wl.T, wl.Hp // 2, dtype=torch.uint8, device=dev)
+            xs = torch.empty(wl.T, wl.Hp // 32, dtype=torch.uint8, device=dev)
+        aq = torch.empty(aq_b, dtype=torch.uint8, device=dev)
+        as_ = torch.empty(as_b, dtype=torch.uint8, device=dev)
+        qm = cfg.quant_mode
+
+        def staged(evs):
+            evs[0].record(stream)
+            lib.moe_route_topk(lg.data_ptr(), wl.T, wl.E, wl.top_k, ids.data_ptr(), wts.data_ptr(), sp)
+            evs[1].record(stream)
+            lib.moe_permute_align(ids.data_ptr(), wl.T, wl.top_k, wl.E, bm, sid.data_ptr(), bexp.data_ptr(),
+                                  offs.data_ptr(), npp.data_ptr(), sp)
+            evs[2].record(stream)
+            lib.moe_quant_act(x.data_ptr(), M.MOE_DTYPE_BF16, wl.T, wl.H, wl.H, wl.Hp, qm, xq.data_ptr(),
+                              xs.data_ptr(), sp)
+            evs[3].record(stream)
+            lib.moe_grouped_gemm1_swiglu(cfgp, wl.T, xq.data_ptr(), xs.data_ptr(), sid.data_ptr(), bexp.data_ptr(),
+                                         npp.data_ptr(), w13.data_ptr(), s13.data_ptr(), aq.data_ptr(),
+                                         as_.data_ptr(), sp)
+            evs[4].record(stream)
+            lib.moe_grouped_gemm2_combine(cfgp, wl.T, aq.data_ptr(), as_.data_ptr(), sid.data_ptr(),
+                                          bexp.data_ptr(), npp.data_ptr(), w2.data_ptr(), s2.data_ptr(),
+                                          wts.data_ptr(), out.data_ptr(), wl.H, ws.data_ptr(), ws.numel(), sp)
+            evs[5].record(stream)
+
+        for i in range(min(args.warmup, args.steps)):
+            staged(ev[i])
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            staged(ev[i])
+        torch.cuda.synchronize()
+        for j, n in enumerate(names):
+            kern[n] = float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)])) * 1e3  # us
+
+    tokens_per_s = wl.T / (ms * 1e-3)
+    flops = wl.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    dom = "gemm1_swiglu"
+    roof = None
+    if kern:
+        dur = kern[dom] * 1e-6
+        gbs = nbytes["gemm1"] / dur / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "moe_gemm_kernel (GEMM1+SwiGLU)",
+                "kernel_us": round(kern[dom], 2), "algorithmic_bytes": nbytes["gemm1"]}
+    res = {
+        "metric": "MoE layer tokens/s + effective TFLOP/s (% of MFMA/HBM roofline), 1 MI355X",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3" if wl.mode == "fp8" else "fp4e2m1",
+        "data": "synthetic (seeded N(0,1) activations/logits, N(0,0.02) weights, quantised by the library)",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "Hp": wl.Hp, "Ip": wl.Ip, "E": wl.E,
+                   "top_k": wl.top_k, "quant": wl.mode, "block_m": bm, "swiglu_limit": wl.swiglu_limit},
+        "effective_tflops": round(tflops, 3),
+        "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[wl.mode], 5),
+        "layer_hbm_frac": round(nbytes["layer"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "active_experts": nbytes["active_experts"],
+        "layer_algorithmic_bytes": nbytes["layer"],
+        "kernels_us": {k: round(v, 2) for k, v in kern.items()},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if args.cpu_sample > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, x, lg, args.cpu_sample)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

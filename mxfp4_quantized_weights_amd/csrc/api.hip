@@ -1,0 +1,357 @@
+// C ABI of libmoe.so: argument validation (before anything is enqueued),
+// workspace layout and kernel sequencing.  See include/moe.h for the contract
+// of every entry point.
+//
+// sglang PR #38546 "[AMD] [GLM-5.3-Flash Day 0] Enable FP8 and Quark MXFP4 MoE
+// on gfx950", contract table: the gate mode is explicit and only separate
+// halves are accepted, the SwiGLU limit is always forwarded, the preshuffled
+// layout belongs to this runner (layout tag), an unsupported configuration
+// fails when it is validated rather than later, and hidden/intermediate
+// padding is carried as metadata.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+constexpr int32_t kMaxExperts = 1024;
+constexpr int32_t kMaxTopK = 16;
+constexpr int32_t kMaxDim = 1 << 16;       // padded hidden / intermediate
+constexpr int64_t kMaxPairs = 1ll << 24;   // T * top_k
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status_t check_cfg(const moe_cfg_t* c) {
+  if (!c) return MOE_ERR_NULL;
+  if (c->num_experts < 1 || c->num_experts > kMaxExperts) return MOE_ERR_SHAPE;
+  if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->num_experts) return MOE_ERR_SHAPE;
+  if (c->quant_mode != MOE_QUANT_FP8_BLOCK && c->quant_mode != MOE_QUANT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (c->gate_mode != MOE_GATE_SEPARATED) return MOE_ERR_UNSUPPORTED;
+  if (c->block_m != 16 && c->block_m != 32 && c->block_m != 64 && c->block_m != 128) return MOE_ERR_UNSUPPORTED;
+  if (!(c->swiglu_limit > 0.0f)) return MOE_ERR_UNSUPPORTED;  // rejects NaN, 0, negatives
+  const moe_pad_t& p = c->pad;
+  if (p.hidden < 1 || p.inter < 1 || p.hidden_padded < p.hidden || p.inter_padded < p.inter) return MOE_ERR_SHAPE;
+  if (p.hidden_padded > kMaxDim || p.inter_padded > kMaxDim) return MOE_ERR_SHAPE;
+  if (p.hidden_padded % 128 != 0 || p.inter_padded % 128 != 0) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+moe_status_t check_tokens(const moe_cfg_t* c, int32_t T) {
+  if (T < 0) return MOE_ERR_SHAPE;
+  if ((int64_t)T * c->top_k > kMaxPairs) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+moe_status_t check_layout(const moe_cfg_t* c) {
+  return c->weight_layout == MOE_LAYOUT_TILED_V1 ? MOE_OK : MOE_ERR_LAYOUT;
+}
+
+int32_t max_blocks(int64_t P, int32_t E, int32_t BM) {
+  int64_t a = (P + (int64_t)E * (BM - 1)) / BM;
+  return (int32_t)(P < a ? P : a);
+}
+
+// Sizes of the pieces of one layer's scratch, in carve order.
+struct Layout {
+  size_t ids, wts, sorted, bexp, offs, npp, xq, xs, aq, as, y, total;
+};
+
+Layout layout_for(const moe_cfg_t* c, int32_t T) {
+  Layout L{};
+  const int64_t P = (int64_t)T * c->top_k;
+  const int32_t nb = max_blocks(P, c->num_experts, c->block_m);
+  const int64_t rows = (int64_t)nb * c->block_m;
+  const int64_t Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
+  const bool fp8 = c->quant_mode == MOE_QUANT_FP8_BLOCK;
+  L.ids = align_up(P * 4);
+  L.wts = align_up(P * 4);
+  L.sorted = align_up(rows * 4);
+  L.bexp = align_up((size_t)nb * 4);
+  L.offs = align_up((size_t)(c->num_experts + 1) * 4);
+  L.npp = align_up(4);
+  L.xq = align_up(fp8 ? T * Hp : T * Hp / 2);
+  L.xs = align_up(fp8 ? T * (Hp / 128) * 4 : T * (Hp / 32));
+  L.aq = align_up(fp8 ? rows * Ip : rows * Ip / 2);
+  L.as = align_up(fp8 ? rows * (Ip / 128) * 4 : rows * (Ip / 32));
+  L.y = align_up(P * Hp * 4);
+  L.total = L.ids + L.wts + L.sorted + L.bexp + L.offs + L.npp + L.xq + L.xs + L.aq + L.as + L.y;
+  return L;
+}
+
+moe::GemmArgs gemm1_args(const moe_cfg_t* c, int32_t T, const void* xq, const void* xs, const int32_t* sorted,
+                         const int32_t* bexp, const int32_t* npp, const void* w13, const void* s13, void* aq,
+                         void* as) {
+  moe::GemmArgs a{};
+  const bool fp8 = c->quant_mode == MOE_QUANT_FP8_BLOCK;
+  const int Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
+  a.A = (const uint8_t*)xq;
+  a.As = xs;
+  a.lda = fp8 ? Hp : Hp / 2;
+  a.ldas = fp8 ? Hp / 128 : Hp / 32;
+  a.sorted_ids = sorted;
+  a.block_expert = bexp;
+  a.npp = npp;
+  a.top_k = c->top_k;
+  a.num_pairs = T * c->top_k;
+  a.B = (const uint8_t*)w13;
+  a.Bs = s13;
+  a.N = 2 * Ip;
+  a.K = Hp;
+  a.n_tiles = Ip / 128;
+  a.aq = (uint8_t*)aq;
+  a.as = as;
+  a.Ip = Ip;
+  a.limit = c->swiglu_limit;
+  return a;
+}
+
+moe::GemmArgs gemm2_args(const moe_cfg_t* c, int32_t T, const void* aq, const void* as, const int32_t* sorted,
+                         const int32_t* bexp, const int32_t* npp, const void* w2, const void* s2, float* y,
+                         const float* topk_w) {
+  moe::GemmArgs a{};
+  const bool fp8 = c->quant_mode == MOE_QUANT_FP8_BLOCK;
+  const int Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
+  a.A = (const uint8_t*)aq;
+  a.As = as;
+  a.lda = fp8 ? Ip : Ip / 2;
+  a.ldas = fp8 ? Ip / 128 : Ip / 32;
+  a.sorted_ids = sorted;
+  a.block_expert = bexp;
+  a.npp = npp;
+  a.top_k = c->top_k;
+  a.num_pairs = T * c->top_k;
+  a.B = (const uint8_t*)w2;
+  a.Bs = s2;
+  a.N = Hp;
+  a.K = Ip;
+  a.n_tiles = (Hp + 255) / 256;
+  a.Ip = Ip;
+  a.limit = c->swiglu_limit;
+  a.y = y;
+  a.topk_w = topk_w;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: a size is out of range or inconsistent";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: a padded size is not a multiple of 128";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: unsupported quant mode, gate mode, block_m, limit or dtype";
+    case MOE_ERR_LAYOUT: return "MOE_ERR_LAYOUT: weight layout tag not accepted by this call";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: kernel launch failed";
+  }
+  return "unknown moe_status_t";
+}
+
+moe_status_t moe_validate_cfg(const moe_cfg_t* cfg) { return check_cfg(cfg); }
+
+int32_t moe_max_blocks(int32_t num_pairs, int32_t num_experts, int32_t block_m) {
+  if (num_pairs < 0 || num_experts < 1 || block_m < 1) return -1;
+  return max_blocks(num_pairs, num_experts, block_m);
+}
+
+size_t moe_workspace_bytes(const moe_cfg_t* cfg, int32_t T_max) {
+  if (check_cfg(cfg) != MOE_OK || check_tokens(cfg, T_max) != MOE_OK) return 0;
+  return layout_for(cfg, T_max).total;
+}
+
+moe_status_t moe_intermediate_bytes(const moe_cfg_t* cfg, int32_t T, size_t* aq_bytes, size_t* as_bytes) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
+  if (!aq_bytes || !as_bytes) return MOE_ERR_NULL;
+  const int64_t rows = (int64_t)max_blocks((int64_t)T * cfg->top_k, cfg->num_experts, cfg->block_m) * cfg->block_m;
+  const int64_t Ip = cfg->pad.inter_padded;
+  const bool fp8 = cfg->quant_mode == MOE_QUANT_FP8_BLOCK;
+  *aq_bytes = (size_t)(fp8 ? rows * Ip : rows * Ip / 2);
+  *as_bytes = (size_t)(fp8 ? rows * (Ip / 128) * 4 : rows * (Ip / 32));
+  return MOE_OK;
+}
+
+moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t top_k, int32_t* ids, float* weights,
+                            void* stream) {
+  if (T < 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > kMaxTopK || top_k > E) return MOE_ERR_SHAPE;
+  if ((int64_t)T * top_k > kMaxPairs) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!logits || !ids || !weights) return MOE_ERR_NULL;
+  return hip_status(moe::launch_route_topk(logits, T, E, top_k, ids, weights, as_stream(stream)));
+}
+
+moe_status_t moe_permute_align(const int32_t* ids, int32_t T, int32_t top_k, int32_t E, int32_t block_m,
+                               int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                               int32_t* num_post_padded, void* stream) {
+  if (T < 0 || E < 1 || E > kMaxExperts || top_k < 1 || top_k > kMaxTopK) return MOE_ERR_SHAPE;
+  if (block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return MOE_ERR_UNSUPPORTED;
+  const int64_t P = (int64_t)T * top_k;
+  if (P > kMaxPairs) return MOE_ERR_SHAPE;
+  if (!expert_offsets || !num_post_padded) return MOE_ERR_NULL;
+  if (P > 0 && (!ids || !sorted_ids || !block_expert)) return MOE_ERR_NULL;
+  const int32_t nb = max_blocks(P, E, block_m);
+  return hip_status(moe::launch_permute_align(ids, (int)P, E, block_m, nb, sorted_ids, block_expert, expert_offsets,
+                                              num_post_padded, as_stream(stream)));
+}
+
+moe_status_t moe_quant_act(const void* in, int32_t in_dtype, int32_t rows, int32_t cols, int64_t ld_in,
+                           int32_t cols_padded, int32_t quant_mode, void* q, void* scales, void* stream) {
+  if (in_dtype != MOE_DTYPE_BF16 && in_dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
+  if (quant_mode != MOE_QUANT_FP8_BLOCK && quant_mode != MOE_QUANT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (rows < 0 || cols < 1 || cols > cols_padded || ld_in < cols) return MOE_ERR_SHAPE;
+  if (cols_padded % 128 != 0) return MOE_ERR_ALIGN;
+  if (rows == 0) return MOE_OK;
+  if (!in || !q || !scales) return MOE_ERR_NULL;
+  return hip_status(moe::launch_quant_rows(in, in_dtype == MOE_DTYPE_BF16, rows, cols, ld_in, cols_padded,
+                                           quant_mode, q, scales, as_stream(stream)));
+}
+
+moe_status_t moe_quant_weights(int32_t quant_mode, const float* w, int32_t E, int32_t N, int32_t K, void* q,
+                               void* scales, void* stream) {
+  if (quant_mode != MOE_QUANT_FP8_BLOCK && quant_mode != MOE_QUANT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (E < 1 || N < 1 || K < 1 || N > kMaxDim * 2 || K > kMaxDim) return MOE_ERR_SHAPE;
+  if (quant_mode == MOE_QUANT_FP8_BLOCK ? (N % 128 != 0 || K % 128 != 0) : (K % 32 != 0)) return MOE_ERR_ALIGN;
+  if (!w || !q || !scales) return MOE_ERR_NULL;
+  hipStream_t s = as_stream(stream);
+  if (quant_mode == MOE_QUANT_FP8_BLOCK)
+    return hip_status(moe::launch_quant_weight_fp8(w, E, N, K, (uint8_t*)q, (float*)scales, s));
+  // MXFP4 groups run along K: the same row quantiser as the activations
+  if (K % 128 != 0) return MOE_ERR_ALIGN;
+  return hip_status(moe::launch_quant_rows(w, false, (int64_t)E * N, K, K, K, moe::kQuantMx, q, scales, s));
+}
+
+moe_status_t moe_preshuffled_bytes(const moe_cfg_t* cfg, int32_t which, size_t* w_bytes, size_t* s_bytes) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (which != 13 && which != 2) return MOE_ERR_SHAPE;
+  if (!w_bytes || !s_bytes) return MOE_ERR_NULL;
+  const int64_t E = cfg->num_experts, Hp = cfg->pad.hidden_padded, Ip = cfg->pad.inter_padded;
+  const int64_t N = which == 13 ? 2 * Ip : Hp, K = which == 13 ? Hp : Ip;
+  if (cfg->quant_mode == MOE_QUANT_FP8_BLOCK) {
+    *w_bytes = (size_t)(E * N * K);
+    *s_bytes = (size_t)(E * (N / 128) * (K / 128) * 4);
+  } else {
+    const int64_t KB = K / 128;
+    *w_bytes = (size_t)(E * N * K / 2);
+    *s_bytes = (size_t)(E * (N / 16) * ((KB + 3) / 4) * 64 * 4);
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_preshuffle_weights(const moe_cfg_t* cfg, int32_t which, const void* w, const void* s, void* w_out,
+                                    void* s_out, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (which != 13 && which != 2) return MOE_ERR_SHAPE;
+  if (!w || !s || !w_out || !s_out) return MOE_ERR_NULL;
+  const int Hp = cfg->pad.hidden_padded, Ip = cfg->pad.inter_padded;
+  const int N = which == 13 ? 2 * Ip : Hp, K = which == 13 ? Hp : Ip;
+  const int mode = cfg->quant_mode == MOE_QUANT_FP8_BLOCK ? moe::kQuantFp8 : moe::kQuantMx;
+  return hip_status(moe::launch_preshuffle(mode, (const uint8_t*)w, s, cfg->num_experts, N, K, (uint8_t*)w_out,
+                                           s_out, as_stream(stream)));
+}
+
+moe_status_t moe_grouped_gemm1_swiglu(const moe_cfg_t* cfg, int32_t T, const void* xq, const void* xs,
+                                      const int32_t* sorted_ids, const int32_t* block_expert,
+                                      const int32_t* num_post_padded, const void* w13, const void* w13_scale, void* aq,
+                                      void* as, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
+  if ((st = check_layout(cfg)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!xq || !xs || !sorted_ids || !block_expert || !num_post_padded || !w13 || !w13_scale || !aq || !as)
+    return MOE_ERR_NULL;
+  const int32_t nb = max_blocks((int64_t)T * cfg->top_k, cfg->num_experts, cfg->block_m);
+  const int mode = cfg->quant_mode == MOE_QUANT_FP8_BLOCK ? moe::kQuantFp8 : moe::kQuantMx;
+  moe::GemmArgs a = gemm1_args(cfg, T, xq, xs, sorted_ids, block_expert, num_post_padded, w13, w13_scale, aq, as);
+  return hip_status(moe::launch_gemm1(mode, cfg->block_m, nb, a, as_stream(stream)));
+}
+
+moe_status_t moe_grouped_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const void* aq, const void* as,
+                                       const int32_t* sorted_ids, const int32_t* block_expert,
+                                       const int32_t* num_post_padded, const void* w2, const void* w2_scale,
+                                       const float* topk_w, void* out_bf16, int64_t ld_out, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
+  if ((st = check_layout(cfg)) != MOE_OK) return st;
+  if (ld_out < cfg->pad.hidden) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!aq || !as || !sorted_ids || !block_expert || !num_post_padded || !w2 || !w2_scale || !topk_w || !out_bf16 ||
+      !ws)
+    return MOE_ERR_NULL;
+  const int64_t P = (int64_t)T * cfg->top_k;
+  const size_t ybytes = align_up((size_t)P * cfg->pad.hidden_padded * 4);
+  if (ws_bytes < ybytes) return MOE_ERR_WORKSPACE;
+  const int32_t nb = max_blocks(P, cfg->num_experts, cfg->block_m);
+  const int mode = cfg->quant_mode == MOE_QUANT_FP8_BLOCK ? moe::kQuantFp8 : moe::kQuantMx;
+  hipStream_t s = as_stream(stream);
+  float* y = (float*)ws;
+  moe::GemmArgs a = gemm2_args(cfg, T, aq, as, sorted_ids, block_expert, num_post_padded, w2, w2_scale, y, topk_w);
+  hipError_t e = moe::launch_gemm2(mode, cfg->block_m, nb, a, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_combine(y, T, cfg->top_k, cfg->pad.hidden, cfg->pad.hidden_padded,
+                                        (uint16_t*)out_bf16, ld_out, s));
+}
+
+moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, int64_t ld_x, const float* router_logits,
+                         const void* w13, const void* w13_scale, const void* w2, const void* w2_scale, void* out_bf16,
+                         int64_t ld_out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
+  if ((st = check_layout(cfg)) != MOE_OK) return st;
+  if (ld_x < cfg->pad.hidden || ld_out < cfg->pad.hidden) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !router_logits || !w13 || !w13_scale || !w2 || !w2_scale || !out_bf16 || !ws) return MOE_ERR_NULL;
+  const Layout L = layout_for(cfg, T);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  uint8_t* p = (uint8_t*)ws;
+  int32_t* ids = (int32_t*)p; p += L.ids;
+  float* wts = (float*)p; p += L.wts;
+  int32_t* sorted = (int32_t*)p; p += L.sorted;
+  int32_t* bexp = (int32_t*)p; p += L.bexp;
+  int32_t* offs = (int32_t*)p; p += L.offs;
+  int32_t* npp = (int32_t*)p; p += L.npp;
+  void* xq = p; p += L.xq;
+  void* xs = p; p += L.xs;
+  void* aq = p; p += L.aq;
+  void* as = p; p += L.as;
+  float* y = (float*)p;
+
+  hipStream_t s = as_stream(stream);
+  const int E = cfg->num_experts, k = cfg->top_k, BM = cfg->block_m;
+  const int64_t P = (int64_t)T * k;
+  const int32_t nb = max_blocks(P, E, BM);
+  const int mode = cfg->quant_mode == MOE_QUANT_FP8_BLOCK ? moe::kQuantFp8 : moe::kQuantMx;
+  hipError_t e;
+  if ((e = moe::launch_route_topk(router_logits, T, E, k, ids, wts, s)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = moe::launch_permute_align(ids, (int)P, E, BM, nb, sorted, bexp, offs, npp, s)) != hipSuccess)
+    return MOE_ERR_HIP;
+  if ((e = moe::launch_quant_rows(x_bf16, true, T, cfg->pad.hidden, ld_x, cfg->pad.hidden_padded, mode, xq, xs, s)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  moe::GemmArgs a1 = gemm1_args(cfg, T, xq, xs, sorted, bexp, npp, w13, w13_scale, aq, as);
+  if ((e = moe::launch_gemm1(mode, BM, nb, a1, s)) != hipSuccess) return MOE_ERR_HIP;
+  moe::GemmArgs a2 = gemm2_args(cfg, T, aq, as, sorted, bexp, npp, w2, w2_scale, y, wts);
+  if ((e = moe::launch_gemm2(mode, BM, nb, a2, s)) != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_combine(y, T, k, cfg->pad.hidden, cfg->pad.hidden_padded, (uint16_t*)out_bf16, ld_out,
+                                        s));
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+// Device-side helpers for the MoE kernels (gfx950): number-format conversions,
+// wave reductions and MFMA wrappers.
+//
+// Formats (sglang PR #38546 "[AMD] [GLM-5.3-Flash Day 0] Enable FP8 and Quark
+// MXFP4 MoE on gfx950", Summary): OCP E4M3FN for block FP8, OCP MXFP4 = E2M1
+// elements with one E8M0 scale per 32 elements.  The rounding conversions
+// (fp32 -> e4m3 / E2M1 / bf16, E8M0 exponents) are written with integer and
+// round-to-nearest-even arithmetic, so their results are fixed by
+// construction; only exact widenings (e4m3 -> f16) use a hardware convert.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE2M1Max = 6.0f;
+
+// E4M3FN code of a finite fp32 value with |v| <= 448, rounded to nearest,
+// ties to even; the sign bit is kept (also for zero).
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t ua = u & 0x7FFFFFFFu;
+  float a = __uint_as_float(ua);
+  uint32_t code;
+  if (a < 0.015625f) {
+    // below the smallest normal 2^-6: multiples of 2^-9; a * 2^9 is exact
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    // keep 3 mantissa bits with round-half-even at bit 20, then rebias 127 -> 7
+    ua += 0x7FFFFu + ((ua >> 20) & 1u);
+    code = (ua >> 20) - (120u << 3);
+  }
+  return sign | code;
+}
+
+// E2M1 code of a finite fp32 value with |v| <= 6 (grid 0, .5, 1, 1.5, 2, 3,
+// 4, 6), rounded to nearest, ties to the even code; sign in bit 3.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
+  float a = fabsf(v);
+  uint32_t c;
+  if (a < 2.0f) {
+    c = (uint32_t)__builtin_rintf(a * 2.0f);          // codes 0..4, spacing 0.5
+  } else if (a < 4.0f) {
+    c = (uint32_t)__builtin_rintf(a) + 2u;            // 2 -> 4, 3 -> 5, 4 -> 6
+  } else {
+    c = (uint32_t)__builtin_rintf(a * 0.5f) + 4u;     // 4 -> 6, 6 -> 7
+  }
+  return sign | c;
+}
+
+// E8M0 byte of an MX block: 2^(floor(log2 amax) - 2) biased by 127, clamped to
+// [0, 254]; 0 for amax == 0.  floor(log2) comes from the exponent bits
+// (subnormals included), never from a log instruction.
+__device__ __forceinline__ uint32_t e8m0_byte(float amax) {
+  uint32_t u = __float_as_uint(amax);
+  if (u == 0u) return 0u;
+  int e;
+  uint32_t ef = u >> 23;
+  if (ef) {
+    e = (int)ef - 127;
+  } else {
+    e = (31 - __builtin_clz(u & 0x7FFFFFu)) - 149;
+  }
+  int b = e - 2 + 127;
+  return (uint32_t)(b < 0 ? 0 : (b > 254 ? 254 : b));
+}
+
+// 2^(127 - b) as fp32 for b in [0, 252] (always a normal number).
+__device__ __forceinline__ float e8m0_inverse(uint32_t b) {
+  return __uint_as_float((254u - b) << 23);
+}
+
+// fp32 -> bf16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Quantise one value of a block-FP8 group whose scale s = amax/448 > 0.
+__device__ __forceinline__ uint32_t fp8_quant(float v, float s) {
+  float r = v / s;  // IEEE division (built with correctly rounded fp32 divide)
+  r = fminf(fmaxf(r, -kE4M3Max), kE4M3Max);
+  return e4m3_code(r);
+}
+
+// Quantise one value of an MX group with scale byte b (inv = 2^(127-b)).
+__device__ __forceinline__ uint32_t mx_quant(float v, float inv) {
+  float r = v * inv;  // exact scaling by a power of two
+  r = fminf(fmaxf(r, -kE2M1Max), kE2M1Max);
+  return e2m1_code(r);
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+// Clamped SwiGLU (FreeToken PR #270, Summary): silu(min(g, L)) * clamp(u, -L, L).
+__device__ __forceinline__ float swiglu_clamped(float g, float u, float L) {
+  float gc = fminf(g, L);
+  float uc = fminf(fmaxf(u, -L), L);
+  return silu_f32(gc) * uc;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float max_xor(float v) {
+#pragma unroll
+  for (int off = 1; off < WIDTH; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// 16x16x128 FP8 (e4m3 x e4m3) MFMA with unit E8M0 scales (byte 127 = 2^0).
+// Lane l holds A row (l % 16), K bytes [32*(l/16), +32); B likewise for its
+// column; the result lane l holds C[4*(l/16) + i][l % 16], i = 0..3.
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// Two e4m3 values (bytes 0,1 or 2,3 of w) to two f16 values.  Exact: every
+// e4m3 value, subnormals included, is an f16 value (scale 1.0).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2(uint32_t w) {
+  v2h h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// 16x16x32 f16 MFMA, fp32 accumulation.  Lane l holds A row (l % 16), 8
+// values of K; result layout as mfma_fp8.  Used where the sum must be exact
+// to fp32 precision: the gfx950 FP8 MFMA drops low-order bits of small
+// products inside its internal sum, the f16 one does not.
+__device__ __forceinline__ v4f mfma_f16(const v8h& a, const v8h& b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x128 FP4 (E2M1 x E2M1) MFMA with per-lane E8M0 scales: lane l's scale
+// applies to its own 32 K-values (its A row / B column, K group l/16).  The A
+// scale is byte 0 of sa; the B scale is byte OPB of sb.
+template <int OPB>
+__device__ __forceinline__ v4f mfma_fp4_scaled(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, sa, OPB, sb);
+}
+
+}  // namespace moe

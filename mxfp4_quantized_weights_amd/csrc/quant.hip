@@ -1,0 +1,240 @@
+// Quantisers and the weight preshuffle.
+//
+// sglang PR #38546 "[AMD] [GLM-5.3-Flash Day 0] Enable FP8 and Quark MXFP4 MoE
+// on gfx950", Summary: block FP8 [128,128] weights with dynamic FP8
+// activations (per token, 1x128 groups here), and OCP MXFP4 1x32 for weights
+// and activations; contract table: the runner that consumes a preshuffled
+// layout owns it.
+//
+// Block FP8 group:  s = amax / 448 (fp32 division), q = RNE(clamp(v / s)),
+//                   amax = 0 -> s = 0, all codes 0x00.
+// MXFP4 group (32): b = clamp(floor(log2 amax) - 2 + 127, 0, 254) (0 for
+//                   amax = 0), q = RNE_E2M1(clamp(v * 2^(127 - b), +-6)),
+//                   element 2i in the low nibble of byte i.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+template <bool BF16>
+__device__ __forceinline__ float2 load_pair(const void* in, int64_t row, int64_t ld, int col, int cols) {
+  float2 r = make_float2(0.0f, 0.0f);
+  if (BF16) {
+    const uint16_t* p = (const uint16_t*)in + row * ld;
+    if (col < cols) r.x = bf16_to_f32(p[col]);
+    if (col + 1 < cols) r.y = bf16_to_f32(p[col + 1]);
+  } else {
+    const float* p = (const float*)in + row * ld;
+    if (col < cols) r.x = p[col];
+    if (col + 1 < cols) r.y = p[col + 1];
+  }
+  return r;
+}
+
+// One wave per 128-column chunk of one row; lane l holds columns 2l, 2l+1.
+// FP8: the chunk is one group.  MX: the chunk is four groups of 16 lanes.
+template <bool BF16, int MODE>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ in, int64_t rows, int cols,
+                                                         int64_t ld_in, int cols_padded,
+                                                         uint8_t* __restrict__ q, void* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int chunks = cols_padded / 128;
+  const int64_t total = rows * chunks;
+  for (int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); c < total; c += (int64_t)gridDim.x * 4) {
+    const int64_t row = c / chunks;
+    const int g = (int)(c % chunks);
+    const int col = g * 128 + 2 * lane;
+    float2 v = load_pair<BF16>(in, row, ld_in, col, cols);
+    float a = fmaxf(fabsf(v.x), fabsf(v.y));
+    if (MODE == kQuantFp8) {
+      a = max_xor<64>(a);
+      uint32_t c0 = 0, c1 = 0;
+      float s = 0.0f;
+      if (a > 0.0f) {
+        s = a / kE4M3Max;
+        c0 = fp8_quant(v.x, s);
+        c1 = fp8_quant(v.y, s);
+      }
+      *(uint16_t*)(q + row * (int64_t)cols_padded + col) = (uint16_t)(c0 | (c1 << 8));
+      if (lane == 0) ((float*)scales)[row * chunks + g] = s;
+    } else {
+      a = max_xor<16>(a);
+      uint32_t b = e8m0_byte(a);
+      float inv = e8m0_inverse(b);
+      uint32_t c0 = mx_quant(v.x, inv), c1 = mx_quant(v.y, inv);
+      q[row * (int64_t)(cols_padded / 2) + col / 2] = (uint8_t)(c0 | (c1 << 4));
+      if ((lane & 15) == 0) ((uint8_t*)scales)[row * (int64_t)(cols_padded / 32) + g * 4 + (lane >> 4)] = (uint8_t)b;
+    }
+  }
+}
+
+hipError_t launch_quant_rows(const void* in, bool in_is_bf16, int64_t rows, int cols, int64_t ld_in,
+                             int cols_padded, int mode, void* q, void* scales, hipStream_t s) {
+  int64_t waves = rows * (cols_padded / 128);
+  int64_t blocks = (waves + 3) / 4;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  dim3 grid((unsigned)blocks), block(256);
+  uint8_t* qb = (uint8_t*)q;
+  if (in_is_bf16) {
+    if (mode == kQuantFp8)
+      hipLaunchKernelGGL((quant_rows_kernel<true, kQuantFp8>), grid, block, 0, s, in, rows, cols, ld_in, cols_padded, qb, scales);
+    else
+      hipLaunchKernelGGL((quant_rows_kernel<true, kQuantMx>), grid, block, 0, s, in, rows, cols, ld_in, cols_padded, qb, scales);
+  } else {
+    if (mode == kQuantFp8)
+      hipLaunchKernelGGL((quant_rows_kernel<false, kQuantFp8>), grid, block, 0, s, in, rows, cols, ld_in, cols_padded, qb, scales);
+    else
+      hipLaunchKernelGGL((quant_rows_kernel<false, kQuantMx>), grid, block, 0, s, in, rows, cols, ld_in, cols_padded, qb, scales);
+  }
+  return hipGetLastError();
+}
+
+// One workgroup per [128, 128] block; thread t covers row t/2, columns
+// 64*(t%2) .. +64.
+__global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const float* __restrict__ w, int N, int K,
+                                                               uint8_t* __restrict__ q, float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int nbk = K / 128, nbn = N / 128;
+  const int64_t blk = blockIdx.x;
+  const int64_t e = blk / ((int64_t)nbn * nbk);
+  const int bn = (int)((blk / nbk) % nbn), bk = (int)(blk % nbk);
+  const int t = threadIdx.x;
+  const int64_t r = (int64_t)bn * 128 + (t >> 1);
+  const int c0 = bk * 128 + (t & 1) * 64;
+  const float4* src = (const float4*)(w + (e * N + r) * (int64_t)K + c0);
+  float4 v[16];
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = src[i];
+    a = fmaxf(a, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+  }
+  a = max_xor<64>(a);
+  if ((t & 63) == 0) red[t >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float s = (a > 0.0f) ? a / kE4M3Max : 0.0f;
+  uint32_t* dst = (uint32_t*)(q + (e * N + r) * (int64_t)K + c0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t word = 0;
+    if (a > 0.0f) {
+      word = fp8_quant(v[i].x, s) | (fp8_quant(v[i].y, s) << 8) | (fp8_quant(v[i].z, s) << 16) |
+             (fp8_quant(v[i].w, s) << 24);
+    }
+    dst[i] = word;
+  }
+  if (t == 0) scales[(e * nbn + bn) * nbk + bk] = s;
+}
+
+hipError_t launch_quant_weight_fp8(const float* w, int E, int N, int K, uint8_t* q, float* scales,
+                                   hipStream_t s) {
+  int64_t blocks = (int64_t)E * (N / 128) * (K / 128);
+  hipLaunchKernelGGL(quant_weight_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, N, K, q, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// TILED_V1 preshuffle.  For each expert, 16-row tile nt and 128-wide K block
+// kb, the kernels' B operand is one MFMA 16x16x128 tile: lane l needs row
+// nt*16 + l%16 and K values kb*128 + 32*(l/16) .. +32.
+//   FP8: tile = 2048 bytes, [h (2)][lane (64)][16 bytes]: half h holds the
+//        lane's K bytes 16h .. 16h+15, so each 16-byte wave load is 1 KB
+//        contiguous.  Block scales stay canonical f32 [E, N/128, K/128].
+//   MX:  tile = 1024 bytes, [lane (64)][16 bytes] (32 packed E2M1).  Scales:
+//        per (expert, nt) and group of 4 K blocks, [lane (64)][4 bytes], byte
+//        i = E8M0 of K block 4q+i for the lane's row and 32-group; missing K
+//        blocks (K/128 not a multiple of 4) hold 0.
+// Tiles are ordered [E][N/16][K/128] so a wave streams K contiguously.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void preshuffle_fp8_kernel(const uint8_t* __restrict__ w, int64_t total_chunks,
+                                                             int N, int K, uint8_t* __restrict__ out) {
+  const int KB = K / 128, NT = N / 16;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total_chunks; c += (int64_t)gridDim.x * 256) {
+    int64_t tile = c >> 7;
+    int within = (int)(c & 127);
+    int h = within >> 6, l = within & 63;
+    int kb = (int)(tile % KB);
+    int64_t en = tile / KB;
+    int nt = (int)(en % NT);
+    int64_t e = en / NT;
+    int64_t row = (int64_t)nt * 16 + (l & 15);
+    int64_t col = (int64_t)kb * 128 + 32 * (l >> 4) + 16 * h;
+    uint4 v = *(const uint4*)(w + (e * N + row) * (int64_t)K + col);
+    *(uint4*)(out + c * 16) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void preshuffle_mx_kernel(const uint8_t* __restrict__ w, int64_t total_chunks,
+                                                            int N, int K, uint8_t* __restrict__ out) {
+  const int KB = K / 128, NT = N / 16;
+  const int64_t ldw = K / 2;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total_chunks; c += (int64_t)gridDim.x * 256) {
+    int64_t tile = c >> 6;
+    int l = (int)(c & 63);
+    int kb = (int)(tile % KB);
+    int64_t en = tile / KB;
+    int nt = (int)(en % NT);
+    int64_t e = en / NT;
+    int64_t row = (int64_t)nt * 16 + (l & 15);
+    int64_t col = (int64_t)kb * 64 + 16 * (l >> 4);
+    uint4 v = *(const uint4*)(w + (e * N + row) * ldw + col);
+    *(uint4*)(out + c * 16) = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void preshuffle_mx_scale_kernel(const uint8_t* __restrict__ s, int64_t total_words,
+                                                                  int N, int K, uint32_t* __restrict__ out) {
+  const int KB = K / 128, KB4 = (KB + 3) / 4, NT = N / 16;
+  const int64_t lds = K / 32;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total_words; c += (int64_t)gridDim.x * 256) {
+    int l = (int)(c & 63);
+    int64_t rest = c >> 6;
+    int kq = (int)(rest % KB4);
+    int64_t en = rest / KB4;
+    int nt = (int)(en % NT);
+    int64_t e = en / NT;
+    int64_t row = (int64_t)nt * 16 + (l & 15);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int kb = kq * 4 + i;
+      if (kb < KB) word |= (uint32_t)s[(e * N + row) * lds + kb * 4 + (l >> 4)] << (8 * i);
+    }
+    out[c] = word;
+  }
+}
+
+__global__ __launch_bounds__(256) void copy_words_kernel(const uint32_t* __restrict__ in, int64_t n,
+                                                         uint32_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) out[i] = in[i];
+}
+
+static unsigned grid_for(int64_t items) {
+  int64_t b = (items + 255) / 256;
+  if (b > 65536) b = 65536;
+  if (b < 1) b = 1;
+  return (unsigned)b;
+}
+
+hipError_t launch_preshuffle(int mode, const uint8_t* w, const void* sc, int E, int N, int K,
+                             uint8_t* w_out, void* s_out, hipStream_t s) {
+  const int64_t KB = K / 128, NT = N / 16;
+  if (mode == kQuantFp8) {
+    int64_t chunks = (int64_t)E * NT * KB * 128;
+    hipLaunchKernelGGL(preshuffle_fp8_kernel, dim3(grid_for(chunks)), dim3(256), 0, s, w, chunks, N, K, w_out);
+    int64_t words = (int64_t)E * (N / 128) * KB;
+    hipLaunchKernelGGL(copy_words_kernel, dim3(grid_for(words)), dim3(256), 0, s, (const uint32_t*)sc, words,
+                       (uint32_t*)s_out);
+  } else {
+    int64_t chunks = (int64_t)E * NT * KB * 64;
+    hipLaunchKernelGGL(preshuffle_mx_kernel, dim3(grid_for(chunks)), dim3(256), 0, s, w, chunks, N, K, w_out);
+    int64_t words = (int64_t)E * NT * ((KB + 3) / 4) * 64;
+    hipLaunchKernelGGL(preshuffle_mx_scale_kernel, dim3(grid_for(words)), dim3(256), 0, s, (const uint8_t*)sc,
+                       words, N, K, (uint32_t*)s_out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

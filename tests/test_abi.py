@@ -1,0 +1,199 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+- libmoe.so loads and exports every function include/moe.h declares;
+- every rejected configuration returns its status code before anything is
+  enqueued (sglang PR #38546 "[AMD] [GLM-5.3-Flash Day 0] Enable FP8 and Quark
+  MXFP4 MoE on gfx950", contract table: unsupported configurations fail at
+  construction; gate mode explicit; limit forwarded; layout owned by the
+  runner; padding metadata).  These calls return before any HIP call, so
+  they are safe without a GPU; the pointer arguments are never dereferenced.
+- workspace / block-count / buffer-size arithmetic.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "mxfp4_quantized_weights_amd", "libmoe.so")
+
+if not os.path.exists(LIB):  # CPU host without a prior build: build here (cross-compile)
+    from mxfp4_quantized_weights_amd import build as _build  # noqa: E402
+    _build.build()
+
+import mxfp4_quantized_weights_amd as M  # noqa: E402
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+OK, NULL, SHAPE, ALIGN, UNSUP, LAYOUT, WS = 0, 1, 2, 3, 4, 5, 6
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = _declared_functions()
+    for must in ("moe_route_topk", "moe_permute_align", "moe_quant_act", "moe_grouped_gemm1_swiglu",
+                 "moe_grouped_gemm2_combine", "moe_forward", "moe_workspace_bytes",
+                 "moe_preshuffle_weights", "moe_status_string"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    declared = set(_declared_functions())
+    assert declared <= exported, declared - exported
+    assert declared == set(M.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(M.lib(), name)
+
+
+def cfg(**kw):
+    base = dict(num_experts=288, top_k=8, quant="fp8", hidden=4096, inter=1024, block_m=16)
+    base.update(kw)
+    return M.make_cfg(validate=False, **base)
+
+
+def status(c):
+    return M.validate_cfg(c)
+
+
+def test_valid_configs():
+    assert status(cfg()) == OK
+    assert status(cfg(quant="mxfp4")) == OK
+    assert status(cfg(hidden=4000, inter=1000, hidden_padded=4096, inter_padded=1024)) == OK
+    assert status(cfg(swiglu_limit=math.inf)) == OK
+    for bm in (16, 32, 64, 128):
+        assert status(cfg(block_m=bm)) == OK
+    assert status(cfg(num_experts=1, top_k=1)) == OK
+    assert status(cfg(num_experts=16, top_k=16)) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gate_mode=M.MOE_GATE_INTERLEAVED), UNSUP),
+    (dict(gate_mode=7), UNSUP),
+    (dict(quant=3), UNSUP),
+    (dict(block_m=48), UNSUP),
+    (dict(block_m=256), UNSUP),
+    (dict(swiglu_limit=0.0), UNSUP),
+    (dict(swiglu_limit=-10.0), UNSUP),
+    (dict(swiglu_limit=math.nan), UNSUP),
+    (dict(hidden=4000, hidden_padded=4000), ALIGN),
+    (dict(inter_padded=1000, inter=1000), ALIGN),
+    (dict(hidden=4100, hidden_padded=4096), SHAPE),
+    (dict(top_k=9, num_experts=8), SHAPE),
+    (dict(top_k=17, num_experts=64), SHAPE),
+    (dict(top_k=0), SHAPE),
+    (dict(num_experts=0), SHAPE),
+    (dict(num_experts=1025), SHAPE),
+    (dict(hidden=0), SHAPE),
+])
+def test_rejected_configs(kw, code):
+    assert status(cfg(**kw)) == code
+    # the same rejection through every entry point that takes a cfg
+    c = cfg(**kw)
+    assert M.workspace_bytes(c, 64) == 0
+    lib = M.lib()
+    r = lib.moe_forward(ctypes.byref(c), 64, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, 1 << 40,
+                        None)
+    assert r == code
+
+
+def test_null_cfg():
+    assert M.lib().moe_validate_cfg(None) == NULL
+    assert M.lib().moe_workspace_bytes(None, 4) == 0
+
+
+def test_layout_tag_is_owned_by_the_runner():
+    c = cfg(weight_layout=M.MOE_LAYOUT_CANONICAL)
+    assert status(c) == OK  # a valid cfg ...
+    lib = M.lib()
+    r = lib.moe_forward(ctypes.byref(c), 64, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, 1 << 40, None)
+    assert r == LAYOUT      # ... whose weights were not preshuffled by this library
+    r = lib.moe_grouped_gemm1_swiglu(ctypes.byref(c), 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert r == LAYOUT
+    c2 = cfg(weight_layout=0x1234)
+    r = lib.moe_grouped_gemm2_combine(ctypes.byref(c2), 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      4096, FAKE, 1 << 40, None)
+    assert r == LAYOUT
+
+
+def test_short_workspace_and_bad_strides():
+    c = cfg()
+    need = M.workspace_bytes(c, 64)
+    assert need > 0
+    lib = M.lib()
+    args = lambda ws, ldx=4096, ldo=4096: (ctypes.byref(c), 64, FAKE, ldx, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ldo,
+                                            FAKE, ws, None)
+    assert lib.moe_forward(*args(need - 1)) == WS
+    assert lib.moe_forward(*args(need, ldx=4095)) == SHAPE
+    assert lib.moe_forward(*args(need, ldo=100)) == SHAPE
+    # null pointers are reported before the workspace is looked at
+    assert lib.moe_forward(ctypes.byref(c), 64, None, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, need,
+                           None) == NULL
+    # T = 0 is a valid no-op
+    assert lib.moe_forward(ctypes.byref(c), 0, None, 4096, None, None, None, None, None, None, 4096, None, 0,
+                           None) == OK
+    assert lib.moe_forward(ctypes.byref(c), -1, FAKE, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, FAKE, need,
+                           None) == SHAPE
+
+
+def test_stage_entry_points_validate_before_launch():
+    lib = M.lib()
+    assert lib.moe_route_topk(FAKE, 4, 8, 9, FAKE, FAKE, None) == SHAPE
+    assert lib.moe_route_topk(FAKE, 4, 8, 17, FAKE, FAKE, None) == SHAPE
+    assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == OK
+    assert lib.moe_route_topk(None, 4, 8, 2, FAKE, FAKE, None) == NULL
+    assert lib.moe_permute_align(FAKE, 4, 2, 8, 8, FAKE, FAKE, FAKE, FAKE, None) == UNSUP
+    assert lib.moe_permute_align(FAKE, 4, 2, 2000, 16, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert lib.moe_quant_act(FAKE, 9, 4, 128, 128, 128, 1, FAKE, FAKE, None) == UNSUP
+    assert lib.moe_quant_act(FAKE, 1, 4, 128, 128, 128, 5, FAKE, FAKE, None) == UNSUP
+    assert lib.moe_quant_act(FAKE, 1, 4, 100, 100, 100, 1, FAKE, FAKE, None) == ALIGN
+    assert lib.moe_quant_act(FAKE, 1, 4, 200, 200, 128, 1, FAKE, FAKE, None) == SHAPE
+    assert lib.moe_quant_act(FAKE, 1, 4, 128, 64, 128, 1, FAKE, FAKE, None) == SHAPE
+    assert lib.moe_quant_act(None, 1, 0, 128, 128, 128, 1, None, None, None) == OK
+    assert lib.moe_quant_weights(1, FAKE, 2, 100, 128, FAKE, FAKE, None) == ALIGN
+    assert lib.moe_quant_weights(2, FAKE, 2, 100, 96, FAKE, FAKE, None) == ALIGN
+    assert lib.moe_quant_weights(7, FAKE, 2, 128, 128, FAKE, FAKE, None) == UNSUP
+    c = cfg()
+    assert lib.moe_preshuffle_weights(ctypes.byref(c), 3, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
+    assert lib.moe_preshuffle_weights(ctypes.byref(c), 13, None, FAKE, FAKE, FAKE, None) == NULL
+
+
+def test_status_strings():
+    for code in range(8):
+        s = M.lib().moe_status_string(code).decode()
+        assert s.startswith(M.STATUS_NAMES[code])
+
+
+def test_block_and_buffer_sizes():
+    import oracle as O
+    for P, E, BM in [(512, 288, 16), (32768, 288, 128), (8, 288, 16), (0, 8, 16), (16384, 288, 64), (5, 1, 128)]:
+        assert M.max_blocks(P, E, BM) == O.max_blocks(P, E, BM)
+    c = cfg(quant="fp8", block_m=128)
+    aq, as_ = M.intermediate_bytes(c, 4096)
+    rows = O.max_blocks(4096 * 8, 288, 128) * 128
+    assert (aq, as_) == (rows * 1024, rows * 8 * 4)
+    c = cfg(quant="mxfp4", block_m=128)
+    assert M.intermediate_bytes(c, 4096) == (rows * 512, rows * 32)
+    assert M.preshuffled_bytes(cfg(), 13) == (288 * 2048 * 4096, 288 * 16 * 32 * 4)
+    assert M.preshuffled_bytes(cfg(), 2) == (288 * 4096 * 1024, 288 * 32 * 8 * 4)
+    assert M.preshuffled_bytes(cfg(quant="mxfp4"), 13) == (288 * 2048 * 2048, 288 * 128 * 8 * 64 * 4)
+    assert M.preshuffled_bytes(cfg(quant="mxfp4"), 2) == (288 * 4096 * 512, 288 * 256 * 2 * 64 * 4)
+    # workspace grows with T and covers the GEMM2 rows for gemm2_combine
+    assert M.workspace_bytes(cfg(), 1) < M.workspace_bytes(cfg(), 64) < M.workspace_bytes(cfg(), 4096)
+    assert M.workspace_bytes(cfg(), 64) >= 64 * 8 * 4096 * 4
+
+
+def test_pick_block_m():
+    assert M.pick_block_m(1, 288, 8) == 16
+    assert M.pick_block_m(64, 288, 8) == 16
+    assert M.pick_block_m(4096, 288, 8) == 128
+    assert M.pick_block_m(600, 288, 8) == 32

@@ -1,0 +1,138 @@
+"""GPU parity of the whole layer (moe_forward through the C ABI) against the
+CPU oracle, on seeded inputs small enough for the oracle to finish in
+seconds while still spanning several tiles, ragged tails and padding, plus
+the method's degenerate cases.  Tolerance: max |out - ref| <= tol * RMS of
+the oracle row, tol = 2e-2 (block FP8) or 6e-2 (MXFP4).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from parity_util import assert_rows_close, bf16_to_f32, gpu_weights, log, oracle_weights_cpu
+
+pytestmark = pytest.mark.gpu
+
+M = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    global M
+    import mxfp4_quantized_weights_amd as mod
+    M = mod
+    yield mod
+
+
+def _run(wl, block_m=None, ld_pad=0, stream=None):
+    bm = block_m or M.pick_block_m(wl.T, wl.E, wl.top_k)
+    cfg = M.make_cfg(wl.E, wl.top_k, wl.mode, wl.H, wl.I, wl.Hp, wl.Ip, block_m=bm,
+                     swiglu_limit=wl.swiglu_limit)
+    ew = gpu_weights(M, cfg, wl, source="cpu")
+    x = W.activations(wl)
+    lg = W.router_logits(wl)
+    xd = torch.zeros(wl.T, wl.H + ld_pad, dtype=torch.bfloat16, device="cuda")
+    xd[:, :wl.H] = x.cuda()
+    out = torch.full((wl.T, wl.H + ld_pad), 7.0, dtype=torch.bfloat16, device="cuda")
+    M.moe_forward(cfg, xd[:, :wl.H], lg.cuda(), *ew.tiled(), out=out[:, :wl.H])
+    torch.cuda.synchronize()
+    if ld_pad:
+        assert torch.all(out[:, wl.H:] == 7.0), "columns past H must not be written"
+    return cfg, ew, x, lg, out[:, :wl.H]
+
+
+def _oracle(wl, x, lg):
+    Q = oracle_weights_cpu(wl)
+    return O.moe_forward(x.float().numpy(), lg.numpy(), Q, wl.top_k, wl.swiglu_limit, wl.H, wl.I)
+
+
+TINY = W.WORKLOADS["tiny_fp8"]
+MID = W.Workload("mid", T=200, H=512, I=384, E=16, top_k=4, mode="fp8", outlier_frac=0.01)
+
+CASES = {
+    "tiny_fp8": (TINY, None),
+    "tiny_mxfp4": (TINY.with_(mode="mxfp4"), None),
+    "mid_fp8_bm16": (MID, 16),
+    "mid_fp8_bm64": (MID, 64),
+    "mid_fp8_bm128": (MID, 128),
+    "mid_mxfp4_bm32": (MID.with_(mode="mxfp4"), 32),
+    "mid_mxfp4_bm128": (MID.with_(mode="mxfp4"), 128),
+    "padded_fp8": (W.Workload("pad", T=96, H=400, I=200, E=8, top_k=3, mode="fp8", Hp=512, Ip=256), 16),
+    "padded_mxfp4": (W.Workload("pad", T=96, H=400, I=200, E=8, top_k=3, mode="mxfp4", Hp=512, Ip=384), 32),
+    "skewed_fp8": (W.Workload("skew", T=160, H=256, I=256, E=32, top_k=8, mode="fp8", zipf_s=1.2), 64),
+    "no_limit_fp8": (MID.with_(swiglu_limit=math.inf, T=64), 16),
+    "tight_limit_mxfp4": (MID.with_(swiglu_limit=0.5, T=64, mode="mxfp4"), 16),
+    "single_token_fp8": (MID.with_(T=1), 16),
+    "single_expert_fp8": (MID.with_(E=1, top_k=1, T=40), 16),
+    "all_experts_mxfp4": (W.Workload("kE", T=24, H=256, I=128, E=16, top_k=16, mode="mxfp4"), 16),
+    "big_k_ragged_fp8": (W.Workload("rag", T=37, H=384, I=640, E=24, top_k=5, mode="fp8"), 32),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_forward_matches_oracle(name):
+    wl, bm = CASES[name]
+    log(f"forward {name}: {W.describe(wl)} block_m={bm}")
+    _, _, x, lg, out = _run(wl, bm)
+    ref = _oracle(wl, x, lg)
+    assert_rows_close(bf16_to_f32(out), ref, wl.mode, name)
+
+
+def test_forward_with_row_strides():
+    wl = MID.with_(T=50)
+    log(f"forward strided: {W.describe(wl)}")
+    _, _, x, lg, out = _run(wl, 16, ld_pad=72)
+    assert_rows_close(bf16_to_f32(out), _oracle(wl, x, lg), wl.mode, "strided")
+
+
+@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+def test_forward_zero_input(mode):
+    wl = MID.with_(T=33, mode=mode)
+    cfg = M.make_cfg(wl.E, wl.top_k, mode, wl.H, wl.I, block_m=16)
+    ew = gpu_weights(M, cfg, wl, source="cpu")
+    out = M.moe_forward(cfg, torch.zeros(wl.T, wl.H, dtype=torch.bfloat16, device="cuda"),
+                        W.router_logits(wl).cuda(), *ew.tiled())
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+
+
+def test_forward_zero_tokens():
+    wl = MID
+    cfg = M.make_cfg(wl.E, wl.top_k, "fp8", wl.H, wl.I, block_m=16)
+    ew = gpu_weights(M, cfg, wl.with_(E=wl.E), source="cpu")
+    out = M.moe_forward(cfg, torch.zeros(0, wl.H, dtype=torch.bfloat16, device="cuda"),
+                        torch.zeros(0, wl.E, device="cuda"), *ew.tiled())
+    torch.cuda.synchronize()
+    assert out.shape == (0, wl.H)
+
+
+@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+def test_forward_repeatable_and_equal_to_stages(mode):
+    """Two runs give identical bits, and moe_forward equals the stage entry
+    points called one by one."""
+    wl = MID.with_(mode=mode, T=120)
+    log(f"repeatability {W.describe(wl)}")
+    cfg, ew, x, lg, out1 = _run(wl, 32)
+    xd, lgd = x.cuda(), lg.cuda()
+    out2 = M.moe_forward(cfg, xd, lgd, *ew.tiled())
+    ids, wts = M.moe_route_topk(lgd, wl.top_k)
+    sid, bexp, offs, npp = M.moe_permute_align(ids, wl.E, 32)
+    xq, xs = M.moe_quant_act(xd, wl.Hp, mode)
+    aq, as_ = M.moe_grouped_gemm1_swiglu(cfg, wl.T, xq, xs, sid, bexp, npp, ew.w13, ew.w13_scale)
+    out3 = M.moe_grouped_gemm2_combine(cfg, wl.T, aq, as_, sid, bexp, npp, ew.w2, ew.w2_scale, wts)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
+
+
+def test_block_m_choices_agree():
+    wl = MID.with_(T=150)
+    outs = []
+    for bm in (16, 32, 64, 128):
+        outs.append(bf16_to_f32(_run(wl, bm)[4]))
+    ref = _oracle(wl, W.activations(wl), W.router_logits(wl))
+    for o in outs:
+        assert_rows_close(o, ref, "fp8", "block_m sweep")

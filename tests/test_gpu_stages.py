@@ -1,0 +1,234 @@
+"""GPU parity of each stage of the layer against the CPU oracle (through the C ABI).
+
+Bit-exact: routing ids, permutation arrays, activation and weight quantiser
+bytes and scales, the preshuffled layout.  Tolerance: routing weights
+(float, rtol 2e-6) and the GEMM1 intermediate codes (accumulation order may
+move a code by one step at a rounding boundary).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from parity_util import log
+
+pytestmark = pytest.mark.gpu
+
+M = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    global M
+    import mxfp4_quantized_weights_amd as mod
+    M = mod
+    yield mod
+
+
+def _spread_values(rng, rows, cols):
+    """Rows of very different magnitudes, including fp32 subnormal rows, an
+    all-zero group, negative zeros and exact ties."""
+    v = rng.standard_normal((rows, cols)).astype(np.float32)
+    v *= np.exp2(rng.integers(-40, 40, (rows, 1))).astype(np.float32)
+    v[0] *= np.float32(1e-38)          # subnormal row
+    v[1, :] = 0.0
+    v[2, :64] = -0.0
+    v[3, 5] = -0.0
+    v[4, :] = rng.integers(-8, 9, cols).astype(np.float32)  # integers: exact halfway cases
+    return v
+
+
+@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quant_act_bitexact(mode, dtype):
+    log(f"quant_act mode={mode} dtype={dtype}")
+    rng = np.random.default_rng(100)
+    rows, cols, cols_p, ld = 37, 300, 384, 320
+    v = _spread_values(rng, rows, ld)
+    t = torch.from_numpy(v)
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    vals = t.float().numpy()[:, :cols]
+    x = t.cuda()[:, :cols]
+    q, s = M.moe_quant_act(x, cols_p, mode)
+    torch.cuda.synchronize()
+    qo, so = O.quant_act(mode, O.pad_cols(vals, cols_p))
+    assert np.array_equal(q.cpu().numpy(), qo)
+    if mode == "fp8":
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    else:
+        assert np.array_equal(s.cpu().numpy(), so)
+
+
+@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+def test_quant_weights_bitexact(mode):
+    log(f"quant_weights mode={mode}")
+    rng = np.random.default_rng(101)
+    E, N, K = 3, 256, 384
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(np.float32)
+    w[1, :128, :128] = 0.0
+    w[2, 128:, 256:] *= 1e4
+    w[0, 5, 7] = -0.0
+    q, s = M.moe_quant_weights(torch.from_numpy(w).cuda(), mode)
+    torch.cuda.synchronize()
+    for e in range(E):
+        if mode == "fp8":
+            qo, so = O.quant_fp8_weight(w[e])
+            assert np.array_equal(s[e].cpu().numpy().view(np.uint32), so.view(np.uint32))
+        else:
+            qo, so = O.quant_mxfp4_rows(w[e])
+            assert np.array_equal(s[e].cpu().numpy(), so)
+        assert np.array_equal(q[e].cpu().numpy(), qo)
+
+
+@pytest.mark.parametrize("T,E,k", [(64, 288, 8), (4096, 288, 8), (33, 8, 2), (7, 1, 1), (5, 16, 16),
+                                   (3, 1024, 16), (129, 65, 3)])
+def test_route_topk(T, E, k):
+    log(f"route_topk T={T} E={E} k={k}")
+    rng = np.random.default_rng(T * 1000 + E)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if T > 10:
+        lg[:T // 3] = rng.integers(-2, 3, (T // 3, E)).astype(np.float32)  # heavy ties
+        lg[T // 3, :] = -0.0
+        lg[T // 3, ::2] = 0.0
+    ids, w = M.moe_route_topk(torch.from_numpy(lg).cuda(), k)
+    torch.cuda.synchronize()
+    ido, wo = O.route_topk(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), ido)
+    assert np.allclose(w.cpu().numpy(), wo, rtol=2e-6, atol=0)
+
+
+@pytest.mark.parametrize("T,E,k,BM,skew", [(1, 288, 8, 16, False), (64, 288, 8, 16, False),
+                                           (4096, 288, 8, 128, False), (2048, 288, 8, 64, True),
+                                           (300, 8, 2, 32, False), (0, 8, 2, 16, False),
+                                           (1000, 1024, 16, 16, False), (17, 1, 1, 128, False),
+                                           (513, 16, 4, 16, True)])
+def test_permute_align_bitexact(T, E, k, BM, skew):
+    log(f"permute_align T={T} E={E} k={k} BM={BM} skew={skew}")
+    rng = np.random.default_rng(T + 7 * E + BM)
+    if skew:
+        p = (np.arange(1, E + 1) ** -1.5)
+        p /= p.sum()
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32) \
+            if T else np.zeros((0, k), np.int32)
+    else:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32) \
+            if T else np.zeros((0, k), np.int32)
+    sid, bexp, offs, npp = M.moe_permute_align(torch.from_numpy(ids).cuda(), E, BM)
+    torch.cuda.synchronize()
+    so, bo, oo, no = O.permute_align(ids, E, BM)
+    assert int(npp.item()) == no
+    assert np.array_equal(offs.cpu().numpy(), oo)
+    assert np.array_equal(sid.cpu().numpy(), so)
+    assert np.array_equal(bexp.cpu().numpy(), bo)
+
+
+def _tiled_fp8_reference(q, E, N, K):
+    """The documented TILED_V1 FP8 layout, rebuilt on the host."""
+    KB, NT = K // 128, N // 16
+    out = np.zeros(E * N * K, np.uint8)
+    t = q.reshape(E, NT, 16, KB, 4, 2, 16)  # e, nt, row, kb, lane/16, h, byte
+    # out[e, nt, kb, h, lane(=g*16+row), byte]
+    out = t.transpose(0, 1, 3, 5, 4, 2, 6).reshape(-1)
+    return out
+
+
+def _tiled_mx_reference(q, s, E, N, K):
+    KB, NT = K // 128, N // 16
+    t = q.reshape(E, NT, 16, KB, 4, 16)  # e, nt, row, kb, lane/16, byte
+    w = t.transpose(0, 1, 3, 4, 2, 5).reshape(-1)
+    KB4 = (KB + 3) // 4
+    sc = np.zeros((E, NT, KB4, 64, 4), np.uint8)
+    s5 = s.reshape(E, NT, 16, KB, 4)  # e, nt, row, kb, group-in-block
+    for kb in range(KB):
+        for g in range(4):
+            sc[:, :, kb // 4, g * 16:(g + 1) * 16, kb % 4] = s5[:, :, :, kb, g]
+    return w, sc.reshape(-1)
+
+
+@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+def test_preshuffle_layout(mode):
+    log(f"preshuffle mode={mode}")
+    rng = np.random.default_rng(102)
+    E, Hp, Ip = 3, 384, 640
+    cfg = M.make_cfg(E, 2, mode, Hp, Ip)
+    for which, N, K in ((13, 2 * Ip, Hp), (2, Hp, Ip)):
+        if mode == "fp8":
+            q = rng.integers(0, 256, (E, N, K), dtype=np.uint8)
+            s = rng.standard_normal((E, N // 128, K // 128)).astype(np.float32)
+        else:
+            q = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+            s = rng.integers(0, 255, (E, N, K // 32), dtype=np.uint8)
+        qo, so = M.moe_preshuffle_weights(cfg, which, torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda())
+        torch.cuda.synchronize()
+        if mode == "fp8":
+            assert np.array_equal(qo.cpu().numpy(), _tiled_fp8_reference(q, E, N, K))
+            assert np.array_equal(so.cpu().numpy().view(np.float32), s.reshape(-1))
+        else:
+            w_ref, s_ref = _tiled_mx_reference(q, s, E, N, K)
+            assert np.array_equal(qo.cpu().numpy(), w_ref)
+            assert np.array_equal(so.cpu().numpy(), s_ref)
+
+
+@pytest.mark.parametrize("mode,BM", [("fp8", 16), ("fp8", 64), ("mxfp4", 32), ("mxfp4", 128)])
+def test_gemm1_swiglu_stage(mode, BM):
+    """GEMM1 + clamped SwiGLU + re-quantisation, fed by the (bit-exact) GPU
+    routing/permutation/quantisation stages; the oracle recomputes everything
+    from the raw inputs."""
+    wl = W.Workload("gemm1", T=48, H=512, I=384, E=8, top_k=2, mode=mode, outlier_frac=0.02)
+    log(f"gemm1 stage {W.describe(wl)} BM={BM}")
+    cfg = M.make_cfg(wl.E, wl.top_k, mode, wl.H, wl.I, block_m=BM)
+    x = W.activations(wl)
+    lg = W.router_logits(wl)
+    from parity_util import gpu_weights, oracle_weights_cpu
+    ew = gpu_weights(M, cfg, wl, source="cpu")
+    xd, lgd = x.cuda(), lg.cuda()
+    ids, wts = M.moe_route_topk(lgd, wl.top_k)
+    sid, bexp, offs, npp = M.moe_permute_align(ids, wl.E, BM)
+    xq, xs = M.moe_quant_act(xd, wl.Hp, mode)
+    aq, as_ = M.moe_grouped_gemm1_swiglu(cfg, wl.T, xq, xs, sid, bexp, npp, ew.w13, ew.w13_scale)
+    torch.cuda.synchronize()
+    Q = oracle_weights_cpu(wl)
+    _, st = O.moe_forward(x.float().numpy(), lg.numpy(), Q, wl.top_k, wl.swiglu_limit, wl.H, wl.I,
+                          return_stages=True)
+    sid_h = sid.cpu().numpy()
+    P = wl.T * wl.top_k
+    rows = aq.numel() // (wl.Ip if mode == "fp8" else wl.Ip // 2)
+    aq_h = aq.cpu().numpy().reshape(rows, -1)
+    if mode == "fp8":
+        as_h = as_.cpu().numpy().view(np.float32).reshape(rows, -1)
+    else:
+        as_h = as_.cpu().numpy().reshape(rows, -1)
+    total = mism = 0
+    worst_scale = worst_val = 0.0
+    for r in range(int(npp.item())):
+        f = int(sid_h[r])
+        if f >= P:
+            assert np.all(aq_h[r] == 0) and np.all(as_h[r] == 0), "pad rows are zero"
+            continue
+        qo, so = st["aq"][(f // wl.top_k, f % wl.top_k)]
+        if mode == "fp8":
+            # the scale is amax/448 of the fp32 intermediate: it inherits the
+            # GEMM's accumulation-order difference
+            rel = np.abs(as_h[r].astype(np.float64) - so) / np.maximum(so, 1e-30)
+            worst_scale = max(worst_scale, float(rel.max()))
+            dg = O.dequant_fp8_rows(aq_h[r][None], as_h[r][None])[0]
+            do = O.dequant_fp8_rows(qo[None], so[None])[0]
+            step = 32.0 / 448.0          # one code step at the top binade, relative to amax
+        else:
+            dg = O.dequant_mxfp4_rows(aq_h[r][None], as_h[r][None])[0]
+            do = O.dequant_mxfp4_rows(qo[None], so[None])[0]
+            step = 2.0 / 4.0             # E2M1 step 2 at the top, amax >= 4 units
+        amax = np.abs(do).max()
+        total += aq_h[r].size
+        mism += int(np.count_nonzero(aq_h[r] != qo))
+        if amax > 0:
+            worst_val = max(worst_val, float(np.abs(dg - do).max() / amax))
+    log(f"  intermediate: {mism} of {total} code bytes differ; worst |deq diff|/amax {worst_val:.3e}; "
+        f"worst FP8 scale rel diff {worst_scale:.2e}")
+    # accumulation-order differences move a code by at most one step at a rounding boundary
+    assert worst_val <= step * 1.01
+    assert mism <= max(8, 0.01 * total)
+    assert worst_scale <= 1e-3
+    assert mism <= max(8, 0.01 * total)
