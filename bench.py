@@ -37,7 +37,23 @@ def parse():
     ap.add_argument("--block-m", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=4, help="tokens in the oracle's timed sample (0 = skip)")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 device-to-device copies of MIB MiB (calibrates HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    """Plain device copy of known size: FETCH_SIZE / WRITE_SIZE of these
+    dispatches give the counters' scale against true bytes."""
+    import torch
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_dispatch": n * 4}), flush=True)
 
 
 def algorithmic_bytes(wl, ids, M):
@@ -64,6 +80,25 @@ def algorithmic_bytes(wl, ids, M):
     gemm2 = active * w2 + aq + P * Hp * 4
     return dict(active_experts=active, layer=layer, gemm1=gemm1, gemm2=gemm2,
                 w13_per_expert=w13, w2_per_expert=w2)
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (calibrated against a plain
+    copy), or None when there is none or the GEMM source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    src = os.path.join(ROOT, "mxfp4_quantized_weights_amd", "csrc", "gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    for line in open(path):
+        if line.startswith("TRAFFIC "):
+            kv = dict(t.split("=", 1) for t in line.split()[1:])
+            if kv.get("gemm_src_sha256") != sha:
+                return None
+            return int(kv["read_bytes"]) + int(kv["write_bytes"])
+    return None
 
 
 def cpu_baseline(wl, x, lg, sample_tokens: int):
@@ -93,6 +128,9 @@ def cpu_baseline(wl, x, lg, sample_tokens: int):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
               "sharding is described, not built", file=sys.stderr)
@@ -205,7 +243,8 @@ def main():
         dur = kern[dom] * 1e-6
         gbs = nbytes["gemm1"] / dur / 1e9
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "moe_gemm_kernel (GEMM1+SwiGLU)",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(wl.name),
+                "kernel": "moe_gemm (GEMM1 + clamped SwiGLU + re-quantisation)",
                 "kernel_us": round(kern[dom], 2), "algorithmic_bytes": nbytes["gemm1"]}
     res = {
         "metric": "MoE layer tokens/s + effective TFLOP/s (% of MFMA/HBM roofline), 1 MI355X",

@@ -28,6 +28,8 @@
  * Conventions for every entry point:
  *   - Every pointer argument is DEVICE memory owned by the caller, except the
  *     moe_cfg_t pointer, which is host memory read during the call only.
+ *     Device buffers must be 16-byte aligned (any hipMalloc / torch
+ *     allocation is); row strides are in elements.
  *   - `stream` is a hipStream_t (NULL = the default stream).  All work is
  *     enqueued on it; no call synchronises, allocates device memory or reads
  *     device memory back to the host, so moe_forward can be captured in a
@@ -140,7 +142,9 @@ moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t t
  *   block_expert int32 [nb]: expert of each block, -1 past the last segment;
  *   expert_offsets int32 [E+1]: exclusive scan of the padded segment sizes;
  *   num_post_padded int32 [1]: expert_offsets[E], left on the device.
- * Experts with no pairs get no block.  ids outside [0, E) are skipped. */
+ * Experts with no pairs get no block.  ids outside [0, E) are skipped (the
+ * pair appears nowhere); a token that lists an expert twice is allowed and
+ * its pairs keep f order (slower path).  E <= 1024. */
 moe_status_t moe_permute_align(const int32_t* ids, int32_t T, int32_t top_k, int32_t E,
                                int32_t block_m, int32_t* sorted_ids, int32_t* block_expert,
                                int32_t* expert_offsets, int32_t* num_post_padded,
@@ -166,7 +170,7 @@ moe_status_t moe_quant_act(const void* in, int32_t in_dtype, int32_t rows, int32
  *   FP8:   N % 128 == 0, K % 128 == 0; q u8 [E, N, K]; scales f32
  *          [E, N/128, K/128] (dequant multipliers), one per [128,128] block,
  *          same arithmetic as moe_quant_act with the block as the group.
- *   MXFP4: K % 32 == 0; q u8 [E, N, K/2]; scales u8 [E, N, K/32]. */
+ *   MXFP4: K % 128 == 0; q u8 [E, N, K/2]; scales u8 [E, N, K/32]. */
 moe_status_t moe_quant_weights(int32_t quant_mode, const float* w, int32_t E, int32_t N,
                                int32_t K, void* q, void* scales, void* stream);
 

@@ -21,7 +21,7 @@ ARCH = "gfx950"
 # Correctly rounded fp32 division: the quantisers' s = amax/448 and v/s must
 # be IEEE divisions to be reproducible.  Denormals are kept (HIP default).
 HIPCC_FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Wall", "-Wno-unused-function",

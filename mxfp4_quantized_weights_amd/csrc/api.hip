@@ -202,8 +202,8 @@ moe_status_t moe_permute_align(const int32_t* ids, int32_t T, int32_t top_k, int
   if (!expert_offsets || !num_post_padded) return MOE_ERR_NULL;
   if (P > 0 && (!ids || !sorted_ids || !block_expert)) return MOE_ERR_NULL;
   const int32_t nb = max_blocks(P, E, block_m);
-  return hip_status(moe::launch_permute_align(ids, (int)P, E, block_m, nb, sorted_ids, block_expert, expert_offsets,
-                                              num_post_padded, as_stream(stream)));
+  return hip_status(moe::launch_permute_align(ids, T, top_k, E, block_m, nb, sorted_ids, block_expert,
+                                              expert_offsets, num_post_padded, as_stream(stream)));
 }
 
 moe_status_t moe_quant_act(const void* in, int32_t in_dtype, int32_t rows, int32_t cols, int64_t ld_in,
@@ -341,7 +341,7 @@ moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, in
   const int mode = cfg->quant_mode == MOE_QUANT_FP8_BLOCK ? moe::kQuantFp8 : moe::kQuantMx;
   hipError_t e;
   if ((e = moe::launch_route_topk(router_logits, T, E, k, ids, wts, s)) != hipSuccess) return MOE_ERR_HIP;
-  if ((e = moe::launch_permute_align(ids, (int)P, E, BM, nb, sorted, bexp, offs, npp, s)) != hipSuccess)
+  if ((e = moe::launch_permute_align(ids, T, k, E, BM, nb, sorted, bexp, offs, npp, s)) != hipSuccess)
     return MOE_ERR_HIP;
   if ((e = moe::launch_quant_rows(x_bf16, true, T, cfg->pad.hidden, ld_x, cfg->pad.hidden_padded, mode, xq, xs, s)) !=
       hipSuccess)

@@ -114,10 +114,22 @@ __device__ __forceinline__ float swiglu_clamped(float g, float u, float L) {
   return silu_f32(gc) * uc;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over aligned groups of WIDTH lanes (4 or 16), every lane of the
+// group receives it.  DPP quad swaps, then half-row and row mirrors.
 template <int WIDTH>
-__device__ __forceinline__ float max_xor(float v) {
-#pragma unroll
-  for (int off = 1; off < WIDTH; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(WIDTH == 4 || WIDTH == 16, "group of 4 or 16 lanes");
+  v = fmaxf(v, dpp_f32<0xB1>(v));     // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));     // quad_perm [2,3,0,1]
+  if constexpr (WIDTH == 16) {
+    v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+    v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+  }
   return v;
 }
 

@@ -18,7 +18,7 @@ constexpr int kQuantFp8F16 = 3;
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);
 
-hipError_t launch_permute_align(const int32_t* ids, int P, int E, int block_m, int nb,
+hipError_t launch_permute_align(const int32_t* ids, int T, int k, int E, int block_m, int nb,
                                 int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets,
                                 int32_t* npp, hipStream_t s);
 

@@ -16,76 +16,118 @@
 
 namespace moe {
 
-template <bool BF16>
-__device__ __forceinline__ float2 load_pair(const void* in, int64_t row, int64_t ld, int col, int cols) {
-  float2 r = make_float2(0.0f, 0.0f);
+// Eight consecutive elements of one row as fp32 (zeros past `cols`).  VEC:
+// the row start and stride allow 16-byte loads.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void load8(const void* in, int64_t row, int64_t ld, int col, int cols, float (&v)[8]) {
   if (BF16) {
-    const uint16_t* p = (const uint16_t*)in + row * ld;
-    if (col < cols) r.x = bf16_to_f32(p[col]);
-    if (col + 1 < cols) r.y = bf16_to_f32(p[col + 1]);
-  } else {
-    const float* p = (const float*)in + row * ld;
-    if (col < cols) r.x = p[col];
-    if (col + 1 < cols) r.y = p[col + 1];
-  }
-  return r;
-}
-
-// One wave per 128-column chunk of one row; lane l holds columns 2l, 2l+1.
-// FP8: the chunk is one group.  MX: the chunk is four groups of 16 lanes.
-template <bool BF16, int MODE>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ in, int64_t rows, int cols,
-                                                         int64_t ld_in, int cols_padded,
-                                                         uint8_t* __restrict__ q, void* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
-  const int chunks = cols_padded / 128;
-  const int64_t total = rows * chunks;
-  for (int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); c < total; c += (int64_t)gridDim.x * 4) {
-    const int64_t row = c / chunks;
-    const int g = (int)(c % chunks);
-    const int col = g * 128 + 2 * lane;
-    float2 v = load_pair<BF16>(in, row, ld_in, col, cols);
-    float a = fmaxf(fabsf(v.x), fabsf(v.y));
-    if (MODE == kQuantFp8) {
-      a = max_xor<64>(a);
-      uint32_t c0 = 0, c1 = 0;
-      float s = 0.0f;
-      if (a > 0.0f) {
-        s = a / kE4M3Max;
-        c0 = fp8_quant(v.x, s);
-        c1 = fp8_quant(v.y, s);
+    const uint16_t* p = (const uint16_t*)in + row * ld + col;
+    if (VEC && col + 8 <= cols) {
+      const uint4 w = *(const uint4*)p;
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(u[i] << 16);
+        v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
       }
-      *(uint16_t*)(q + row * (int64_t)cols_padded + col) = (uint16_t)(c0 | (c1 << 8));
-      if (lane == 0) ((float*)scales)[row * chunks + g] = s;
     } else {
-      a = max_xor<16>(a);
-      uint32_t b = e8m0_byte(a);
-      float inv = e8m0_inverse(b);
-      uint32_t c0 = mx_quant(v.x, inv), c1 = mx_quant(v.y, inv);
-      q[row * (int64_t)(cols_padded / 2) + col / 2] = (uint8_t)(c0 | (c1 << 4));
-      if ((lane & 15) == 0) ((uint8_t*)scales)[row * (int64_t)(cols_padded / 32) + g * 4 + (lane >> 4)] = (uint8_t)b;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (col + i < cols) ? bf16_to_f32(p[i]) : 0.0f;
+    }
+  } else {
+    const float* p = (const float*)in + row * ld + col;
+    if (VEC && col + 8 <= cols) {
+      const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (col + i < cols) ? p[i] : 0.0f;
     }
   }
 }
 
+// A wave quantises four 128-column units (16 lanes each, 8 elements per
+// lane); a unit is one FP8 group or four MX groups of 4 lanes.
+template <bool BF16, bool VEC, int MODE>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ in, int64_t rows, int cols,
+                                                         int64_t ld_in, int cols_padded,
+                                                         uint8_t* __restrict__ q, void* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int units = cols_padded / 128;
+  const int64_t total = rows * units;
+  const int64_t stride = (int64_t)gridDim.x * 16;
+  for (int64_t u = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4); u - (lane >> 4) < total;
+       u += stride) {
+    const bool live = u < total;
+    const int64_t row = live ? u / units : 0;
+    const int g = live ? (int)(u % units) : 0;
+    const int col = g * 128 + (lane & 15) * 8;
+    float v[8];
+    if (live) {
+      load8<BF16, VEC>(in, row, ld_in, col, cols, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+    if constexpr (MODE == kQuantFp8) {
+      a = group_max<16>(a);
+      uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      const float s = (a > 0.0f) ? a / kE4M3Max : 0.0f;
+      if (a > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = fp8_quant(v[i], s);
+      }
+      if (live) {
+        *(uint2*)(q + row * (int64_t)cols_padded + col) =
+            make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+        if ((lane & 15) == 0) ((float*)scales)[row * units + g] = s;
+      }
+    } else {
+      a = group_max<4>(a);
+      const uint32_t b = e8m0_byte(a);
+      const float inv = e8m0_inverse(b);
+      uint32_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= mx_quant(v[i], inv) << (4 * i);
+      if (live) {
+        *(uint32_t*)(q + row * (int64_t)(cols_padded / 2) + col / 2) = w;
+        if ((lane & 3) == 0) ((uint8_t*)scales)[row * (int64_t)(cols_padded / 32) + col / 32] = (uint8_t)b;
+      }
+    }
+  }
+}
+
+template <bool BF16, bool VEC>
+static void launch_quant_rows_t(dim3 grid, hipStream_t s, const void* in, int64_t rows, int cols, int64_t ld_in,
+                                int cols_padded, int mode, uint8_t* q, void* scales) {
+  if (mode == kQuantFp8)
+    hipLaunchKernelGGL((quant_rows_kernel<BF16, VEC, kQuantFp8>), grid, dim3(256), 0, s, in, rows, cols, ld_in,
+                       cols_padded, q, scales);
+  else
+    hipLaunchKernelGGL((quant_rows_kernel<BF16, VEC, kQuantMx>), grid, dim3(256), 0, s, in, rows, cols, ld_in,
+                       cols_padded, q, scales);
+}
+
 hipError_t launch_quant_rows(const void* in, bool in_is_bf16, int64_t rows, int cols, int64_t ld_in,
                              int cols_padded, int mode, void* q, void* scales, hipStream_t s) {
-  int64_t waves = rows * (cols_padded / 128);
-  int64_t blocks = (waves + 3) / 4;
+  const int64_t units = rows * (cols_padded / 128);
+  int64_t blocks = (units + 15) / 16;  // 16 units per workgroup
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;
-  dim3 grid((unsigned)blocks), block(256);
+  dim3 grid((unsigned)blocks);
   uint8_t* qb = (uint8_t*)q;
+  const int esize = in_is_bf16 ? 2 : 4;
+  const bool vec = ((uintptr_t)in % 16 == 0) && ((ld_in * esize) % 16 == 0);
   if (in_is_bf16) {
-    if (mode == kQuantFp8)
-      hipLaunchKernelGGL((quant_rows_kernel<true, kQuantFp8>), grid, block, 0, s, in, rows, cols, ld_in, cols_padded, qb, scales);
-    else
-      hipLaunchKernelGGL((quant_rows_kernel<true, kQuantMx>), grid, block, 0, s, in, rows, cols, ld_in, cols_padded, qb, scales);
+    if (vec) launch_quant_rows_t<true, true>(grid, s, in, rows, cols, ld_in, cols_padded, mode, qb, scales);
+    else launch_quant_rows_t<true, false>(grid, s, in, rows, cols, ld_in, cols_padded, mode, qb, scales);
   } else {
-    if (mode == kQuantFp8)
-      hipLaunchKernelGGL((quant_rows_kernel<false, kQuantFp8>), grid, block, 0, s, in, rows, cols, ld_in, cols_padded, qb, scales);
-    else
-      hipLaunchKernelGGL((quant_rows_kernel<false, kQuantMx>), grid, block, 0, s, in, rows, cols, ld_in, cols_padded, qb, scales);
+    if (vec) launch_quant_rows_t<false, true>(grid, s, in, rows, cols, ld_in, cols_padded, mode, qb, scales);
+    else launch_quant_rows_t<false, false>(grid, s, in, rows, cols, ld_in, cols_padded, mode, qb, scales);
   }
   return hipGetLastError();
 }
@@ -110,7 +152,10 @@ __global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const float* __re
     v[i] = src[i];
     a = fmaxf(a, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
   }
-  a = max_xor<64>(a);
+  a = group_max<16>(a);
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 16)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 32)));
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 48)));
   if ((t & 63) == 0) red[t >> 6] = a;
   __syncthreads();
   a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));

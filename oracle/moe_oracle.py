@@ -324,6 +324,8 @@ def permute_align(ids: np.ndarray, num_experts: int, block_m: int):
     multiple of BM; experts with no pairs get no block.  Every block of BM rows
     belongs to one expert (block_expert).  Arrays are sized for the worst case
     (max_blocks blocks); entries past num_post_padded hold P / -1.
+    Reading for ids outside [0, E) (not produced by routing): such pairs are
+    not routed to any expert and appear nowhere in sorted_ids.
     Returns (sorted_ids int32 [max_blocks*BM], block_expert int32 [max_blocks],
              offsets int32 [E+1], num_post_padded int).
     """
@@ -333,7 +335,8 @@ def permute_align(ids: np.ndarray, num_experts: int, block_m: int):
     nb = max_blocks(P, num_experts, block_m)
     counts = np.zeros(num_experts, np.int64)
     for e in flat:
-        counts[e] += 1
+        if 0 <= e < num_experts:
+            counts[e] += 1
     padded = ((counts + block_m - 1) // block_m) * block_m
     offsets = np.zeros(num_experts + 1, np.int64)
     offsets[1:] = np.cumsum(padded)
@@ -342,6 +345,8 @@ def permute_align(ids: np.ndarray, num_experts: int, block_m: int):
     cursor = offsets[:-1].copy()
     for f in range(P):
         e = flat[f]
+        if not 0 <= e < num_experts:
+            continue
         sorted_ids[cursor[e]] = f
         cursor[e] += 1
     for e in range(num_experts):

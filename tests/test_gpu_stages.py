@@ -103,11 +103,21 @@ def test_route_topk(T, E, k):
                                            (4096, 288, 8, 128, False), (2048, 288, 8, 64, True),
                                            (300, 8, 2, 32, False), (0, 8, 2, 16, False),
                                            (1000, 1024, 16, 16, False), (17, 1, 1, 128, False),
-                                           (513, 16, 4, 16, True)])
+                                           (513, 16, 4, 16, True), (200, 8, 4, 16, "dup"),
+                                           (3000, 64, 8, 32, "dup"), (100, 16, 3, 64, "bad")])
 def test_permute_align_bitexact(T, E, k, BM, skew):
+    """Includes tokens that list an expert twice ("dup": the pairs keep f
+    order) and ids outside [0, E) ("bad": skipped by both sides)."""
     log(f"permute_align T={T} E={E} k={k} BM={BM} skew={skew}")
     rng = np.random.default_rng(T + 7 * E + BM)
-    if skew:
+    if skew == "dup":
+        ids = rng.integers(0, E, (T, k)).astype(np.int32)
+        ids[::3, 1] = ids[::3, 0]
+    elif skew == "bad":
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        ids[::5, 0] = -1
+        ids[1::7, 1] = E + 3
+    elif skew:
         p = (np.arange(1, E + 1) ** -1.5)
         p /= p.sum()
         ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32) \

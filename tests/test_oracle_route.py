@@ -148,3 +148,17 @@ def test_max_blocks_bound_is_tight_enough():
     assert O.max_blocks(288, 288, 128) == 288
     assert O.max_blocks(8, 288, 16) == 8
     assert O.max_blocks(512, 288, 16) == (512 + 288 * 15) // 16
+
+
+def test_permute_align_skips_out_of_range_ids():
+    ids = np.array([[0, 5], [-1, 1], [1, 0]], np.int32)
+    sorted_ids, block_expert, offsets, npp = O.permute_align(ids, 2, 16)
+    assert npp == 32 and offsets.tolist() == [0, 16, 32]
+    assert sorted_ids[:3].tolist() == [0, 5, 6] and np.all(sorted_ids[3:16] == 6)
+    assert sorted_ids[16:18].tolist() == [3, 4] and np.all(sorted_ids[18:] == 6)
+
+
+def test_permute_align_duplicate_experts_keep_f_order():
+    ids = np.array([[1, 1], [0, 1]], np.int32)
+    sorted_ids, _, offsets, _ = O.permute_align(ids, 2, 16)
+    assert sorted_ids[offsets[1]:offsets[1] + 3].tolist() == [0, 1, 3]
