@@ -170,19 +170,19 @@ __device__ __forceinline__ void load_w_scales(const GemmArgs& p, int e, const in
 // ---------------------------------------------------------------------------
 
 // GEMM1: gate in acc[m][jj], up in acc[m][jj+2] (jj = 0, 1) for intermediate
-// column 32*wave + 16*jj + lane%16 of the N tile.  SwiGLU, re-quantise the
-// row per 1x128 (FP8, amax across the 4 waves) or per 1x32 (MX, the wave's
-// own 32 columns), stage the codes in LDS, write 16-byte chunks.
-template <int MODE, int BM>
-__device__ __forceinline__ void epilogue_gemm1(const GemmArgs& p, const v4f (&acc)[BM / 16][4], float (*red)[BM],
-                                               uint8_t* stage, int row0, int nt, int wave) {
-  constexpr int MT = BM / 16;
+// column 32*wn + 16*jj + lane%16 of the N tile, rows rbase + m*16 +
+// 4*(lane/16) + i.  SwiGLU, re-quantise the row per 1x128 (FP8, amax across
+// the 4 column waves) or per 1x32 (MX, the wave's own 32 columns), stage the
+// codes in LDS, write 16-byte chunks.  NTH threads take part.
+template <int MODE, int BM, int MTW, int NTH>
+__device__ __forceinline__ void epilogue_gemm1(const GemmArgs& p, const v4f (&acc)[MTW][4], float (*red)[BM],
+                                               uint8_t* stage, int row0, int nt, int wn, int rbase) {
   const int tid = threadIdx.x, lane = tid & 63;
   const float L = p.limit;
-  float av[MT][2][4];
-  float rmax[MT][4];
+  float av[MTW][2][4];
+  float rmax[MTW][4];
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+  for (int m = 0; m < MTW; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float mx = 0.0f;
@@ -197,47 +197,47 @@ __device__ __forceinline__ void epilogue_gemm1(const GemmArgs& p, const v4f (&ac
   if constexpr (MODE != kQuantMx) {
     if ((lane & 15) == 0) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+      for (int m = 0; m < MTW; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][m * 16 + 4 * (lane >> 4) + i] = rmax[m][i];
+        for (int i = 0; i < 4; ++i) red[wn][rbase + m * 16 + 4 * (lane >> 4) + i] = rmax[m][i];
     }
     __syncthreads();
     const int nsc = p.Ip / 128;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MTW; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = m * 16 + 4 * (lane >> 4) + i;
+        const int r = rbase + m * 16 + 4 * (lane >> 4) + i;
         float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
         float s = amax / kE4M3Max;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           uint32_t code = (amax > 0.0f) ? fp8_quant(av[m][jj][i], s) : 0u;
-          stage[r * 128 + 32 * wave + 16 * jj + (lane & 15)] = (uint8_t)code;
+          stage[r * 128 + 32 * wn + 16 * jj + (lane & 15)] = (uint8_t)code;
         }
-        if (wave == 0 && (lane & 15) == 0) ((float*)p.as)[(int64_t)(row0 + r) * nsc + nt] = (amax > 0.0f) ? s : 0.0f;
+        if (wn == 0 && (lane & 15) == 0) ((float*)p.as)[(int64_t)(row0 + r) * nsc + nt] = (amax > 0.0f) ? s : 0.0f;
       }
     __syncthreads();
-    for (int c = tid; c < BM * 8; c += 256) {
+    for (int c = tid; c < BM * 8; c += NTH) {
       int r = c >> 3, cc = c & 7;
       *(uint4*)(p.aq + (int64_t)(row0 + r) * p.Ip + nt * 128 + cc * 16) = *(const uint4*)(&stage[r * 128 + cc * 16]);
     }
   } else {
     const int nsc = p.Ip / 32;
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MTW; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = m * 16 + 4 * (lane >> 4) + i;
+        const int r = rbase + m * 16 + 4 * (lane >> 4) + i;
         uint32_t b = e8m0_byte(rmax[m][i]);
         float inv = e8m0_inverse(b);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
-          stage[r * 128 + 32 * wave + 16 * jj + (lane & 15)] = (uint8_t)mx_quant(av[m][jj][i], inv);
-        if ((lane & 15) == 0) ((uint8_t*)p.as)[(int64_t)(row0 + r) * nsc + nt * 4 + wave] = (uint8_t)b;
+          stage[r * 128 + 32 * wn + 16 * jj + (lane & 15)] = (uint8_t)mx_quant(av[m][jj][i], inv);
+        if ((lane & 15) == 0) ((uint8_t*)p.as)[(int64_t)(row0 + r) * nsc + nt * 4 + wn] = (uint8_t)b;
       }
     __syncthreads();
-    for (int c = tid; c < BM * 4; c += 256) {
+    for (int c = tid; c < BM * 4; c += NTH) {
       int r = c >> 2, cc = c & 3;
       const uint8_t* src = &stage[r * 128 + cc * 32];
       uint32_t w[4];
@@ -257,19 +257,19 @@ __device__ __forceinline__ void epilogue_gemm1(const GemmArgs& p, const v4f (&ac
 }
 
 // GEMM2: y[pair, column] = topk_w[pair] * C for the real pairs of the block.
-template <int BM>
-__device__ __forceinline__ void epilogue_gemm2(const GemmArgs& p, const v4f (&acc)[BM / 16][4], const int32_t* sid_lds,
-                                               int nt, int wave) {
+template <int MTW>
+__device__ __forceinline__ void epilogue_gemm2(const GemmArgs& p, const v4f (&acc)[MTW][4], const int32_t* sid_lds,
+                                               int nt, int wn, int rbase) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int m = 0; m < BM / 16; ++m)
+  for (int m = 0; m < MTW; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = m * 16 + 4 * (lane >> 4) + i;
+      const int r = rbase + m * 16 + 4 * (lane >> 4) + i;
       const int sid = sid_lds[r];
       if (sid < p.num_pairs) {
         const float wt = p.topk_w[sid];
-        float* yrow = p.y + (int64_t)sid * p.N + nt * 256 + 64 * wave + (lane & 15);
+        float* yrow = p.y + (int64_t)sid * p.N + nt * 256 + 64 * wn + (lane & 15);
 #pragma unroll
         for (int j = 0; j < 4; ++j) yrow[16 * j] = wt * acc[m][j][i];
       }
@@ -295,84 +295,323 @@ __device__ __forceinline__ bool wave_tiles(const GemmArgs& p, int nt, int wave, 
 }
 
 // ===========================================================================
-// LDS-staged kernel (block_m 64 / 128): the A tile of each K block is loaded
-// once per workgroup into LDS (double buffered) and read by the 4 waves.
+// Ring kernel (block_m 64 / 128, prefill shapes).
+//
+// Operands go from HBM to LDS with direct global->LDS loads
+// (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16*l), through a
+// ring of S K-block slots, so S-1 K blocks are in flight per workgroup without
+// holding them in registers.  The weight tiles are copied verbatim from the
+// TILED_V1 layout, which already is MFMA fragment order; the gathered token
+// rows are placed in the same order by the per-lane source addresses.  Every
+// wave issues the same number of loads per slot, so one s_waitcnt vmcnt(N)
+// per K block plus a barrier make the slot visible to all waves.
+//
+// The MFMA runs transposed: the weight tile is operand A and the 16 tokens are
+// operand B, so lane l holds 4 consecutive weight rows (output columns) of one
+// token.  For block FP8 those 4 values share one 128x128 weight scale, and the
+// per-K-block promotion costs one fma per output value.
+//
+// Waves: (wt, wn) = (wave / 4, wave % 4); wt picks 64 tokens (4 row tiles), wn
+// the wave's 4 weight tiles: GEMM1 gate tiles 2wn, 2wn+1 and the matching up
+// tiles 8+2wn, 9+2wn of the N tile; GEMM2 tiles 4wn .. 4wn+3.
 // ===========================================================================
 template <int MODE, int BM>
-struct alignas(16) GemmSmem {
-  uint8_t a[2][BM * GemmCfg<MODE>::ASTR];
-  uint32_t asc[2][BM];  // FP8: f32 bits of the act scale; MX: 4 E8M0 bytes
-  int32_t src[BM];      // A source row (token or sorted position), -1 = pad
-  int32_t sid[BM];      // pair index of each row
-  float red[4][BM];     // GEMM1 FP8 epilogue: per-wave row amax
+struct Ring {
+  static constexpr int NWAVE = BM / 16;  // (BM / 64) token halves x 4 column waves
+  static constexpr int NTH = NWAVE * 64;
+  static constexpr int TILE = (MODE == kQuantMx) ? 1024 : 2048;  // one 16 x 128 operand tile
+  static constexpr int HALVES = TILE / 1024;
+  static constexpr int AROW = (MODE == kQuantMx) ? 64 : 128;     // token bytes per K block
+  static constexpr int W_OFF = 0;                                // 16 weight tiles
+  static constexpr int T_OFF = 16 * TILE;                        // BM/16 token tiles
+  static constexpr int TS_OFF = T_OFF + (BM / 16) * TILE;        // per-wave token scales
+  static constexpr int WS_OFF = TS_OFF + NWAVE * 256;            // MX: weight scale dwords
+  static constexpr int SLOT = WS_OFF + ((MODE == kQuantMx) ? 16 * 256 : 0);
+  static constexpr int DW = 16 * HALVES / NWAVE;                 // loads per wave per slot
+  static constexpr int DT = (BM / 16) * HALVES / NWAVE;
+  static constexpr int DWS = (MODE == kQuantMx) ? 16 / NWAVE : 0;
+  static constexpr int D = DW + DT + 1 + DWS;
+  static_assert(16 * HALVES % NWAVE == 0 && (BM / 16) * HALVES % NWAVE == 0, "uniform loads per wave");
 };
 
+// Direct global->LDS loads, written as inline assembly so that the compiler's
+// automatic wait insertion does not see them (it would add vmcnt(0) in front
+// of every LDS read of the ring); the kernel waits for them itself.  M0 holds
+// the wave-uniform LDS base (one wait state before the load reads it).  The
+// weight loads carry the non-temporal hint: weights are read once per launch.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the compiler does not use it in these kernels
+template <bool NT>
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding and
+// its LDS operations are complete, then barrier.  The "memory" clobber keeps
+// the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Uniform fp32 load through the scalar data cache (read only).
+__device__ __forceinline__ float uniform_load(const float* p) {
+  return *(const __attribute__((address_space(4))) float*)p;
+}
+
+// Per-lane source addresses of one wave's loads at K block 0.
 template <int MODE, int BM>
-__device__ __forceinline__ void load_a_regs(const GemmArgs& p, const GemmSmem<MODE, BM>& sm, int kb,
-                                            uint4 (&ar)[(BM * GemmCfg<MODE>::CPR + 255) / 256], uint32_t& sr) {
-  constexpr int CPR = GemmCfg<MODE>::CPR;
-  constexpr int NCH = (BM * CPR + 255) / 256;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    int c = tid + 256 * i;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (c < BM * CPR) {
-      int r = c / CPR, cc = c % CPR;
-      int src = sm.src[r];
-      if (src >= 0) v = *(const uint4*)(p.A + (int64_t)src * p.lda + (int64_t)kb * GemmCfg<MODE>::AROW + cc * 16);
-    }
-    ar[i] = v;
-  }
-  sr = 0;
-  if (tid < BM) {
-    int src = sm.src[tid];
-    if (src >= 0) {
-      if constexpr (MODE != kQuantMx)
-        sr = ((const uint32_t*)p.As)[(int64_t)src * p.ldas + kb];
-      else
-        sr = *(const uint32_t*)((const uint8_t*)p.As + (int64_t)src * p.ldas + kb * 4);
-    }
+struct RingSrc {
+  using R = Ring<MODE, BM>;
+  const uint8_t* w[R::DW];
+  const uint8_t* t[R::DT];
+  const uint8_t* ts;
+  const uint8_t* ws[R::DWS > 0 ? R::DWS : 1];
+};
+
+// Weight tile t16 of local tile i (0..15) of N tile nt.
+template <bool G1>
+__device__ __forceinline__ int ring_tile(const GemmArgs& p, int nt, int i) {
+  if constexpr (G1) {
+    return (i < 8) ? nt * 8 + i : p.Ip / 16 + nt * 8 + (i - 8);
+  } else {
+    const int t = nt * 16 + i, last = p.N / 16 - 1;
+    return t < last ? t : last;  // tail tiles of a half N tile load a valid duplicate
   }
 }
 
 template <int MODE, int BM>
-__device__ __forceinline__ void store_a_lds(GemmSmem<MODE, BM>& sm, int buf,
-                                            const uint4 (&ar)[(BM * GemmCfg<MODE>::CPR + 255) / 256], uint32_t sr) {
-  constexpr int CPR = GemmCfg<MODE>::CPR;
-  constexpr int NCH = (BM * CPR + 255) / 256;
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const uint8_t* slot, int wave, int kb) {
+  using R = Ring<MODE, BM>;
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(slot));
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    int c = tid + 256 * i;
-    if (c < BM * CPR) {
-      int r = c / CPR, cc = c % CPR;
-      if constexpr (MODE == kQuantFp8F16) {
-        // widen 16 e4m3 values to f16 (K order kept)
-        const uint4 v = ar[i];
-        uint4 lo = make_uint4(e4m3x2_to_f16x2<false>(v.x), e4m3x2_to_f16x2<true>(v.x),
-                              e4m3x2_to_f16x2<false>(v.y), e4m3x2_to_f16x2<true>(v.y));
-        uint4 hi = make_uint4(e4m3x2_to_f16x2<false>(v.z), e4m3x2_to_f16x2<true>(v.z),
-                              e4m3x2_to_f16x2<false>(v.w), e4m3x2_to_f16x2<true>(v.w));
-        *(uint4*)(&sm.a[buf][r * GemmCfg<MODE>::ASTR + cc * 32]) = lo;
-        *(uint4*)(&sm.a[buf][r * GemmCfg<MODE>::ASTR + cc * 32 + 16]) = hi;
-      } else {
-        *(uint4*)(&sm.a[buf][r * GemmCfg<MODE>::ASTR + cc * 16]) = ar[i];
+  for (int q = 0; q < R::DW; ++q)
+    dma16<true>(src.w[q] + (int64_t)kb * R::TILE, base + R::W_OFF + (wave * R::DW + q) * 1024);
+#pragma unroll
+  for (int q = 0; q < R::DT; ++q) dma16<false>(src.t[q] + kb * R::AROW, base + R::T_OFF + (wave * R::DT + q) * 1024);
+  dma4(src.ts + kb * 4, base + R::TS_OFF + wave * 256);
+  if constexpr (R::DWS > 0) {
+#pragma unroll
+    for (int q = 0; q < R::DWS; ++q) dma4(src.ws[q] + (kb >> 2) * 256, base + R::WS_OFF + (wave * R::DWS + q) * 256);
+  }
+}
+
+__device__ __forceinline__ v8i lds_frag32(const uint8_t* p) {  // 32 FP8 bytes: halves 1 KB apart
+  const uint4 lo = *(const uint4*)p, hi = *(const uint4*)(p + 1024);
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+__device__ __forceinline__ v8i lds_frag16(const uint8_t* p) {  // 32 E2M1 values
+  const uint4 lo = *(const uint4*)p;
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+}
+
+template <int OPA>
+__device__ __forceinline__ v4f mfma_fp4_scaled_t(const v8i& w, const v8i& t, v4f c, int sw, int st) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, t, c, 4, 4, OPA, sw, 0, st);
+}
+
+// One K block of the wave's 4 token tiles x 4 weight tiles from slot `slot`.
+// acc[m][j][i] = C[token (wt*4+m)*16 + lane%16][weight row 16*tile_j + 4*(lane/16) + i].
+template <int MODE, int BM, bool G1, int KB4>
+__device__ __forceinline__ void ring_compute(const uint8_t* slot, const int (&tiles)[4], int wave, int wt,
+                                             float sw0, float sw1, v4f (&acc)[4][4]) {
+  using R = Ring<MODE, BM>;
+  const int lane = threadIdx.x & 63;
+  const uint8_t* wl = slot + R::W_OFF + lane * 16;
+  const uint8_t* tl = slot + R::T_OFF + wt * 4 * R::TILE + lane * 16;
+  const uint8_t* tsl = slot + R::TS_OFF + wave * 256 + (lane & 15) * 16;
+  if constexpr (MODE == kQuantMx) {
+    const uint4 tsd = *(const uint4*)tsl;
+    const int sh = 8 * (lane >> 4);
+    const int st[4] = {(int)((tsd.x >> sh) & 0xFFu), (int)((tsd.y >> sh) & 0xFFu), (int)((tsd.z >> sh) & 0xFFu),
+                       (int)((tsd.w >> sh) & 0xFFu)};
+    v8i w[4];
+    int sw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = lds_frag16(wl + tiles[j] * R::TILE);
+      sw[j] = *(const int*)(slot + R::WS_OFF + tiles[j] * 256 + lane * 4);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const v8i t = lds_frag16(tl + m * R::TILE);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[m][j] = mfma_fp4_scaled_t<KB4>(w[j], t, acc[m][j], sw[j], st[m]);
+    }
+  } else {
+    const float4 ts = *(const float4*)tsl;
+    const float tsc[4] = {ts.x, ts.y, ts.z, ts.w};
+    // GEMM1: tiles 0,1 are gate rows (scale sw0), 2,3 up rows (sw1); GEMM2: all sw0
+    if constexpr (MODE == kQuantFp8) {
+      v8i w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = lds_frag32(wl + tiles[j] * R::TILE);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const v8i t = lds_frag32(tl + m * R::TILE);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float s = tsc[m] * ((G1 && j >= 2) ? sw1 : sw0);
+          const v4f c = mfma_fp8(w[j], t, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(c[i], s, acc[m][j][i]);
+        }
+      }
+    } else {
+      v8h wh[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) widen_fp8(lds_frag32(wl + tiles[j] * R::TILE), wh[j]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        v8h th[4];
+        widen_fp8(lds_frag32(tl + m * R::TILE), th);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float s = tsc[m] * ((G1 && j >= 2) ? sw1 : sw0);
+          v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) c = mfma_f16(wh[j][k], th[k], c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(c[i], s, acc[m][j][i]);
+        }
       }
     }
   }
-  if (tid < BM) sm.asc[buf][tid] = sr;
 }
 
-template <int MODE, int BM, bool G1>
-__global__ __launch_bounds__(256) void moe_gemm_lds_kernel(GemmArgs p) {
-  constexpr int MT = BM / 16;
-  constexpr int ASTR = GemmCfg<MODE>::ASTR;
-  constexpr int NCH = (BM * GemmCfg<MODE>::CPR + 255) / 256;
-  __shared__ GemmSmem<MODE, BM> sm;
+// GEMM1 epilogue for the transposed accumulators: lane l holds, for token
+// t = wt*64 + m*16 + l%16, intermediate columns 32*wn + 16*jj + 4*(l/16) + i
+// of the N tile (gate in acc[m][jj], up in acc[m][jj+2]).  Pad rows give 0.
+template <int MODE, int BM>
+__device__ __forceinline__ void epilogue_gemm1_t(const GemmArgs& p, const v4f (&acc)[4][4], float (*red)[BM],
+                                                 const int32_t* src_lds, uint8_t* stage, int row0, int nt, int wt,
+                                                 int wn) {
+  constexpr int NTH = Ring<MODE, BM>::NTH;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, c16 = lane & 15;
+  const float L = p.limit;
+  float av[4][2][4];
+  float tmax[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const bool real = src_lds[wt * 64 + m * 16 + c16] >= 0;
+    float mx = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = real ? swiglu_clamped(acc[m][jj][i], acc[m][jj + 2][i], L) : 0.0f;
+        av[m][jj][i] = a;
+        mx = fmaxf(mx, fabsf(a));
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    tmax[m] = mx;
+  }
+  if constexpr (MODE != kQuantMx) {
+    if (q == 0) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) red[wn][wt * 64 + m * 16 + c16] = tmax[m];
+    }
+    __syncthreads();
+    const int nsc = p.Ip / 128;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int t = wt * 64 + m * 16 + c16;
+      const float amax = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
+      const float s = amax / kE4M3Max;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) packed |= ((amax > 0.0f) ? fp8_quant(av[m][jj][i], s) : 0u) << (8 * i);
+        *(uint32_t*)(stage + t * 128 + 32 * wn + 16 * jj + 4 * q) = packed;
+      }
+      if (wn == 0 && q == 0) ((float*)p.as)[(int64_t)(row0 + t) * nsc + nt] = (amax > 0.0f) ? s : 0.0f;
+    }
+    __syncthreads();
+    for (int c = tid; c < BM * 8; c += NTH) {
+      const int r = c >> 3, cc = c & 7;
+      *(uint4*)(p.aq + (int64_t)(row0 + r) * p.Ip + nt * 128 + cc * 16) = *(const uint4*)(stage + r * 128 + cc * 16);
+    }
+  } else {
+    const int nsc = p.Ip / 32;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int t = wt * 64 + m * 16 + c16;
+      const uint32_t b = e8m0_byte(tmax[m]);
+      const float inv = e8m0_inverse(b);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) packed |= mx_quant(av[m][jj][i], inv) << (4 * i);
+        *(uint16_t*)(stage + t * 64 + 16 * wn + 8 * jj + 2 * q) = (uint16_t)packed;
+      }
+      if (q == 0) ((uint8_t*)p.as)[(int64_t)(row0 + t) * nsc + nt * 4 + wn] = (uint8_t)b;
+    }
+    __syncthreads();
+    for (int c = tid; c < BM * 4; c += NTH) {
+      const int r = c >> 2, cc = c & 3;
+      *(uint4*)(p.aq + (int64_t)(row0 + r) * (p.Ip / 2) + nt * 64 + cc * 16) = *(const uint4*)(stage + r * 64 + cc * 16);
+    }
+  }
+}
+
+// GEMM2 epilogue (transposed accumulators): y[pair, 4 columns] per lane.
+template <int BM>
+__device__ __forceinline__ void epilogue_gemm2_t(const GemmArgs& p, const v4f (&acc)[4][4], const int32_t* sid_lds,
+                                                 int nt, int wt, int wn) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int sid = sid_lds[wt * 64 + m * 16 + c16];
+    if (sid < p.num_pairs) {
+      const float w = p.topk_w[sid];
+      float* yrow = p.y + (int64_t)sid * p.N + nt * 256 + 64 * wn + 4 * q;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v4f v = acc[m][j];
+        *(float4*)(yrow + 16 * j) = make_float4(w * v[0], w * v[1], w * v[2], w * v[3]);
+      }
+    }
+  }
+}
+
+template <int MODE, int BM, bool G1, int S>
+__global__ __launch_bounds__(BM * 4) void moe_gemm_ring_kernel(GemmArgs p) {
+  using R = Ring<MODE, BM>;
+  static_assert(S >= 2 && S <= 5, "ring depth");
+  static_assert(MODE != kQuantMx || S == 4, "MX: S == 4 so that kb % 4 is the slot index");
+  __shared__ __attribute__((aligned(1024))) uint8_t slot0[R::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot1[R::SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot2[S > 2 ? R::SLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot3[S > 3 ? R::SLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot4[S > 4 ? R::SLOT : 16];
+  __shared__ int32_t src_lds[BM];
+  __shared__ int32_t sid_lds[BM];
+  __shared__ float red[4][BM];
+  auto slot = [&](auto ic) -> uint8_t* {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i == 0) return slot0;
+    else if constexpr (i == 1) return slot1;
+    else if constexpr (i == 2) return slot2;
+    else if constexpr (i == 3) return slot3;
+    else return slot4;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wt = wave >> 2, wn = wave & 3;
   const int mblk = blockIdx.x / p.n_tiles;
   const int nt = blockIdx.x % p.n_tiles;
   const int npp = __builtin_amdgcn_readfirstlane(*p.npp);
@@ -383,100 +622,113 @@ __global__ __launch_bounds__(256) void moe_gemm_lds_kernel(GemmArgs p) {
   const int NT16 = p.N / 16;
 
   if (tid < BM) {
-    int sid = p.sorted_ids[row0 + tid];
-    bool valid = sid < p.num_pairs;
-    sm.sid[tid] = sid;
-    sm.src[tid] = valid ? (G1 ? sid / p.top_k : row0 + tid) : -1;
+    const int sid = p.sorted_ids[row0 + tid];
+    const bool valid = sid < p.num_pairs;
+    sid_lds[tid] = sid;
+    src_lds[tid] = valid ? (G1 ? sid / p.top_k : row0 + tid) : -1;
   }
-  int t16[4];
-  const bool wave_active = wave_tiles<G1>(p, nt, wave, t16);
-  int64_t tbase[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) tbase[j] = ((int64_t)e * NT16 + (wave_active ? t16[j] : 0)) * KB;
+  __syncthreads();
 
-  v4f acc[MT][4];
+  // per-lane load addresses (pad rows read token 0 / their own zero rows; their
+  // results are discarded or zeroed in the epilogue)
+  RingSrc<MODE, BM> rs;
 #pragma unroll
-  for (int m = 0; m < MT; ++m)
+  for (int q = 0; q < R::DW; ++q) {
+    const int g = wave * R::DW + q, tile = g / R::HALVES, h = g % R::HALVES;
+    const int t16 = ring_tile<G1>(p, nt, tile);
+    rs.w[q] = p.B + (((int64_t)e * NT16 + t16) * KB) * R::TILE + h * 1024 + lane * 16;
+  }
+  auto row_of = [&](int r) -> int64_t {
+    const int s = src_lds[r];
+    return G1 ? (s >= 0 ? s : 0) : (int64_t)(row0 + r);
+  };
+#pragma unroll
+  for (int q = 0; q < R::DT; ++q) {
+    const int g = wave * R::DT + q, mt = g / R::HALVES, h = g % R::HALVES;
+    const int64_t row = row_of(mt * 16 + (lane & 15));
+    rs.t[q] = p.A + row * p.lda + (lane >> 4) * (R::AROW / 4) + h * 16;
+  }
+  {
+    const int64_t row = row_of(wt * 64 + (lane & 3) * 16 + (lane >> 2));
+    rs.ts = (MODE == kQuantMx) ? (const uint8_t*)p.As + row * p.ldas : (const uint8_t*)p.As + row * p.ldas * 4;
+  }
+  if constexpr (R::DWS > 0) {
+    const int KBq = (KB + 3) / 4;
+#pragma unroll
+    for (int q = 0; q < R::DWS; ++q) {
+      const int t16 = ring_tile<G1>(p, nt, wave * R::DWS + q);
+      rs.ws[q] = (const uint8_t*)p.Bs + ((((int64_t)e * NT16 + t16) * KBq) * 64 + lane) * 4;
+    }
+  }
+
+  // the wave's 4 local weight tiles and its FP8 weight-scale rows
+  int tiles[4];
+  bool active;
+  const float* wsr0 = nullptr;
+  const float* wsr1 = nullptr;
+  if constexpr (G1) {
+    tiles[0] = 2 * wn; tiles[1] = 2 * wn + 1; tiles[2] = 8 + 2 * wn; tiles[3] = 9 + 2 * wn;
+    active = true;
+    if constexpr (MODE != kQuantMx) {
+      const int NB = p.N / 128;
+      wsr0 = (const float*)p.Bs + ((int64_t)e * NB + nt) * KB;
+      wsr1 = (const float*)p.Bs + ((int64_t)e * NB + p.Ip / 128 + nt) * KB;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tiles[j] = 4 * wn + j;
+    active = nt * 256 + 64 * wn < p.N;
+    if constexpr (MODE != kQuantMx) {
+      const int NB = p.N / 128;
+      const int blk = min(nt * 2 + (wn >> 1), NB - 1);
+      wsr0 = (const float*)p.Bs + ((int64_t)e * NB + blk) * KB;
+      wsr1 = wsr0;
+    }
+  }
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[m][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  __syncthreads();
-  uint4 ar[NCH];
-  uint32_t sr;
-  load_a_regs<MODE, BM>(p, sm, 0, ar, sr);
-  store_a_lds<MODE, BM>(sm, 0, ar, sr);
-  v8i bc[4], bn[4];
-  if (wave_active) load_b<MODE>(p, tbase, 0, bc);
-  int sbw[4] = {0, 0, 0, 0};
-  __syncthreads();
+  // Prologue: K blocks 0 .. S-2 in flight.  Every K-block step then issues
+  // exactly one slot (past the last block it reloads block KB-1 into the slot
+  // just freed, which is never read), so the wait count is the constant
+  // (S-2)*D and the steps of a full group carry no branch between the loads
+  // and the LDS reads: the compiler's own wait insertion can then tell the
+  // ring slots apart and adds no vmcnt(0).
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (ring_issue<MODE, BM>(rs, slot(std::integral_constant<int, I>{}), wave, min(I, KB - 1)), ...);
+  }(std::make_integer_sequence<int, S - 1>{});
 
-  for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb & 1;
-    const bool more = kb + 1 < KB;
-    if (more) {
-      if (wave_active) load_b<MODE>(p, tbase, kb + 1, bn);
-      load_a_regs<MODE, BM>(p, sm, kb + 1, ar, sr);
+  auto step = [&](auto dc, int kb) {
+    constexpr int d = decltype(dc)::value;
+    float sw0 = 0.0f, sw1 = 0.0f;
+    if constexpr (MODE != kQuantMx) {
+      sw0 = uniform_load(wsr0 + kb);
+      sw1 = G1 ? uniform_load(wsr1 + kb) : sw0;
     }
-    if (wave_active) {
-      if constexpr (MODE == kQuantMx) {
-        if ((kb & 3) == 0) load_b_scales(p, e, t16, kb, sbw);
-        v8i a[MT];
-        int sa[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const int r = m * 16 + (lane & 15);
-          uint4 a0 = *(const uint4*)(&sm.a[buf][r * ASTR + (lane >> 4) * 16]);
-          a[m] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
-          sa[m] = (int)((sm.asc[buf][r] >> (8 * (lane >> 4))) & 0xFFu);
-        }
-        step_mx_kb<MT>(kb, a, sa, bc, sbw, acc);
-      } else {
-        float sw[4];
-        load_w_scales(p, e, t16, kb, sw);
-        float sa[MT][4];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const uint4 s4 = *(const uint4*)(&sm.asc[buf][m * 16 + (lane >> 4) * 4]);
-          sa[m][0] = __uint_as_float(s4.x);
-          sa[m][1] = __uint_as_float(s4.y);
-          sa[m][2] = __uint_as_float(s4.z);
-          sa[m][3] = __uint_as_float(s4.w);
-        }
-        if constexpr (MODE == kQuantFp8) {
-          v8i a[MT];
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const uint8_t* ap = &sm.a[buf][(m * 16 + (lane & 15)) * ASTR + (lane >> 4) * 32];
-            uint4 a0 = *(const uint4*)ap;
-            uint4 a1 = *(const uint4*)(ap + 16);
-            a[m] = v8i{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-          }
-          step_fp8<MT>(a, sa, bc, sw, acc);
-        } else {
-          v8h a[MT][4];
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            const uint8_t* ap = &sm.a[buf][(m * 16 + (lane & 15)) * ASTR + (lane >> 4) * 64];
-#pragma unroll
-            for (int st = 0; st < 4; ++st) a[m][st] = *(const v8h*)(ap + 16 * st);
-          }
-          step_f16<MT>(a, sa, bc, sw, acc);
-        }
-      }
-    }
-    if (more) store_a_lds<MODE, BM>(sm, buf ^ 1, ar, sr);
-    __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bc[j] = bn[j];
-    }
+    vm_wait_barrier<(S - 2) * R::D>();
+    ring_issue<MODE, BM>(rs, slot(std::integral_constant<int, (d + S - 1) % S>{}), wave, min(kb + S - 1, KB - 1));
+    if (active) ring_compute<MODE, BM, G1, d & 3>(slot(std::integral_constant<int, d>{}), tiles, wave, wt, sw0, sw1, acc);
+  };
+  int kb0 = 0;
+  for (; kb0 + S <= KB; kb0 += S) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      (step(std::integral_constant<int, I>{}, kb0 + I), ...);
+    }(std::make_integer_sequence<int, S>{});
   }
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((kb0 + I < KB ? step(std::integral_constant<int, I>{}, kb0 + I) : void()), ...);
+  }(std::make_integer_sequence<int, S - 1>{});
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail reloads land before slot 0 is reused
 
+  __syncthreads();  // every wave is done with the ring; slot 0 becomes the epilogue stage
   if constexpr (G1) {
-    epilogue_gemm1<MODE, BM>(p, acc, sm.red, &sm.a[0][0], row0, nt, wave);
+    epilogue_gemm1_t<MODE, BM>(p, acc, red, src_lds, slot0, row0, nt, wt, wn);
   } else {
-    if (!wave_active) return;
-    epilogue_gemm2<BM>(p, acc, sm.sid, nt, wave);
+    if (active) epilogue_gemm2_t<BM>(p, acc, sid_lds, nt, wt, wn);
   }
 }
 
@@ -640,25 +892,33 @@ __global__ __launch_bounds__(256) void moe_gemm_direct_kernel(GemmArgs p) {
   }
 
   if constexpr (G1) {
-    epilogue_gemm1<MODE, BM>(p, acc, sm.red, sm.stage, row0, nt, wave);
+    epilogue_gemm1<MODE, BM, MT, 256>(p, acc, sm.red, sm.stage, row0, nt, wave, 0);
   } else {
     if (!wave_active) return;
-    epilogue_gemm2<BM>(p, acc, sm.sid, nt, wave);
+    epilogue_gemm2<MT>(p, acc, sm.sid, nt, wave, 0);
   }
 }
 
 #ifndef MOE_DIRECT_PD
 #define MOE_DIRECT_PD 2
 #endif
+#ifndef MOE_RING_S_FP8
+#define MOE_RING_S_FP8 3
+#endif
 
 template <int MODE, bool G1>
 static hipError_t launch_gemm_mode(int block_m, int nb, const GemmArgs& a, hipStream_t s) {
+  constexpr int SR = (MODE == kQuantMx) ? 4 : MOE_RING_S_FP8;
   dim3 grid((unsigned)((int64_t)nb * a.n_tiles)), block(256);
   switch (block_m) {
     case 16: hipLaunchKernelGGL((moe_gemm_direct_kernel<MODE, 16, G1, MOE_DIRECT_PD>), grid, block, 0, s, a); break;
     case 32: hipLaunchKernelGGL((moe_gemm_direct_kernel<MODE, 32, G1, MOE_DIRECT_PD>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((moe_gemm_lds_kernel<MODE, 64, G1>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((moe_gemm_lds_kernel<MODE, 128, G1>), grid, block, 0, s, a); break;
+    case 64:
+      hipLaunchKernelGGL((moe_gemm_ring_kernel<MODE, 64, G1, SR>), grid, dim3(Ring<MODE, 64>::NTH), 0, s, a);
+      break;
+    default:
+      hipLaunchKernelGGL((moe_gemm_ring_kernel<MODE, 128, G1, SR>), grid, dim3(Ring<MODE, 128>::NTH), 0, s, a);
+      break;
   }
   return hipGetLastError();
 }
