@@ -315,6 +315,11 @@ __device__ __forceinline__ bool wave_tiles(const GemmArgs& p, int nt, int wave, 
 // the wave's 4 weight tiles: GEMM1 gate tiles 2wn, 2wn+1 and the matching up
 // tiles 8+2wn, 9+2wn of the N tile; GEMM2 tiles 4wn .. 4wn+3.
 // ===========================================================================
+#ifndef MOE_XCD_MAP
+#define MOE_XCD_MAP 1
+#endif
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
 template <int MODE, int BM>
 struct Ring {
   static constexpr int NWAVE = BM / 16;  // (BM / 64) token halves x 4 column waves
@@ -324,13 +329,13 @@ struct Ring {
   static constexpr int AROW = (MODE == kQuantMx) ? 64 : 128;     // token bytes per K block
   static constexpr int W_OFF = 0;                                // 16 weight tiles
   static constexpr int T_OFF = 16 * TILE;                        // BM/16 token tiles
-  static constexpr int TS_OFF = T_OFF + (BM / 16) * TILE;        // per-wave token scales
-  static constexpr int WS_OFF = TS_OFF + NWAVE * 256;            // MX: weight scale dwords
-  static constexpr int SLOT = WS_OFF + ((MODE == kQuantMx) ? 16 * 256 : 0);
+  static constexpr int TS_OFF = T_OFF + (BM / 16) * TILE;        // token scales, 256 B per 64 tokens
+  static constexpr int SLOT = TS_OFF + (BM / 64) * 256;
+  static constexpr int WS_BYTES = 16 * 256;                      // MX: one group of weight scale dwords
   static constexpr int DW = 16 * HALVES / NWAVE;                 // loads per wave per slot
   static constexpr int DT = (BM / 16) * HALVES / NWAVE;
-  static constexpr int DWS = (MODE == kQuantMx) ? 16 / NWAVE : 0;
-  static constexpr int D = DW + DT + 1 + DWS;
+  static constexpr int DWS = (MODE == kQuantMx) ? 16 / NWAVE : 0;  // every 4th K block only
+  static constexpr int D = DW + DT + 1;                          // loads per wave in every K block
   static_assert(16 * HALVES % NWAVE == 0 && (BM / 16) * HALVES % NWAVE == 0, "uniform loads per wave");
 };
 
@@ -390,20 +395,48 @@ __device__ __forceinline__ int ring_tile(const GemmArgs& p, int nt, int i) {
   }
 }
 
+// Loads of K block kb into `slot`.  Token scales: each wave fetches 16 of the
+// 64 scales of its token half (lanes 0..15 only), placed so that lane l of a
+// compute wave finds the scales of token tiles m = 0..3, row l % 16, in one
+// 16-byte word.  MX weight scales (one dword holds 4 K blocks) are fetched
+// only when `ws` is non-null, into that buffer.
 template <int MODE, int BM>
-__device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const uint8_t* slot, int wave, int kb) {
+__device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const uint8_t* slot, int wave, int kb,
+                                           const uint8_t* ws) {
   using R = Ring<MODE, BM>;
+  const int lane = threadIdx.x & 63;
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(slot));
 #pragma unroll
   for (int q = 0; q < R::DW; ++q)
     dma16<true>(src.w[q] + (int64_t)kb * R::TILE, base + R::W_OFF + (wave * R::DW + q) * 1024);
 #pragma unroll
   for (int q = 0; q < R::DT; ++q) dma16<false>(src.t[q] + kb * R::AROW, base + R::T_OFF + (wave * R::DT + q) * 1024);
-  dma4(src.ts + kb * 4, base + R::TS_OFF + wave * 256);
+  if (lane < 16) dma4(src.ts + kb * 4, base + R::TS_OFF + (wave >> 2) * 256 + (wave & 3) * 64);
   if constexpr (R::DWS > 0) {
+    if (ws != nullptr) {
+      const uint32_t wbase = __builtin_amdgcn_readfirstlane(lds_addr(ws));
 #pragma unroll
-    for (int q = 0; q < R::DWS; ++q) dma4(src.ws[q] + (kb >> 2) * 256, base + R::WS_OFF + (wave * R::DWS + q) * 256);
+      for (int q = 0; q < R::DWS; ++q) dma4(src.ws[q] + (kb >> 2) * 256, wbase + (wave * R::DWS + q) * 256);
+    }
   }
+}
+
+// Per-lane row of the token-scale load (see ring_issue): entry i = 16*(wave%4)
+// + lane of token half wt holds token tile i % 4, row i / 4.
+__device__ __forceinline__ int ring_scale_row(int wave, int lane) {
+  const int i = (wave & 3) * 16 + (lane & 15);
+  return (wave >> 2) * 64 + (i & 3) * 16 + (i >> 2);
+}
+
+// FP8 token tile in LDS: load h of the tile holds, at lane j's 16 bytes, row
+// j % 16 and K bytes 64h + 16(j/16) .. +16 (whole 64-byte row segments per
+// load).  The MFMA fragment of lane l (row l % 16, K bytes 32(l/16) .. +32)
+// is then the two 16-byte words below.
+__device__ __forceinline__ v8i lds_tok32(const uint8_t* tile, int lane) {
+  const int q = lane >> 4;
+  const uint8_t* p = tile + (q >> 1) * 1024 + (q & 1) * 512 + (lane & 15) * 16;
+  const uint4 lo = *(const uint4*)p, hi = *(const uint4*)(p + 256);
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
 __device__ __forceinline__ v8i lds_frag32(const uint8_t* p) {  // 32 FP8 bytes: halves 1 KB apart
@@ -422,31 +455,34 @@ __device__ __forceinline__ v4f mfma_fp4_scaled_t(const v8i& w, const v8i& t, v4f
 
 // One K block of the wave's 4 token tiles x 4 weight tiles from slot `slot`.
 // acc[m][j][i] = C[token (wt*4+m)*16 + lane%16][weight row 16*tile_j + 4*(lane/16) + i].
-template <int MODE, int BM, bool G1, int KB4>
-__device__ __forceinline__ void ring_compute(const uint8_t* slot, const int (&tiles)[4], int wave, int wt,
-                                             float sw0, float sw1, v4f (&acc)[4][4]) {
+template <int MODE, int BM, bool G1>
+__device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t* ws, const int (&tiles)[4], int wt,
+                                             int kb, float sw0, float sw1, v4f (&acc)[4][4]) {
   using R = Ring<MODE, BM>;
   const int lane = threadIdx.x & 63;
   const uint8_t* wl = slot + R::W_OFF + lane * 16;
-  const uint8_t* tl = slot + R::T_OFF + wt * 4 * R::TILE + lane * 16;
-  const uint8_t* tsl = slot + R::TS_OFF + wave * 256 + (lane & 15) * 16;
+  const uint8_t* tt = slot + R::T_OFF + wt * 4 * R::TILE;  // the wave's 4 token tiles
+  const uint8_t* tl = tt + lane * 16;
+  const uint8_t* tsl = slot + R::TS_OFF + wt * 256 + (lane & 15) * 16;
   if constexpr (MODE == kQuantMx) {
     const uint4 tsd = *(const uint4*)tsl;
     const int sh = 8 * (lane >> 4);
     const int st[4] = {(int)((tsd.x >> sh) & 0xFFu), (int)((tsd.y >> sh) & 0xFFu), (int)((tsd.z >> sh) & 0xFFu),
                        (int)((tsd.w >> sh) & 0xFFu)};
+    // weight scale dword: the E8M0 bytes of 4 consecutive K blocks; this one's is byte kb % 4
+    const int wsh = 8 * (kb & 3);
     v8i w[4];
     int sw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       w[j] = lds_frag16(wl + tiles[j] * R::TILE);
-      sw[j] = *(const int*)(slot + R::WS_OFF + tiles[j] * 256 + lane * 4);
+      sw[j] = (int)((*(const uint32_t*)(ws + tiles[j] * 256 + lane * 4) >> wsh) & 0xFFu);
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const v8i t = lds_frag16(tl + m * R::TILE);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[m][j] = mfma_fp4_scaled_t<KB4>(w[j], t, acc[m][j], sw[j], st[m]);
+      for (int j = 0; j < 4; ++j) acc[m][j] = mfma_fp4_scaled_t<0>(w[j], t, acc[m][j], sw[j], st[m]);
     }
   } else {
     const float4 ts = *(const float4*)tsl;
@@ -458,7 +494,7 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const int (&ti
       for (int j = 0; j < 4; ++j) w[j] = lds_frag32(wl + tiles[j] * R::TILE);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const v8i t = lds_frag32(tl + m * R::TILE);
+        const v8i t = lds_tok32(tt + m * R::TILE, lane);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float s = tsc[m] * ((G1 && j >= 2) ? sw1 : sw0);
@@ -468,42 +504,99 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const int (&ti
         }
       }
     } else {
-      v8h wh[4][4];
+      // FP8 -> f16 widening is the bulk of the VALU work; the 16 (weight,
+      // token) tiles are visited in an order that needs a new operand only
+      // every other tile, and each operand is widened during the MFMAs of the
+      // tiles before its first use, so the MFMA and VALU pipes overlap.
+      // raw fragments are read from LDS two tiles before they are widened
+      v8i wraw[4], traw[4];
+      wraw[0] = lds_frag32(wl + tiles[0] * R::TILE);
+      wraw[1] = lds_frag32(wl + tiles[1] * R::TILE);
+      traw[0] = lds_tok32(tt, lane);
+      traw[1] = lds_tok32(tt + R::TILE, lane);
+      constexpr int kRead[16] = {2, -1, 6, -1, 3, -1, 7, -1, -1, -1, -1, -1, -1, -1, -1, -1};
+      v8h wh[4][4], th[4][4];
+      widen_fp8(wraw[0], wh[0]);
+      widen_fp8(traw[0], th[0]);
+      // tile order (weight tile, token tile) and the widening done meanwhile:
+      // kWiden[g] = 1 + operand (0..3 weights, 4..7 tokens) whose quarter
+      // kPart[g] (of 4 steps, kSteps[g] steps) is widened during tile g
+      constexpr int kW[16] = {0, 1, 0, 1, 2, 2, 0, 1, 2, 3, 3, 3, 0, 1, 2, 3};
+      constexpr int kT[16] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2, 3, 3, 3, 3};
+      constexpr int kOp[16] = {1, 5, 2, 2, 6, 6, 3, 3, 3, 7, 7, 7, -1, -1, -1, -1};
+      constexpr int kFirst[16] = {0, 0, 0, 2, 0, 2, 0, 2, 3, 0, 2, 3, 0, 0, 0, 0};
+      constexpr int kLast[16] = {4, 4, 2, 4, 2, 4, 2, 3, 4, 2, 3, 4, 0, 0, 0, 0};
+      v4f prev = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) widen_fp8(lds_frag32(wl + tiles[j] * R::TILE), wh[j]);
+      for (int g = 0; g < 16; ++g) {
+        const int j = kW[g], m = kT[g];
+        v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        v8h th[4];
-        widen_fp8(lds_frag32(tl + m * R::TILE), th);
+        for (int k = 0; k < 4; ++k) c = mfma_f16(wh[j][k], th[m][k], c);
+        if (kRead[g] >= 4)
+          traw[kRead[g] - 4] = lds_tok32(tt + (kRead[g] - 4) * R::TILE, lane);
+        else if (kRead[g] >= 0)
+          wraw[kRead[g]] = lds_frag32(wl + tiles[kRead[g]] * R::TILE);
+        if (kOp[g] >= 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float s = tsc[m] * ((G1 && j >= 2) ? sw1 : sw0);
-          v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) c = mfma_f16(wh[j][k], th[k], c);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(c[i], s, acc[m][j][i]);
+          for (int st = kFirst[g]; st < kLast[g]; ++st) {
+            const int op = kOp[g];
+            const v8i& raw = (op < 4) ? wraw[op] : traw[op - 4];
+            const uint32_t d0 = (uint32_t)raw[2 * st], d1 = (uint32_t)raw[2 * st + 1];
+            const uint4 v = make_uint4(e4m3x2_to_f16x2<false>(d0), e4m3x2_to_f16x2<true>(d0),
+                                       e4m3x2_to_f16x2<false>(d1), e4m3x2_to_f16x2<true>(d1));
+            if (op < 4)
+              wh[op][st] = __builtin_bit_cast(v8h, v);
+            else
+              th[op - 4][st] = __builtin_bit_cast(v8h, v);
+          }
         }
+        if (g > 0) {
+          const int pj = kW[g - 1], pm = kT[g - 1];
+          const float s = tsc[pm] * ((G1 && pj >= 2) ? sw1 : sw0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[pm][pj][i] = fmaf(prev[i], s, acc[pm][pj][i]);
+        }
+        prev = c;
+      }
+      {
+        const float s = tsc[3] * ((G1) ? sw1 : sw0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[3][3][i] = fmaf(prev[i], s, acc[3][3][i]);
       }
     }
   }
 }
 
-// GEMM1 epilogue for the transposed accumulators: lane l holds, for token
-// t = wt*64 + m*16 + l%16, intermediate columns 32*wn + 16*jj + 4*(l/16) + i
-// of the N tile (gate in acc[m][jj], up in acc[m][jj+2]).  Pad rows give 0.
+// ===========================================================================
+// Streaming kernel (block_m 64 / 128): the ring kernel made persistent.  One
+// workgroup per CU walks a list of (M block, N tile) items, and its load ring
+// runs on across item boundaries: the first K blocks of the next item are in
+// flight while the current item finishes and writes its epilogue, so the
+// ring never drains.  Item metadata (sorted pair ids, and for GEMM2 the
+// routing weights of those pairs) also arrives by direct-to-LDS loads, one
+// item ahead, so no load the compiler would wait on sits in the stream.
+// ===========================================================================
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ int uniform_load_i32(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+// GEMM1 epilogue of the streaming kernel: as epilogue_gemm1_t, but the codes
+// go to HBM straight from registers (4 FP8 codes or 4 E2M1 nibbles per lane
+// and 16-column group) instead of through an LDS stage.
 template <int MODE, int BM>
-__device__ __forceinline__ void epilogue_gemm1_t(const GemmArgs& p, const v4f (&acc)[4][4], float (*red)[BM],
-                                                 const int32_t* src_lds, uint8_t* stage, int row0, int nt, int wt,
-                                                 int wn) {
-  constexpr int NTH = Ring<MODE, BM>::NTH;
-  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, c16 = lane & 15;
+__device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&acc)[4][4], float (*red)[BM],
+                                                 const int32_t* sid, int row0, int nt, int wt, int wn) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
   const float L = p.limit;
   float av[4][2][4];
   float tmax[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const bool real = src_lds[wt * 64 + m * 16 + c16] >= 0;
+    const bool real = sid[wt * 64 + m * 16 + c16] < p.num_pairs;
     float mx = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
@@ -522,26 +615,22 @@ __device__ __forceinline__ void epilogue_gemm1_t(const GemmArgs& p, const v4f (&
 #pragma unroll
       for (int m = 0; m < 4; ++m) red[wn][wt * 64 + m * 16 + c16] = tmax[m];
     }
-    __syncthreads();
+    lds_barrier();
     const int nsc = p.Ip / 128;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int t = wt * 64 + m * 16 + c16;
       const float amax = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
       const float s = amax / kE4M3Max;
+      uint8_t* row = p.aq + (int64_t)(row0 + t) * p.Ip + nt * 128 + 32 * wn + 4 * q;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         uint32_t packed = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) packed |= ((amax > 0.0f) ? fp8_quant(av[m][jj][i], s) : 0u) << (8 * i);
-        *(uint32_t*)(stage + t * 128 + 32 * wn + 16 * jj + 4 * q) = packed;
+        *(uint32_t*)(row + 16 * jj) = packed;
       }
       if (wn == 0 && q == 0) ((float*)p.as)[(int64_t)(row0 + t) * nsc + nt] = (amax > 0.0f) ? s : 0.0f;
-    }
-    __syncthreads();
-    for (int c = tid; c < BM * 8; c += NTH) {
-      const int r = c >> 3, cc = c & 7;
-      *(uint4*)(p.aq + (int64_t)(row0 + r) * p.Ip + nt * 128 + cc * 16) = *(const uint4*)(stage + r * 128 + cc * 16);
     }
   } else {
     const int nsc = p.Ip / 32;
@@ -550,34 +639,31 @@ __device__ __forceinline__ void epilogue_gemm1_t(const GemmArgs& p, const v4f (&
       const int t = wt * 64 + m * 16 + c16;
       const uint32_t b = e8m0_byte(tmax[m]);
       const float inv = e8m0_inverse(b);
+      uint8_t* row = p.aq + (int64_t)(row0 + t) * (p.Ip / 2) + nt * 64 + 16 * wn + 2 * q;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         uint32_t packed = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) packed |= mx_quant(av[m][jj][i], inv) << (4 * i);
-        *(uint16_t*)(stage + t * 64 + 16 * wn + 8 * jj + 2 * q) = (uint16_t)packed;
+        *(uint16_t*)(row + 8 * jj) = (uint16_t)packed;
       }
       if (q == 0) ((uint8_t*)p.as)[(int64_t)(row0 + t) * nsc + nt * 4 + wn] = (uint8_t)b;
-    }
-    __syncthreads();
-    for (int c = tid; c < BM * 4; c += NTH) {
-      const int r = c >> 2, cc = c & 3;
-      *(uint4*)(p.aq + (int64_t)(row0 + r) * (p.Ip / 2) + nt * 64 + cc * 16) = *(const uint4*)(stage + r * 64 + cc * 16);
     }
   }
 }
 
-// GEMM2 epilogue (transposed accumulators): y[pair, 4 columns] per lane.
+// GEMM2 epilogue of the streaming kernel: routing weights from LDS.
 template <int BM>
-__device__ __forceinline__ void epilogue_gemm2_t(const GemmArgs& p, const v4f (&acc)[4][4], const int32_t* sid_lds,
-                                                 int nt, int wt, int wn) {
+__device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&acc)[4][4], const int32_t* sid,
+                                                 const float* wts, int nt, int wt, int wn) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const int sid = sid_lds[wt * 64 + m * 16 + c16];
-    if (sid < p.num_pairs) {
-      const float w = p.topk_w[sid];
-      float* yrow = p.y + (int64_t)sid * p.N + nt * 256 + 64 * wn + 4 * q;
+    const int t = wt * 64 + m * 16 + c16;
+    const int s = sid[t];
+    if (s < p.num_pairs) {
+      const float w = wts[t];
+      float* yrow = p.y + (int64_t)s * p.N + nt * 256 + 64 * wn + 4 * q;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const v4f v = acc[m][j];
@@ -587,19 +673,25 @@ __device__ __forceinline__ void epilogue_gemm2_t(const GemmArgs& p, const v4f (&
   }
 }
 
+// Any K works.  Item metadata of item ii+1 is loaded when the loads of item ii
+// start; when an item has fewer than S-1 K blocks that is too late for the
+// ring's own waits to cover it, and the kernel then waits for it explicitly.
 template <int MODE, int BM, bool G1, int S>
-__global__ __launch_bounds__(BM * 4) void moe_gemm_ring_kernel(GemmArgs p) {
+__global__ __launch_bounds__(BM * 4) void moe_gemm_stream_kernel(GemmArgs p) {
   using R = Ring<MODE, BM>;
-  static_assert(S >= 2 && S <= 5, "ring depth");
-  static_assert(MODE != kQuantMx || S == 4, "MX: S == 4 so that kb % 4 is the slot index");
+  static_assert(S >= 3 && S <= 5, "ring depth");
+  constexpr int NI = BM / 64;  // dword loads that cover one BM-long array
+  constexpr int NB = S + 1;    // item-metadata buffers (items in flight, plus one)
+  constexpr int NWS = S + 1;   // MX weight-scale group buffers
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[R::SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[R::SLOT];
-  __shared__ __attribute__((aligned(1024))) uint8_t slot2[S > 2 ? R::SLOT : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t slot2[R::SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t slot3[S > 3 ? R::SLOT : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t slot4[S > 4 ? R::SLOT : 16];
-  __shared__ int32_t src_lds[BM];
-  __shared__ int32_t sid_lds[BM];
+  __shared__ __attribute__((aligned(256))) int32_t ids_lds[NB][BM];
+  __shared__ __attribute__((aligned(256))) float wts_lds[G1 ? 1 : NB][BM];
   __shared__ float red[4][BM];
+  __shared__ __attribute__((aligned(256))) uint8_t ws_buf[MODE == kQuantMx ? NWS : 1][MODE == kQuantMx ? R::WS_BYTES : 16];
   auto slot = [&](auto ic) -> uint8_t* {
     constexpr int i = decltype(ic)::value;
     if constexpr (i == 0) return slot0;
@@ -612,79 +704,122 @@ __global__ __launch_bounds__(BM * 4) void moe_gemm_ring_kernel(GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wt = wave >> 2, wn = wave & 3;
-  const int mblk = blockIdx.x / p.n_tiles;
-  const int nt = blockIdx.x % p.n_tiles;
+  // items of XCD x: the contiguous chunk x; workgroup j of the XCD takes
+  // items j, j + nw, j + 2 nw, ... of it (nw workgroups per XCD)
   const int npp = __builtin_amdgcn_readfirstlane(*p.npp);
-  if (mblk * BM >= npp) return;
-  const int e = __builtin_amdgcn_readfirstlane(p.block_expert[mblk]);
-  const int row0 = mblk * BM;
+  const int items = (npp / BM) * p.n_tiles;
+  const int per = (items + kXcds - 1) / kXcds;
+  const int lo = (blockIdx.x % kXcds) * per;
+  const int hi = min(lo + per, items);
+  const int nw = gridDim.x / kXcds;
+  const int first = lo + (int)(blockIdx.x / kXcds);
+  if (first >= hi) return;
+  const int n_my = (hi - first + nw - 1) / nw;
   const int KB = p.K / 128;
   const int NT16 = p.N / 16;
+  const int total = n_my * KB;
+  const bool short_items = KB < S - 1;
+  auto item_m = [&](int ii) { return (first + ii * nw) / p.n_tiles; };
+  auto item_nt = [&](int ii) { return (first + ii * nw) % p.n_tiles; };
 
-  if (tid < BM) {
-    const int sid = p.sorted_ids[row0 + tid];
-    const bool valid = sid < p.num_pairs;
-    sid_lds[tid] = sid;
-    src_lds[tid] = valid ? (G1 ? sid / p.top_k : row0 + tid) : -1;
-  }
-  __syncthreads();
-
-  // per-lane load addresses (pad rows read token 0 / their own zero rows; their
-  // results are discarded or zeroed in the epilogue)
-  RingSrc<MODE, BM> rs;
-#pragma unroll
-  for (int q = 0; q < R::DW; ++q) {
-    const int g = wave * R::DW + q, tile = g / R::HALVES, h = g % R::HALVES;
-    const int t16 = ring_tile<G1>(p, nt, tile);
-    rs.w[q] = p.B + (((int64_t)e * NT16 + t16) * KB) * R::TILE + h * 1024 + lane * 16;
-  }
-  auto row_of = [&](int r) -> int64_t {
-    const int s = src_lds[r];
-    return G1 ? (s >= 0 ? s : 0) : (int64_t)(row0 + r);
+  // sorted pair ids of item ii -> ids_lds[ii % NB] (waves 0 .. NI-1)
+  auto issue_ids = [&](int ii) {
+    if (wave < NI) dma4(p.sorted_ids + item_m(ii) * BM + wave * 64 + lane, lds_addr(&ids_lds[ii % NB][wave * 64]));
   };
-#pragma unroll
-  for (int q = 0; q < R::DT; ++q) {
-    const int g = wave * R::DT + q, mt = g / R::HALVES, h = g % R::HALVES;
-    const int64_t row = row_of(mt * 16 + (lane & 15));
-    rs.t[q] = p.A + row * p.lda + (lane >> 4) * (R::AROW / 4) + h * 16;
-  }
-  {
-    const int64_t row = row_of(wt * 64 + (lane & 3) * 16 + (lane >> 2));
-    rs.ts = (MODE == kQuantMx) ? (const uint8_t*)p.As + row * p.ldas : (const uint8_t*)p.As + row * p.ldas * 4;
-  }
-  if constexpr (R::DWS > 0) {
-    const int KBq = (KB + 3) / 4;
-#pragma unroll
-    for (int q = 0; q < R::DWS; ++q) {
-      const int t16 = ring_tile<G1>(p, nt, wave * R::DWS + q);
-      rs.ws[q] = (const uint8_t*)p.Bs + ((((int64_t)e * NT16 + t16) * KBq) * 64 + lane) * 4;
+  // GEMM2: routing weight of each row of item ii (its ids must be visible)
+  auto issue_wts = [&](int ii) {
+    if constexpr (!G1) {
+      if (wave >= NI && wave < 2 * NI) {
+        const int r0 = (wave - NI) * 64;
+        const int s = ids_lds[ii % NB][r0 + lane];
+        dma4(p.topk_w + (s < p.num_pairs ? s : 0), lds_addr(&wts_lds[ii % NB][r0]));
+      }
     }
-  }
+  };
 
-  // the wave's 4 local weight tiles and its FP8 weight-scale rows
+  // ---- issue side: per-lane source addresses of the item being loaded
+  RingSrc<MODE, BM> rs;
+  int wts_step = -1, wts_item = 0;
+  auto setup_issue = [&](int ii, int s) {
+    const int m = item_m(ii), nt = item_nt(ii);
+    const int e = uniform_load_i32(p.block_expert + m);
+#pragma unroll
+    for (int q = 0; q < R::DW; ++q) {
+      const int g = wave * R::DW + q, tile = g / R::HALVES, h = g % R::HALVES;
+      rs.w[q] = p.B + (((int64_t)e * NT16 + ring_tile<G1>(p, nt, tile)) * KB) * R::TILE + h * 1024 + lane * 16;
+    }
+    const int32_t* ids = ids_lds[ii % NB];
+    auto row_of = [&](int r) -> int64_t {
+      if constexpr (G1) {
+        const int sid = ids[r];
+        return sid < p.num_pairs ? sid / p.top_k : 0;
+      } else {
+        return (int64_t)m * BM + r;
+      }
+    };
+#pragma unroll
+    for (int q = 0; q < R::DT; ++q) {
+      const int g = wave * R::DT + q, mt = g / R::HALVES, h = g % R::HALVES;
+      rs.t[q] = p.A + row_of(mt * 16 + (lane & 15)) * p.lda + h * 64 + (lane >> 4) * 16;
+    }
+    {
+      const int64_t row = row_of(ring_scale_row(wave, lane));
+      rs.ts = (MODE == kQuantMx) ? (const uint8_t*)p.As + row * p.ldas : (const uint8_t*)p.As + row * p.ldas * 4;
+    }
+    if constexpr (R::DWS > 0) {
+      const int KBq = (KB + 3) / 4;
+#pragma unroll
+      for (int q = 0; q < R::DWS; ++q)
+        rs.ws[q] = (const uint8_t*)p.Bs +
+                   ((((int64_t)e * NT16 + ring_tile<G1>(p, nt, wave * R::DWS + q)) * KBq) * 64 + lane) * 4;
+    }
+    // metadata of the next item: ids now; GEMM2 weights S-1 steps later,
+    // once the ring's waits have covered the ids (or right away after an
+    // explicit wait when items are short)
+    if (ii + 1 < n_my) {
+      issue_ids(ii + 1);
+      if (short_items) {
+        vm_wait_barrier<0>();
+        if constexpr (!G1) {
+          issue_wts(ii + 1);
+          vm_wait_barrier<0>();
+        }
+      } else {
+        wts_step = s + S - 1;
+        wts_item = ii + 1;
+      }
+    }
+  };
+
+  // ---- compute side: state of the item being multiplied
   int tiles[4];
-  bool active;
-  const float* wsr0 = nullptr;
-  const float* wsr1 = nullptr;
   if constexpr (G1) {
     tiles[0] = 2 * wn; tiles[1] = 2 * wn + 1; tiles[2] = 8 + 2 * wn; tiles[3] = 9 + 2 * wn;
-    active = true;
-    if constexpr (MODE != kQuantMx) {
-      const int NB = p.N / 128;
-      wsr0 = (const float*)p.Bs + ((int64_t)e * NB + nt) * KB;
-      wsr1 = (const float*)p.Bs + ((int64_t)e * NB + p.Ip / 128 + nt) * KB;
-    }
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) tiles[j] = 4 * wn + j;
-    active = nt * 256 + 64 * wn < p.N;
-    if constexpr (MODE != kQuantMx) {
-      const int NB = p.N / 128;
-      const int blk = min(nt * 2 + (wn >> 1), NB - 1);
-      wsr0 = (const float*)p.Bs + ((int64_t)e * NB + blk) * KB;
-      wsr1 = wsr0;
-    }
   }
+  int c_nt = 0, c_row0 = 0;
+  bool active = true;
+  const float* wsr0 = nullptr;
+  const float* wsr1 = nullptr;
+  auto setup_compute = [&](int ii) {
+    const int m = item_m(ii);
+    c_nt = item_nt(ii);
+    c_row0 = m * BM;
+    if constexpr (!G1) active = c_nt * 256 + 64 * wn < p.N;
+    if constexpr (MODE != kQuantMx) {
+      const int e = uniform_load_i32(p.block_expert + m);
+      const int NB128 = p.N / 128;
+      if constexpr (G1) {
+        wsr0 = (const float*)p.Bs + ((int64_t)e * NB128 + c_nt) * KB;
+        wsr1 = (const float*)p.Bs + ((int64_t)e * NB128 + p.Ip / 128 + c_nt) * KB;
+      } else {
+        wsr0 = (const float*)p.Bs + ((int64_t)e * NB128 + min(c_nt * 2 + (wn >> 1), NB128 - 1)) * KB;
+        wsr1 = wsr0;
+      }
+    }
+  };
 
   v4f acc[4][4];
 #pragma unroll
@@ -692,44 +827,77 @@ __global__ __launch_bounds__(BM * 4) void moe_gemm_ring_kernel(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[m][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Prologue: K blocks 0 .. S-2 in flight.  Every K-block step then issues
-  // exactly one slot (past the last block it reloads block KB-1 into the slot
-  // just freed, which is never read), so the wait count is the constant
-  // (S-2)*D and the steps of a full group carry no branch between the loads
-  // and the LDS reads: the compiler's own wait insertion can then tell the
-  // ring slots apart and adds no vmcnt(0).
+  // issue cursor (item, K block) and MX weight-scale groups: the group of up
+  // to 4 K blocks that starts at K block kb (kb % 4 == 0) goes to
+  // ws_buf[group count % NWS] with the loads of that K block
+  int i_ii = 0, i_kb = 0, i_grp = 0;
+  auto issue_next = [&](auto slot_c, int s) {
+    if (i_ii < n_my) {
+      const uint8_t* ws = nullptr;
+      if constexpr (MODE == kQuantMx) {
+        if ((i_kb & 3) == 0) ws = ws_buf[(i_grp++) % NWS];
+      }
+      ring_issue<MODE, BM>(rs, slot(slot_c), wave, i_kb, ws);
+      if (++i_kb == KB) {
+        i_kb = 0;
+        if (++i_ii < n_my) setup_issue(i_ii, s);
+      }
+    } else {
+      ring_issue<MODE, BM>(rs, slot(slot_c), wave, KB - 1, nullptr);  // past the end: reload, never read
+    }
+  };
+
+  // prologue: metadata of item 0, then K blocks 0 .. S-2 of the stream
+  issue_ids(0);
+  vm_wait_barrier<0>();
+  if constexpr (!G1) {
+    issue_wts(0);
+    vm_wait_barrier<0>();
+  }
+  setup_issue(0, -(S - 1));  // logically before the loads of stage 0
+  setup_compute(0);
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    (ring_issue<MODE, BM>(rs, slot(std::integral_constant<int, I>{}), wave, min(I, KB - 1)), ...);
+    (issue_next(std::integral_constant<int, I>{}, I - (S - 1)), ...);
   }(std::make_integer_sequence<int, S - 1>{});
 
-  auto step = [&](auto dc, int kb) {
+  int c_ii = 0, c_kb = 0, c_grp = 0;  // compute cursor
+  const uint8_t* c_ws = ws_buf[0];
+  auto step = [&](auto dc, int s) {
     constexpr int d = decltype(dc)::value;
     float sw0 = 0.0f, sw1 = 0.0f;
     if constexpr (MODE != kQuantMx) {
-      sw0 = uniform_load(wsr0 + kb);
-      sw1 = G1 ? uniform_load(wsr1 + kb) : sw0;
+      sw0 = uniform_load(wsr0 + c_kb);
+      sw1 = G1 ? uniform_load(wsr1 + c_kb) : sw0;
     }
     vm_wait_barrier<(S - 2) * R::D>();
-    ring_issue<MODE, BM>(rs, slot(std::integral_constant<int, (d + S - 1) % S>{}), wave, min(kb + S - 1, KB - 1));
-    if (active) ring_compute<MODE, BM, G1, d & 3>(slot(std::integral_constant<int, d>{}), tiles, wave, wt, sw0, sw1, acc);
+    if (s == wts_step) issue_wts(wts_item);
+    issue_next(std::integral_constant<int, (d + S - 1) % S>{}, s);
+    if constexpr (MODE == kQuantMx) {
+      if ((c_kb & 3) == 0) c_ws = ws_buf[(c_grp++) % NWS];
+    }
+    if (active)
+      ring_compute<MODE, BM, G1>(slot(std::integral_constant<int, d>{}), c_ws, tiles, wt, c_kb, sw0, sw1, acc);
+    if (++c_kb == KB) {
+      const int32_t* ids = ids_lds[c_ii % NB];
+      if constexpr (G1) {
+        epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
+      } else {
+        if (active) epilogue_gemm2_s<BM>(p, acc, ids, wts_lds[c_ii % NB], c_nt, wt, wn);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      c_kb = 0;
+      if (++c_ii < n_my) setup_compute(c_ii);
+    }
   };
-  int kb0 = 0;
-  for (; kb0 + S <= KB; kb0 += S) {
+  for (int s0 = 0; s0 < total; s0 += S) {
     [&]<int... I>(std::integer_sequence<int, I...>) {
-      (step(std::integral_constant<int, I>{}, kb0 + I), ...);
+      ((s0 + I < total ? step(std::integral_constant<int, I>{}, s0 + I) : void()), ...);
     }(std::make_integer_sequence<int, S>{});
   }
-  [&]<int... I>(std::integer_sequence<int, I...>) {
-    ((kb0 + I < KB ? step(std::integral_constant<int, I>{}, kb0 + I) : void()), ...);
-  }(std::make_integer_sequence<int, S - 1>{});
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the tail reloads land before slot 0 is reused
-
-  __syncthreads();  // every wave is done with the ring; slot 0 becomes the epilogue stage
-  if constexpr (G1) {
-    epilogue_gemm1_t<MODE, BM>(p, acc, red, src_lds, slot0, row0, nt, wt, wn);
-  } else {
-    if (active) epilogue_gemm2_t<BM>(p, acc, sid_lds, nt, wt, wn);
-  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after the workgroup ends
 }
 
 // ===========================================================================
@@ -905,19 +1073,42 @@ __global__ __launch_bounds__(256) void moe_gemm_direct_kernel(GemmArgs p) {
 #ifndef MOE_RING_S_FP8
 #define MOE_RING_S_FP8 3
 #endif
+#ifndef MOE_RING_S_MX
+#define MOE_RING_S_MX 5
+#endif
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 template <int MODE, bool G1>
 static hipError_t launch_gemm_mode(int block_m, int nb, const GemmArgs& a, hipStream_t s) {
-  constexpr int SR = (MODE == kQuantMx) ? 4 : MOE_RING_S_FP8;
+  constexpr int SR = (MODE == kQuantMx) ? MOE_RING_S_MX : MOE_RING_S_FP8;
   dim3 grid((unsigned)((int64_t)nb * a.n_tiles)), block(256);
+  // the ring kernels map workgroups to items per XCD: every XCD needs as many
+  // workgroups as the largest chunk, so the grid is a multiple of kXcds
+  const int64_t items = (int64_t)nb * a.n_tiles;
+  dim3 ring_grid((unsigned)((items + kXcds - 1) / kXcds * kXcds));
+  // the streaming kernel: one workgroup per CU (its LDS use allows no more)
+  const int64_t wgs = (device_cus() + kXcds - 1) / kXcds * kXcds;
+  dim3 stream_grid((unsigned)(items < wgs ? ring_grid.x : wgs));
   switch (block_m) {
     case 16: hipLaunchKernelGGL((moe_gemm_direct_kernel<MODE, 16, G1, MOE_DIRECT_PD>), grid, block, 0, s, a); break;
     case 32: hipLaunchKernelGGL((moe_gemm_direct_kernel<MODE, 32, G1, MOE_DIRECT_PD>), grid, block, 0, s, a); break;
     case 64:
-      hipLaunchKernelGGL((moe_gemm_ring_kernel<MODE, 64, G1, SR>), grid, dim3(Ring<MODE, 64>::NTH), 0, s, a);
+      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 64, G1, SR>), stream_grid, dim3(Ring<MODE, 64>::NTH), 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((moe_gemm_ring_kernel<MODE, 128, G1, SR>), grid, dim3(Ring<MODE, 128>::NTH), 0, s, a);
+      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 128, G1, SR>), stream_grid, dim3(Ring<MODE, 128>::NTH), 0, s, a);
       break;
   }
   return hipGetLastError();

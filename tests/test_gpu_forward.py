@@ -51,6 +51,7 @@ def _oracle(wl, x, lg):
 
 TINY = W.WORKLOADS["tiny_fp8"]
 MID = W.Workload("mid", T=200, H=512, I=384, E=16, top_k=4, mode="fp8", outlier_frac=0.01)
+STREAM = W.Workload("stream", T=2048, H=1536, I=1024, E=8, top_k=4, mode="fp8", outlier_frac=0.01)
 
 CASES = {
     "tiny_fp8": (TINY, None),
@@ -69,6 +70,12 @@ CASES = {
     "single_expert_fp8": (MID.with_(E=1, top_k=1, T=40), 16),
     "all_experts_mxfp4": (W.Workload("kE", T=24, H=256, I=128, E=16, top_k=16, mode="mxfp4"), 16),
     "big_k_ragged_fp8": (W.Workload("rag", T=37, H=384, I=640, E=24, top_k=5, mode="fp8"), 32),
+    # more (M block, N tile) items than workgroups: the persistent GEMMs walk
+    # several items each and their load rings run across item boundaries
+    "stream_fp8_bm64": (STREAM, 64),
+    "stream_fp8_bm128": (STREAM, 128),
+    "stream_mxfp4_bm64": (STREAM.with_(mode="mxfp4"), 64),
+    "stream_mxfp4_bm128": (STREAM.with_(mode="mxfp4"), 128),
 }
 
 
