@@ -8,57 +8,26 @@
 // "glm5_next: support GLM-5.3-Flash (hybrid KDA + DSA, mHC, NVFP4 expert
 // offload)", Summary: silu(min(gate, lim)) * clamp(up, -lim, lim).
 //
-// Work decomposition: one workgroup (4 waves) per (M block, N tile).  An M
-// block is block_m rows of the expert-sorted pair list, all of one expert.
-//   GEMM1: N tile = 128 intermediate columns = 256 w13 rows; wave w owns
-//          intermediate columns 32w..32w+31, i.e. two 16-row gate tiles and
-//          the two matching up tiles, so the SwiGLU pairs gate and up values
-//          inside one lane.
-//   GEMM2: N tile = 256 output columns; wave w owns rows 64w..64w+63.
-// B (weights) goes straight from HBM into MFMA operand registers from the
-// TILED_V1 layout (1 KB contiguous per wave load).  For block_m >= 64 the A
-// (activation) tile of each 128-wide K block is staged through LDS (double
-// buffered); for block_m <= 32 each lane loads its A fragments directly and
-// the K loop has no barrier (see moe_gemm_direct_kernel).
-//   FP8: each 128-wide K block is one scale block, so its fp32 partial sum
-//        is scaled by act_scale(row) * w_scale(block) and added to the
+// Work decomposition.  An item is one (M block, N tile): block_m rows of the
+// expert-sorted pair list (all of one expert) times 256 weight rows.
+//   GEMM1: the N tile is 128 intermediate columns = 128 gate rows and the
+//          matching 128 up rows of w13, so a lane holds the gate and up value
+//          of the same column and the 1x128 requantisation group is whole.
+//   GEMM2: the N tile is 256 output columns.
+// One persistent workgroup per CU walks a list of items (the moe_gemm_stream
+// kernel below); weight tiles and gathered activation rows stream into LDS.
+//   FP8: each 128-wide K block is one scale block, so its fp32 partial sum is
+//        scaled by act_scale(row) * w_scale(block) and added to the
 //        accumulator (fp32 promotion per K block).  GEMM1 widens the FP8
 //        operands to f16 and uses the f16 MFMA (exact fp32 sums); GEMM2 uses
 //        the FP8 MFMA directly.
-//   MX:  the scaled MFMA applies the E8M0 scales of A and B itself.
+//   MX:  the scaled MFMA applies the E8M0 scales of both operands itself.
 #include <utility>
 
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
-
-template <int MODE>
-struct GemmCfg {
-  static constexpr int AROW = (MODE == kQuantMx) ? 64 : 128;        // A bytes per row per K block (HBM)
-  static constexpr int LROW = (MODE == kQuantFp8F16) ? 256 : AROW;  // bytes per row in LDS
-  static constexpr int ASTR = LROW + 16;                             // padded LDS row stride
-  static constexpr int CPR = AROW / 16;                              // 16-byte chunks per A row
-};
-
-// ---------------------------------------------------------------------------
-// One 128-wide K block of the wave's MT x 4 output tiles, on register operands.
-//   a: A fragments of the MT row subtiles; b: the 4 B tiles (FP8 bytes, or
-//   packed E2M1 in the low 4 dwords); FP8 modes add act scales sa (rows
-//   4*(lane/16)+i of each subtile) and weight block scales sw (per tile).
-// ---------------------------------------------------------------------------
-template <int MT>
-__device__ __forceinline__ void step_fp8(const v8i (&a)[MT], const float (&sa)[MT][4], const v8i (&b)[4],
-                                         const float (&sw)[4], v4f (&acc)[MT][4]) {
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v4f t = mfma_fp8(a[m], b[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(t[i], sa[m][i] * sw[j], acc[m][j][i]);
-    }
-}
 
 // The lane's 32 FP8 bytes as four f16 operands: step st holds bytes
 // 8st..8st+7, i.e. K = 32*(lane/16) + 8st + i for both A and B.
@@ -72,230 +41,8 @@ __device__ __forceinline__ void widen_fp8(const v8i& w, v8h (&h)[4]) {
   }
 }
 
-template <int MT>
-__device__ __forceinline__ void step_f16(const v8h (&a)[MT][4], const float (&sa)[MT][4], const v8i (&b)[4],
-                                         const float (&sw)[4], v4f (&acc)[MT][4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v8h bh[4];
-    widen_fp8(b[j], bh);
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      v4f t = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int st = 0; st < 4; ++st) t = mfma_f16(a[m][st], bh[st], t);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(t[i], sa[m][i] * sw[j], acc[m][j][i]);
-    }
-  }
-}
-
-template <int MT, int OPB>
-__device__ __forceinline__ void step_mx(const v8i (&a)[MT], const int (&sa)[MT], const v8i (&b)[4],
-                                        const int (&sb)[4], v4f (&acc)[MT][4]) {
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[m][j] = mfma_fp4_scaled<OPB>(a[m], b[j], acc[m][j], sa[m], sb[j]);
-}
-
-template <int MT>
-__device__ __forceinline__ void step_mx_kb(int kb, const v8i (&a)[MT], const int (&sa)[MT], const v8i (&b)[4],
-                                           const int (&sb)[4], v4f (&acc)[MT][4]) {
-  switch (kb & 3) {
-    case 0: step_mx<MT, 0>(a, sa, b, sb, acc); break;
-    case 1: step_mx<MT, 1>(a, sa, b, sb, acc); break;
-    case 2: step_mx<MT, 2>(a, sa, b, sb, acc); break;
-    default: step_mx<MT, 3>(a, sa, b, sb, acc); break;
-  }
-}
-
-#ifndef MOE_NT_B
-#define MOE_NT_B 1
-#endif
-#ifndef MOE_KROT
-#define MOE_KROT 0
-#endif
-
-// Weights are read once per launch: optionally with a non-temporal hint.
-__device__ __forceinline__ uint4 load_stream(const uint8_t* ptr) {
-#if MOE_NT_B
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 v = __builtin_nontemporal_load((const u32x4*)ptr);
-  return make_uint4(v.x, v.y, v.z, v.w);
-#else
-  return *(const uint4*)ptr;
-#endif
-}
-
-// B operand registers for the wave's 4 tiles at K block kb (TILED_V1).
-template <int MODE>
-__device__ __forceinline__ void load_b(const GemmArgs& p, const int64_t (&tbase)[4], int kb, v8i (&b)[4]) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if constexpr (MODE != kQuantMx) {
-      const uint8_t* t = p.B + (tbase[j] + kb) * 2048 + lane * 16;
-      uint4 lo = load_stream(t);
-      uint4 hi = load_stream(t + 1024);
-      b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    } else {
-      const uint8_t* t = p.B + (tbase[j] + kb) * 1024 + lane * 16;
-      uint4 lo = load_stream(t);
-      b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
-    }
-  }
-}
-
-// E8M0 dwords of the wave's B tiles for the group of 4 K blocks holding kb.
-__device__ __forceinline__ void load_b_scales(const GemmArgs& p, int e, const int (&t16)[4], int kb, int (&sb)[4]) {
-  const int lane = threadIdx.x & 63;
-  const int KB = p.K / 128, NT16 = p.N / 16;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    sb[j] = (int)((const uint32_t*)p.Bs)[(((int64_t)e * NT16 + t16[j]) * ((KB + 3) / 4) + kb / 4) * 64 + lane];
-}
-
-// fp32 block scales of the wave's B tiles at kb (uniform per wave).
-__device__ __forceinline__ void load_w_scales(const GemmArgs& p, int e, const int (&t16)[4], int kb, float (&sw)[4]) {
-  const int KB = p.K / 128;
-  const float* ws = (const float*)p.Bs;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) sw[j] = ws[((int64_t)e * (p.N / 128) + t16[j] / 8) * KB + kb];
-}
-
-// ---------------------------------------------------------------------------
-// Epilogues.  Lane holds acc[m][j][i] = C[row m*16 + 4*(lane/16) + i]
-// [column 16*j + lane%16 of the wave's tiles].
-// ---------------------------------------------------------------------------
-
-// GEMM1: gate in acc[m][jj], up in acc[m][jj+2] (jj = 0, 1) for intermediate
-// column 32*wn + 16*jj + lane%16 of the N tile, rows rbase + m*16 +
-// 4*(lane/16) + i.  SwiGLU, re-quantise the row per 1x128 (FP8, amax across
-// the 4 column waves) or per 1x32 (MX, the wave's own 32 columns), stage the
-// codes in LDS, write 16-byte chunks.  NTH threads take part.
-template <int MODE, int BM, int MTW, int NTH>
-__device__ __forceinline__ void epilogue_gemm1(const GemmArgs& p, const v4f (&acc)[MTW][4], float (*red)[BM],
-                                               uint8_t* stage, int row0, int nt, int wn, int rbase) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const float L = p.limit;
-  float av[MTW][2][4];
-  float rmax[MTW][4];
-#pragma unroll
-  for (int m = 0; m < MTW; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float mx = 0.0f;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        float a = swiglu_clamped(acc[m][jj][i], acc[m][jj + 2][i], L);
-        av[m][jj][i] = a;
-        mx = fmaxf(mx, fabsf(a));
-      }
-      rmax[m][i] = group_max<16>(mx);
-    }
-  if constexpr (MODE != kQuantMx) {
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int m = 0; m < MTW; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wn][rbase + m * 16 + 4 * (lane >> 4) + i] = rmax[m][i];
-    }
-    __syncthreads();
-    const int nsc = p.Ip / 128;
-#pragma unroll
-    for (int m = 0; m < MTW; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rbase + m * 16 + 4 * (lane >> 4) + i;
-        float amax = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
-        float s = amax / kE4M3Max;
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          uint32_t code = (amax > 0.0f) ? fp8_quant(av[m][jj][i], s) : 0u;
-          stage[r * 128 + 32 * wn + 16 * jj + (lane & 15)] = (uint8_t)code;
-        }
-        if (wn == 0 && (lane & 15) == 0) ((float*)p.as)[(int64_t)(row0 + r) * nsc + nt] = (amax > 0.0f) ? s : 0.0f;
-      }
-    __syncthreads();
-    for (int c = tid; c < BM * 8; c += NTH) {
-      int r = c >> 3, cc = c & 7;
-      *(uint4*)(p.aq + (int64_t)(row0 + r) * p.Ip + nt * 128 + cc * 16) = *(const uint4*)(&stage[r * 128 + cc * 16]);
-    }
-  } else {
-    const int nsc = p.Ip / 32;
-#pragma unroll
-    for (int m = 0; m < MTW; ++m)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = rbase + m * 16 + 4 * (lane >> 4) + i;
-        uint32_t b = e8m0_byte(rmax[m][i]);
-        float inv = e8m0_inverse(b);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-          stage[r * 128 + 32 * wn + 16 * jj + (lane & 15)] = (uint8_t)mx_quant(av[m][jj][i], inv);
-        if ((lane & 15) == 0) ((uint8_t*)p.as)[(int64_t)(row0 + r) * nsc + nt * 4 + wn] = (uint8_t)b;
-      }
-    __syncthreads();
-    for (int c = tid; c < BM * 4; c += NTH) {
-      int r = c >> 2, cc = c & 3;
-      const uint8_t* src = &stage[r * 128 + cc * 32];
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int b2 = 0; b2 < 4; ++b2) {
-          uint32_t lo = src[q * 8 + 2 * b2], hi = src[q * 8 + 2 * b2 + 1];
-          v |= (lo | (hi << 4)) << (8 * b2);
-        }
-        w[q] = v;
-      }
-      *(uint4*)(p.aq + (int64_t)(row0 + r) * (p.Ip / 2) + nt * 64 + cc * 16) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
-}
-
-// GEMM2: y[pair, column] = topk_w[pair] * C for the real pairs of the block.
-template <int MTW>
-__device__ __forceinline__ void epilogue_gemm2(const GemmArgs& p, const v4f (&acc)[MTW][4], const int32_t* sid_lds,
-                                               int nt, int wn, int rbase) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int m = 0; m < MTW; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rbase + m * 16 + 4 * (lane >> 4) + i;
-      const int sid = sid_lds[r];
-      if (sid < p.num_pairs) {
-        const float wt = p.topk_w[sid];
-        float* yrow = p.y + (int64_t)sid * p.N + nt * 256 + 64 * wn + (lane & 15);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) yrow[16 * j] = wt * acc[m][j][i];
-      }
-    }
-}
-
-// The wave's four 16-row B tiles: GEMM1 gate tiles nt*8+2w, +1 and the
-// matching up tiles Ip/16 + ...; GEMM2 rows nt*256 + 64w + 16j.
-template <bool G1>
-__device__ __forceinline__ bool wave_tiles(const GemmArgs& p, int nt, int wave, int (&t16)[4]) {
-  if constexpr (G1) {
-    const int ib = p.Ip / 16;
-    t16[0] = nt * 8 + 2 * wave;
-    t16[1] = t16[0] + 1;
-    t16[2] = ib + t16[0];
-    t16[3] = ib + t16[1];
-    return true;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) t16[j] = nt * 16 + 4 * wave + j;
-    return nt * 256 + 64 * wave < p.N;
-  }
-}
-
 // ===========================================================================
-// Ring kernel (block_m 64 / 128, prefill shapes).
+// The load ring and the per-K-block compute.
 //
 // Operands go from HBM to LDS with direct global->LDS loads
 // (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16*l), through a
@@ -311,32 +58,41 @@ __device__ __forceinline__ bool wave_tiles(const GemmArgs& p, int nt, int wave, 
 // token.  For block FP8 those 4 values share one 128x128 weight scale, and the
 // per-K-block promotion costs one fma per output value.
 //
-// Waves: (wt, wn) = (wave / 4, wave % 4); wt picks 64 tokens (4 row tiles), wn
-// the wave's 4 weight tiles: GEMM1 gate tiles 2wn, 2wn+1 and the matching up
-// tiles 8+2wn, 9+2wn of the N tile; GEMM2 tiles 4wn .. 4wn+3.
+// Waves: (wt, wn) = (wave / 4, wave % 4); wt picks 64 tokens (4 row tiles; a
+// block of fewer than 64 rows has one token group), wn the wave's 4 weight
+// tiles: GEMM1 gate tiles 2wn, 2wn+1 and the matching up tiles 8+2wn, 9+2wn
+// of the N tile; GEMM2 tiles 4wn .. 4wn+3.
 // ===========================================================================
-#ifndef MOE_XCD_MAP
-#define MOE_XCD_MAP 1
-#endif
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
+// Waves of a workgroup: 4 column waves (the N tile's 16 weight tiles, 4 each)
+// times BM/64 token halves of 64 tokens; for BM < 64 one token group of BM/16
+// tiles.  A wave multiplies MT token tiles by its 4 weight tiles.
+constexpr int ring_waves(int bm) { return bm >= 64 ? bm / 16 : 4; }
 
 template <int MODE, int BM>
 struct Ring {
-  static constexpr int NWAVE = BM / 16;  // (BM / 64) token halves x 4 column waves
+  static constexpr int NWAVE = ring_waves(BM);
   static constexpr int NTH = NWAVE * 64;
+  static constexpr int MT = BM >= 64 ? 4 : BM / 16;              // token tiles per wave
+  static constexpr int TT = BM / 16;                             // token tiles per slot
   static constexpr int TILE = (MODE == kQuantMx) ? 1024 : 2048;  // one 16 x 128 operand tile
   static constexpr int HALVES = TILE / 1024;
   static constexpr int AROW = (MODE == kQuantMx) ? 64 : 128;     // token bytes per K block
   static constexpr int W_OFF = 0;                                // 16 weight tiles
-  static constexpr int T_OFF = 16 * TILE;                        // BM/16 token tiles
-  static constexpr int TS_OFF = T_OFF + (BM / 16) * TILE;        // token scales, 256 B per 64 tokens
-  static constexpr int SLOT = TS_OFF + (BM / 64) * 256;
+  static constexpr int T_OFF = 16 * TILE;                        // TT token tiles
+  static constexpr int TS_OFF = T_OFF + TT * TILE;               // token scales, 256 B per 64 tokens
+  static constexpr int NTS = BM >= 64 ? BM / 64 : 1;
+  static constexpr int SLOT = TS_OFF + NTS * 256;
   static constexpr int WS_BYTES = 16 * 256;                      // MX: one group of weight scale dwords
-  static constexpr int DW = 16 * HALVES / NWAVE;                 // loads per wave per slot
-  static constexpr int DT = (BM / 16) * HALVES / NWAVE;
+  static constexpr int DW = 16 * HALVES / NWAVE;                 // weight loads per wave per slot
+  static constexpr int NTD = TT * HALVES;                        // token loads per slot
+  static constexpr int DT = (NTD + NWAVE - 1) / NWAVE;           // ... per wave (BM < 64: waves < NTD)
   static constexpr int DWS = (MODE == kQuantMx) ? 16 / NWAVE : 0;  // every 4th K block only
-  static constexpr int D = DW + DT + 1;                          // loads per wave in every K block
-  static_assert(16 * HALVES % NWAVE == 0 && (BM / 16) * HALVES % NWAVE == 0, "uniform loads per wave");
+  // loads every wave issues in every K block (waits use this minimum; waves
+  // that issue more only wait longer)
+  static constexpr int D = DW + NTD / NWAVE + 1;
+  static_assert(16 * HALVES % NWAVE == 0 && (NTD % NWAVE == 0 || NTD < NWAVE), "load split");
 };
 
 // Direct global->LDS loads, written as inline assembly so that the compiler's
@@ -410,7 +166,8 @@ __device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const u
   for (int q = 0; q < R::DW; ++q)
     dma16<true>(src.w[q] + (int64_t)kb * R::TILE, base + R::W_OFF + (wave * R::DW + q) * 1024);
 #pragma unroll
-  for (int q = 0; q < R::DT; ++q) dma16<false>(src.t[q] + kb * R::AROW, base + R::T_OFF + (wave * R::DT + q) * 1024);
+  for (int q = 0; q < R::DT; ++q)
+    if (wave * R::DT + q < R::NTD) dma16<false>(src.t[q] + kb * R::AROW, base + R::T_OFF + (wave * R::DT + q) * 1024);
   if (lane < 16) dma4(src.ts + kb * 4, base + R::TS_OFF + (wave >> 2) * 256 + (wave & 3) * 64);
   if constexpr (R::DWS > 0) {
     if (ws != nullptr) {
@@ -457,13 +214,14 @@ __device__ __forceinline__ v4f mfma_fp4_scaled_t(const v8i& w, const v8i& t, v4f
 // acc[m][j][i] = C[token (wt*4+m)*16 + lane%16][weight row 16*tile_j + 4*(lane/16) + i].
 template <int MODE, int BM, bool G1>
 __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t* ws, const int (&tiles)[4], int wt,
-                                             int kb, float sw0, float sw1, v4f (&acc)[4][4]) {
+                                             int kb, float sw0, float sw1, v4f (&acc)[Ring<MODE, BM>::MT][4]) {
   using R = Ring<MODE, BM>;
   const int lane = threadIdx.x & 63;
   const uint8_t* wl = slot + R::W_OFF + lane * 16;
   const uint8_t* tt = slot + R::T_OFF + wt * 4 * R::TILE;  // the wave's 4 token tiles
   const uint8_t* tl = tt + lane * 16;
   const uint8_t* tsl = slot + R::TS_OFF + wt * 256 + (lane & 15) * 16;
+  constexpr int MT = R::MT;
   if constexpr (MODE == kQuantMx) {
     const uint4 tsd = *(const uint4*)tsl;
     const int sh = 8 * (lane >> 4);
@@ -479,7 +237,7 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
       sw[j] = (int)((*(const uint32_t*)(ws + tiles[j] * 256 + lane * 4) >> wsh) & 0xFFu);
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < MT; ++m) {
       const v8i t = lds_frag16(tl + m * R::TILE);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[m][j] = mfma_fp4_scaled_t<0>(w[j], t, acc[m][j], sw[j], st[m]);
@@ -493,12 +251,30 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[j] = lds_frag32(wl + tiles[j] * R::TILE);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
+      for (int m = 0; m < MT; ++m) {
         const v8i t = lds_tok32(tt + m * R::TILE, lane);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float s = tsc[m] * ((G1 && j >= 2) ? sw1 : sw0);
           const v4f c = mfma_fp8(w[j], t, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(c[i], s, acc[m][j][i]);
+        }
+      }
+    } else if constexpr (MT < 4) {
+      v8h wh[4][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) widen_fp8(lds_frag32(wl + tiles[j] * R::TILE), wh[j]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        v8h th[4];
+        widen_fp8(lds_tok32(tt + m * R::TILE, lane), th);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float s = tsc[m] * ((G1 && j >= 2) ? sw1 : sw0);
+          v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) c = mfma_f16(wh[j][k], th[k], c);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(c[i], s, acc[m][j][i]);
         }
@@ -569,9 +345,9 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
 }
 
 // ===========================================================================
-// Streaming kernel (block_m 64 / 128): the ring kernel made persistent.  One
-// workgroup per CU walks a list of (M block, N tile) items, and its load ring
-// runs on across item boundaries: the first K blocks of the next item are in
+// Streaming kernel (every block_m).  One persistent workgroup per CU walks a
+// list of (M block, N tile) items, and its load ring runs on across item
+// boundaries: the first K blocks of the next item are in
 // flight while the current item finishes and writes its epilogue, so the
 // ring never drains.  Item metadata (sorted pair ids, and for GEMM2 the
 // routing weights of those pairs) also arrives by direct-to-LDS loads, one
@@ -584,18 +360,23 @@ __device__ __forceinline__ int uniform_load_i32(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
-// GEMM1 epilogue of the streaming kernel: as epilogue_gemm1_t, but the codes
-// go to HBM straight from registers (4 FP8 codes or 4 E2M1 nibbles per lane
-// and 16-column group) instead of through an LDS stage.
+// GEMM1 epilogue: lane l holds, for token t = wt*64 + m*16 + l%16, the
+// intermediate columns 32*wn + 16*jj + 4*(l/16) + i of the N tile (gate in
+// acc[m][jj], up in acc[m][jj+2]).  Clamped SwiGLU, then the row's 1x128
+// amax across the 4 column waves (FP8, through LDS) or the wave's own 1x32
+// amax (MX), RNE codes, stored straight from registers (4 FP8 codes or 4 E2M1
+// nibbles per lane and 16-column group).  Pad rows give zero codes.
 template <int MODE, int BM>
-__device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&acc)[4][4], float (*red)[BM],
-                                                 const int32_t* sid, int row0, int nt, int wt, int wn) {
+__device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&acc)[Ring<MODE, BM>::MT][4],
+                                                 float (*red)[BM], const int32_t* sid, int row0, int nt, int wt,
+                                                 int wn) {
+  constexpr int MT = Ring<MODE, BM>::MT;
   const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
   const float L = p.limit;
-  float av[4][2][4];
-  float tmax[4];
+  float av[MT][2][4];
+  float tmax[MT];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MT; ++m) {
     const bool real = sid[wt * 64 + m * 16 + c16] < p.num_pairs;
     float mx = 0.0f;
 #pragma unroll
@@ -613,12 +394,12 @@ __device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&
   if constexpr (MODE != kQuantMx) {
     if (q == 0) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) red[wn][wt * 64 + m * 16 + c16] = tmax[m];
+      for (int m = 0; m < MT; ++m) red[wn][wt * 64 + m * 16 + c16] = tmax[m];
     }
     lds_barrier();
     const int nsc = p.Ip / 128;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < MT; ++m) {
       const int t = wt * 64 + m * 16 + c16;
       const float amax = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
       const float s = amax / kE4M3Max;
@@ -635,7 +416,7 @@ __device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&
   } else {
     const int nsc = p.Ip / 32;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < MT; ++m) {
       const int t = wt * 64 + m * 16 + c16;
       const uint32_t b = e8m0_byte(tmax[m]);
       const float inv = e8m0_inverse(b);
@@ -652,13 +433,14 @@ __device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&
   }
 }
 
-// GEMM2 epilogue of the streaming kernel: routing weights from LDS.
-template <int BM>
-__device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&acc)[4][4], const int32_t* sid,
+// GEMM2 epilogue: y[pair, 4 consecutive columns] = routing weight * C per
+// lane and weight tile; routing weights from LDS.
+template <int MT>
+__device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&acc)[MT][4], const int32_t* sid,
                                                  const float* wts, int nt, int wt, int wn) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MT; ++m) {
     const int t = wt * 64 + m * 16 + c16;
     const int s = sid[t];
     if (s < p.num_pairs) {
@@ -677,10 +459,12 @@ __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&
 // start; when an item has fewer than S-1 K blocks that is too late for the
 // ring's own waits to cover it, and the kernel then waits for it explicitly.
 template <int MODE, int BM, bool G1, int S>
-__global__ __launch_bounds__(BM * 4) void moe_gemm_stream_kernel(GemmArgs p) {
+__global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(GemmArgs p) {
   using R = Ring<MODE, BM>;
   static_assert(S >= 3 && S <= 5, "ring depth");
-  constexpr int NI = BM / 64;  // dword loads that cover one BM-long array
+  constexpr int MT = R::MT;
+  constexpr int NI = BM >= 64 ? BM / 64 : 1;  // dword loads that cover one BM-long array
+  const bool id_lane = BM >= 64 || (int)(threadIdx.x & 63) < BM;
   constexpr int NB = S + 1;    // item-metadata buffers (items in flight, plus one)
   constexpr int NWS = S + 1;   // MX weight-scale group buffers
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[R::SLOT];
@@ -724,12 +508,13 @@ __global__ __launch_bounds__(BM * 4) void moe_gemm_stream_kernel(GemmArgs p) {
 
   // sorted pair ids of item ii -> ids_lds[ii % NB] (waves 0 .. NI-1)
   auto issue_ids = [&](int ii) {
-    if (wave < NI) dma4(p.sorted_ids + item_m(ii) * BM + wave * 64 + lane, lds_addr(&ids_lds[ii % NB][wave * 64]));
+    if (wave < NI && id_lane)
+      dma4(p.sorted_ids + item_m(ii) * BM + wave * 64 + lane, lds_addr(&ids_lds[ii % NB][wave * 64]));
   };
   // GEMM2: routing weight of each row of item ii (its ids must be visible)
   auto issue_wts = [&](int ii) {
     if constexpr (!G1) {
-      if (wave >= NI && wave < 2 * NI) {
+      if (wave >= NI && wave < 2 * NI && id_lane) {
         const int r0 = (wave - NI) * 64;
         const int s = ids_lds[ii % NB][r0 + lane];
         dma4(p.topk_w + (s < p.num_pairs ? s : 0), lds_addr(&wts_lds[ii % NB][r0]));
@@ -749,12 +534,13 @@ __global__ __launch_bounds__(BM * 4) void moe_gemm_stream_kernel(GemmArgs p) {
       rs.w[q] = p.B + (((int64_t)e * NT16 + ring_tile<G1>(p, nt, tile)) * KB) * R::TILE + h * 1024 + lane * 16;
     }
     const int32_t* ids = ids_lds[ii % NB];
+    // rows past BM (the unused scale entries of a small block) read row 0 / the block's first row
     auto row_of = [&](int r) -> int64_t {
       if constexpr (G1) {
-        const int sid = ids[r];
+        const int sid = r < BM ? ids[r] : p.num_pairs;
         return sid < p.num_pairs ? sid / p.top_k : 0;
       } else {
-        return (int64_t)m * BM + r;
+        return (int64_t)m * BM + (r < BM ? r : 0);
       }
     };
 #pragma unroll
@@ -821,9 +607,9 @@ __global__ __launch_bounds__(BM * 4) void moe_gemm_stream_kernel(GemmArgs p) {
     }
   };
 
-  v4f acc[4][4];
+  v4f acc[MT][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[m][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -882,10 +668,10 @@ __global__ __launch_bounds__(BM * 4) void moe_gemm_stream_kernel(GemmArgs p) {
       if constexpr (G1) {
         epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
       } else {
-        if (active) epilogue_gemm2_s<BM>(p, acc, ids, wts_lds[c_ii % NB], c_nt, wt, wn);
+        if (active) epilogue_gemm2_s<MT>(p, acc, ids, wts_lds[c_ii % NB], c_nt, wt, wn);
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[m][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       c_kb = 0;
@@ -900,181 +686,14 @@ __global__ __launch_bounds__(BM * 4) void moe_gemm_stream_kernel(GemmArgs p) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may land in LDS after the workgroup ends
 }
 
-// ===========================================================================
-// Direct kernel (block_m 16 / 32, decode shapes): no LDS in the K loop.
-// Each lane loads its own A fragments from global memory (the few token rows
-// stay in L2) and the waves stream their B tiles independently through a ring
-// of PD K blocks in registers, so PD-1 blocks of weights are in flight while
-// one is multiplied.
-// ===========================================================================
-template <int BM>
-struct alignas(16) DirectSmem {
-  int32_t src[BM];
-  int32_t sid[BM];
-  float red[4][BM];
-  uint8_t stage[BM * 128];
-};
-
-template <int MODE>
-struct RawA {                    // one A fragment in HBM format
-  uint4 lo, hi;                  // FP8: 32 bytes; MX: lo = 16 bytes
-};
-
-template <int MODE, int BM, bool G1, int PD>
-__global__ __launch_bounds__(256) void moe_gemm_direct_kernel(GemmArgs p) {
-  constexpr int MT = BM / 16;
-  constexpr bool FP8ANY = MODE != kQuantMx;
-  __shared__ DirectSmem<BM> sm;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int mblk = blockIdx.x / p.n_tiles;
-  const int nt = blockIdx.x % p.n_tiles;
-  const int npp = __builtin_amdgcn_readfirstlane(*p.npp);
-  if (mblk * BM >= npp) return;
-  const int e = __builtin_amdgcn_readfirstlane(p.block_expert[mblk]);
-  const int row0 = mblk * BM;
-  const int KB = p.K / 128;
-  const int NT16 = p.N / 16;
-
-  if (tid < BM) {
-    int sid = p.sorted_ids[row0 + tid];
-    bool valid = sid < p.num_pairs;
-    sm.sid[tid] = sid;
-    sm.src[tid] = valid ? (G1 ? sid / p.top_k : row0 + tid) : -1;
-  }
-  int t16[4];
-  const bool wave_active = wave_tiles<G1>(p, nt, wave, t16);
-  int64_t tbase[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) tbase[j] = ((int64_t)e * NT16 + (wave_active ? t16[j] : 0)) * KB;
-  __syncthreads();
-
-  // this lane's A rows: fragment row m*16 + lane%16, scale rows m*16 + 4*(lane/16) + i
-  int asrc[MT];
-  int ssrc[MT][4];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    asrc[m] = sm.src[m * 16 + (lane & 15)];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ssrc[m][i] = sm.src[m * 16 + 4 * (lane >> 4) + i];
-  }
-
-  v4f acc[MT][4];
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[m][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  if (wave_active) {
-    v8i rb[PD][4];
-    RawA<MODE> ra[PD][MT];
-    float rsa[PD][MT][4];   // FP8: act scales
-    int rsx[PD][MT];        // MX: act scale byte
-    float rsw[PD][4];       // FP8: weight block scales
-    int rsb[PD][4];         // MX: weight scale dwords
-
-    auto load_slot = [&](auto d_c, int kb) {
-      constexpr int d = decltype(d_c)::value;
-      load_b<MODE>(p, tbase, kb, rb[d]);
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        uint4 lo = make_uint4(0, 0, 0, 0), hi = make_uint4(0, 0, 0, 0);
-        if (asrc[m] >= 0) {
-          if constexpr (FP8ANY) {
-            const uint8_t* ap = p.A + (int64_t)asrc[m] * p.lda + (int64_t)kb * 128 + (lane >> 4) * 32;
-            lo = *(const uint4*)ap;
-            hi = *(const uint4*)(ap + 16);
-          } else {
-            lo = *(const uint4*)(p.A + (int64_t)asrc[m] * p.lda + (int64_t)kb * 64 + (lane >> 4) * 16);
-          }
-        }
-        ra[d][m].lo = lo;
-        ra[d][m].hi = hi;
-        if constexpr (FP8ANY) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            rsa[d][m][i] = ssrc[m][i] >= 0 ? ((const float*)p.As)[(int64_t)ssrc[m][i] * p.ldas + kb] : 0.0f;
-        } else {
-          rsx[d][m] = asrc[m] >= 0 ? (int)((const uint8_t*)p.As)[(int64_t)asrc[m] * p.ldas + kb * 4 + (lane >> 4)] : 0;
-        }
-      }
-      if constexpr (FP8ANY)
-        load_w_scales(p, e, t16, kb, rsw[d]);
-      else
-        load_b_scales(p, e, t16, kb, rsb[d]);
-    };
-
-    auto compute_slot = [&](auto d_c, int kb) {
-      constexpr int d = decltype(d_c)::value;
-      if constexpr (MODE == kQuantMx) {
-        v8i a[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-          a[m] = v8i{(int)ra[d][m].lo.x, (int)ra[d][m].lo.y, (int)ra[d][m].lo.z, (int)ra[d][m].lo.w, 0, 0, 0, 0};
-        step_mx_kb<MT>(kb, a, rsx[d], rb[d], rsb[d], acc);
-      } else if constexpr (MODE == kQuantFp8) {
-        v8i a[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-          a[m] = v8i{(int)ra[d][m].lo.x, (int)ra[d][m].lo.y, (int)ra[d][m].lo.z, (int)ra[d][m].lo.w,
-                     (int)ra[d][m].hi.x, (int)ra[d][m].hi.y, (int)ra[d][m].hi.z, (int)ra[d][m].hi.w};
-        step_fp8<MT>(a, rsa[d], rb[d], rsw[d], acc);
-      } else {
-        v8h a[MT][4];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          v8i raw = v8i{(int)ra[d][m].lo.x, (int)ra[d][m].lo.y, (int)ra[d][m].lo.z, (int)ra[d][m].lo.w,
-                        (int)ra[d][m].hi.x, (int)ra[d][m].hi.y, (int)ra[d][m].hi.z, (int)ra[d][m].hi.w};
-          widen_fp8(raw, a[m]);
-        }
-        step_f16<MT>(a, rsa[d], rb[d], rsw[d], acc);
-      }
-    };
-
-    // K blocks are visited from a per-workgroup starting block so that the
-    // waves in flight do not all address the same offset of their streams.
-#if MOE_KROT
-    const int kstart = (int)(((unsigned)blockIdx.x * 7u) % (unsigned)KB);
-#else
-    const int kstart = 0;
-#endif
-    auto kmap = [&](int kk) { int kb = kk + kstart; return kb >= KB ? kb - KB : kb; };
-    // prologue: fill the ring
-    [&]<int... D>(std::integer_sequence<int, D...>) {
-      ((D < KB ? load_slot(std::integral_constant<int, D>{}, kmap(D)) : void()), ...);
-    }(std::make_integer_sequence<int, PD>{});
-
-    for (int kb0 = 0; kb0 < KB; kb0 += PD) {
-      [&]<int... D>(std::integer_sequence<int, D...>) {
-        (([&] {
-           const int kk = kb0 + D;
-           if (kk < KB) {
-             compute_slot(std::integral_constant<int, D>{}, kmap(kk));
-             if (kk + PD < KB) load_slot(std::integral_constant<int, D>{}, kmap(kk + PD));
-           }
-         }()),
-         ...);
-      }(std::make_integer_sequence<int, PD>{});
-    }
-  }
-
-  if constexpr (G1) {
-    epilogue_gemm1<MODE, BM, MT, 256>(p, acc, sm.red, sm.stage, row0, nt, wave, 0);
-  } else {
-    if (!wave_active) return;
-    epilogue_gemm2<MT>(p, acc, sm.sid, nt, wave, 0);
-  }
-}
-
-#ifndef MOE_DIRECT_PD
-#define MOE_DIRECT_PD 2
-#endif
 #ifndef MOE_RING_S_FP8
 #define MOE_RING_S_FP8 3
 #endif
 #ifndef MOE_RING_S_MX
 #define MOE_RING_S_MX 5
+#endif
+#ifndef MOE_RING_S_SMALL
+#define MOE_RING_S_SMALL 4
 #endif
 
 // Compute units of the current device (cached per device).
@@ -1092,23 +711,26 @@ static int device_cus() {
 
 template <int MODE, bool G1>
 static hipError_t launch_gemm_mode(int block_m, int nb, const GemmArgs& a, hipStream_t s) {
-  constexpr int SR = (MODE == kQuantMx) ? MOE_RING_S_MX : MOE_RING_S_FP8;
-  dim3 grid((unsigned)((int64_t)nb * a.n_tiles)), block(256);
-  // the ring kernels map workgroups to items per XCD: every XCD needs as many
-  // workgroups as the largest chunk, so the grid is a multiple of kXcds
+  constexpr int SR = (MODE == kQuantMx) ? MOE_RING_S_MX : MOE_RING_S_FP8;    // block_m 64 / 128
+  constexpr int SD = (MODE == kQuantMx) ? MOE_RING_S_MX : MOE_RING_S_SMALL;  // block_m 16 / 32
+  // One workgroup per CU (the ring's LDS use allows no more), fewer when
+  // there are fewer items; a multiple of kXcds so that every XCD gets the
+  // same number of workgroups.
   const int64_t items = (int64_t)nb * a.n_tiles;
-  dim3 ring_grid((unsigned)((items + kXcds - 1) / kXcds * kXcds));
-  // the streaming kernel: one workgroup per CU (its LDS use allows no more)
   const int64_t wgs = (device_cus() + kXcds - 1) / kXcds * kXcds;
-  dim3 stream_grid((unsigned)(items < wgs ? ring_grid.x : wgs));
+  const dim3 grid((unsigned)(items < wgs ? (items + kXcds - 1) / kXcds * kXcds : wgs));
   switch (block_m) {
-    case 16: hipLaunchKernelGGL((moe_gemm_direct_kernel<MODE, 16, G1, MOE_DIRECT_PD>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((moe_gemm_direct_kernel<MODE, 32, G1, MOE_DIRECT_PD>), grid, block, 0, s, a); break;
+    case 16:
+      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 16, G1, SD>), grid, dim3(Ring<MODE, 16>::NTH), 0, s, a);
+      break;
+    case 32:
+      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 32, G1, SD>), grid, dim3(Ring<MODE, 32>::NTH), 0, s, a);
+      break;
     case 64:
-      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 64, G1, SR>), stream_grid, dim3(Ring<MODE, 64>::NTH), 0, s, a);
+      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 64, G1, SR>), grid, dim3(Ring<MODE, 64>::NTH), 0, s, a);
       break;
     default:
-      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 128, G1, SR>), stream_grid, dim3(Ring<MODE, 128>::NTH), 0, s, a);
+      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 128, G1, SR>), grid, dim3(Ring<MODE, 128>::NTH), 0, s, a);
       break;
   }
   return hipGetLastError();

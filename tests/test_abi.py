@@ -197,3 +197,4 @@ def test_pick_block_m():
     assert M.pick_block_m(64, 288, 8) == 16
     assert M.pick_block_m(4096, 288, 8) == 128
     assert M.pick_block_m(600, 288, 8) == 32
+    assert M.pick_block_m(2048, 288, 8) == 128

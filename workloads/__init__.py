@@ -153,8 +153,8 @@ def all_w2(wl: Workload, experts=None, device="cpu") -> torch.Tensor:
 
 
 def pick_block_m(wl_or_T, E: int = 0, top_k: int = 0) -> int:
-    """Rows per expert block: 16 when experts see few tokens (decode), else
-    larger.  A host-side launch choice, not part of the method."""
+    """Rows per expert block: 16 / 32 when experts see few tokens (decode),
+    else 128.  A host-side launch choice, not part of the method."""
     if isinstance(wl_or_T, Workload):
         T, E, top_k = wl_or_T.T, wl_or_T.E, wl_or_T.top_k
     else:
@@ -164,8 +164,6 @@ def pick_block_m(wl_or_T, E: int = 0, top_k: int = 0) -> int:
         return 16
     if per_expert <= 32:
         return 32
-    if per_expert <= 64:
-        return 64
     return 128
 
 
