@@ -465,7 +465,10 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   constexpr int MT = R::MT;
   constexpr int NI = BM >= 64 ? BM / 64 : 1;  // dword loads that cover one BM-long array
   const bool id_lane = BM >= 64 || (int)(threadIdx.x & 63) < BM;
-  constexpr int NB = S + 1;    // item-metadata buffers (items in flight, plus one)
+  // Item-metadata buffers.  While item c is multiplied, the loads run S-1 K
+  // blocks ahead and the metadata one item further: with one K block per item
+  // that is item c + S + 1, so S + 2 buffers keep item c's ids and weights.
+  constexpr int NB = S + 2;
   constexpr int NWS = S + 1;   // MX weight-scale group buffers
   __shared__ __attribute__((aligned(1024))) uint8_t slot0[R::SLOT];
   __shared__ __attribute__((aligned(1024))) uint8_t slot1[R::SLOT];

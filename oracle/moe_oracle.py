@@ -457,6 +457,10 @@ def moe_forward(x: np.ndarray, logits: np.ndarray, W: QuantWeights, top_k: int,
     6. y = deq(aq) . deq(w2[e])^T, fp32.
     7. out[t] = sum over slots j = 0..k-1, in slot order, of fl32(w[t,j] * y),
        accumulated in fp32; first H columns.
+
+    With ``return_stages`` it also returns the routing, the quantised input,
+    per (sample token, slot) pair the SwiGLU output ``a`` (fp32, before
+    re-quantisation) and its codes/scales ``aq``, and the per-pair ``y``.
     """
     mode = W.mode
     x = np.asarray(x, F32)
@@ -470,6 +474,7 @@ def moe_forward(x: np.ndarray, logits: np.ndarray, W: QuantWeights, top_k: int,
     n = len(tok)
     y = np.zeros((n, top_k, Hp), F32)
     aq_all = {}
+    a_all = {}
     for e in np.unique(ids):
         w13d, w2d = dequant_expert(W, int(e))
         rows = np.argwhere(ids == e)  # (token index in sample, slot) pairs, increasing f
@@ -482,12 +487,13 @@ def moe_forward(x: np.ndarray, logits: np.ndarray, W: QuantWeights, top_k: int,
             y[t, j] = yy[i]
             if return_stages:
                 aq_all[(int(t), int(j))] = (aq[i], as_[i])
+                a_all[(int(t), int(j))] = a[i]
     out = np.zeros((n, Hp), F32)
     for j in range(top_k):
         out = (out + (wts[:, j:j + 1] * y[:, j]).astype(F32)).astype(F32)
     out = out[:, :hidden]
     if return_stages:
-        return out, dict(ids=ids, weights=wts, xq=xq, xs=xs, y=y, aq=aq_all)
+        return out, dict(ids=ids, weights=wts, xq=xq, xs=xs, y=y, aq=aq_all, a=a_all)
     return out
 
 

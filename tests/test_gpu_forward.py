@@ -2,7 +2,10 @@
 CPU oracle, on seeded inputs small enough for the oracle to finish in
 seconds while still spanning several tiles, ragged tails and padding, plus
 the method's degenerate cases.  Tolerance: max |out - ref| <= tol * RMS of
-the oracle row, tol = 2e-2 (block FP8) or 6e-2 (MXFP4).
+the oracle row, tol = 2e-2 (block FP8) or 6e-2 (MXFP4), after allowing for
+intermediate codes whose oracle value is at a re-quantisation rounding tie
+(either code is correct up to the fp32 summation order of GEMM1; the
+allowance is computed from the oracle's own values).
 """
 import math
 
@@ -12,7 +15,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from parity_util import assert_rows_close, bf16_to_f32, gpu_weights, log, oracle_weights_cpu
+from parity_util import (assert_rows_close, bf16_to_f32, gpu_weights, log, oracle_weights_cpu,
+                         requant_tie_allowance)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,9 +53,18 @@ def _oracle(wl, x, lg):
     return O.moe_forward(x.float().numpy(), lg.numpy(), Q, wl.top_k, wl.swiglu_limit, wl.H, wl.I)
 
 
+def _oracle_with_ties(wl, x, lg):
+    """Oracle output and the re-quantisation tie allowance of every row."""
+    Q = oracle_weights_cpu(wl)
+    ref, st = O.moe_forward(x.float().numpy(), lg.numpy(), Q, wl.top_k, wl.swiglu_limit, wl.H, wl.I,
+                            return_stages=True)
+    return ref, requant_tie_allowance(st, Q, wl.mode, wl.H)
+
+
 TINY = W.WORKLOADS["tiny_fp8"]
 MID = W.Workload("mid", T=200, H=512, I=384, E=16, top_k=4, mode="fp8", outlier_frac=0.01)
 STREAM = W.Workload("stream", T=2048, H=1536, I=1024, E=8, top_k=4, mode="fp8", outlier_frac=0.01)
+SHORT_K = W.Workload("short_k", T=2048, H=2048, I=128, E=8, top_k=4, mode="fp8", outlier_frac=0.01)
 
 CASES = {
     "tiny_fp8": (TINY, None),
@@ -76,6 +89,11 @@ CASES = {
     "stream_fp8_bm128": (STREAM, 128),
     "stream_mxfp4_bm64": (STREAM.with_(mode="mxfp4"), 64),
     "stream_mxfp4_bm128": (STREAM.with_(mode="mxfp4"), 128),
+    # GEMM2 with a single K block (Ip = 128) and many items per workgroup: the
+    # loads run several items ahead of the compute
+    "short_k_fp8_bm128": (SHORT_K, 128),
+    "short_k_fp8_bm16": (SHORT_K.with_(T=512), 16),
+    "short_k_mxfp4_bm128": (SHORT_K.with_(mode="mxfp4"), 128),
 }
 
 
@@ -84,8 +102,8 @@ def test_forward_matches_oracle(name):
     wl, bm = CASES[name]
     log(f"forward {name}: {W.describe(wl)} block_m={bm}")
     _, _, x, lg, out = _run(wl, bm)
-    ref = _oracle(wl, x, lg)
-    assert_rows_close(bf16_to_f32(out), ref, wl.mode, name)
+    ref, tie = _oracle_with_ties(wl, x, lg)
+    assert_rows_close(bf16_to_f32(out), ref, wl.mode, name, allowance=tie)
 
 
 def test_forward_with_row_strides():

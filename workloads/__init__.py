@@ -84,6 +84,19 @@ WORKLOADS = {
     # skewed routing, padded hidden/intermediate sizes
     "skewed_padded_fp8": Workload("skewed_padded_fp8", T=2048, H=4000, I=1000, E=288, top_k=8,
                                   mode="fp8", Hp=4096, Ip=1024, zipf_s=1.2),
+    # one GPU's share of the layer under tensor parallelism over I (each GPU
+    # holds Ip/n of the gate and up halves and the matching w2 columns)
+    "tp4_decode_fp8": Workload("tp4_decode_fp8", T=64, H=4096, I=256, E=288, top_k=8, mode="fp8"),
+    "tp8_prefill_fp8": Workload("tp8_prefill_fp8", T=4096, H=4096, I=128, E=288, top_k=8, mode="fp8",
+                                outlier_frac=0.01),
+    "tp4_prefill_mxfp4": Workload("tp4_prefill_mxfp4", T=4096, H=4096, I=256, E=288, top_k=8,
+                                  mode="mxfp4"),
+    # a shared expert: one dense FFN under the same contracts (E = 1, top-1,
+    # routing weight 1)
+    "shared_expert_fp8": Workload("shared_expert_fp8", T=4096, H=4096, I=1024, E=1, top_k=1, mode="fp8",
+                                  outlier_frac=0.01),
+    "shared_expert_mxfp4": Workload("shared_expert_mxfp4", T=64, H=4096, I=1024, E=1, top_k=1,
+                                    mode="mxfp4"),
 }
 
 
