@@ -754,32 +754,48 @@ hipError_t launch_gemm2(int mode, int block_m, int nb, const GemmArgs& a, hipStr
 }
 
 // out[t, h] = bf16(sum_j y[t*k + j, h]) with the slot sum in order j = 0..k-1.
+// 8 columns per thread (two 16-byte non-temporal loads per slot: y is read
+// once); the 8 bf16 results go out as one 16-byte store when the row stride
+// allows it.  Columns h .. h+7 stay inside the padded row (Hp is a multiple of
+// 128), only those below H are stored.
+__device__ __forceinline__ float4 load_nt4(const float* p) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 v = __builtin_nontemporal_load((const f4*)p);
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int k, int H, int Hp,
-                                                      uint16_t* __restrict__ out, int64_t ld_out) {
+                                                      uint16_t* __restrict__ out, int64_t ld_out, int vec_store) {
   const int t = blockIdx.y;
-  const int h = (blockIdx.x * 256 + threadIdx.x) * 4;
+  const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (h >= H) return;
   const float* base = y + (int64_t)t * k * Hp + h;
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   for (int j = 0; j < k; ++j) {
-    float4 v = *(const float4*)(base + (int64_t)j * Hp);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+    const float4 v0 = load_nt4(base + (int64_t)j * Hp), v1 = load_nt4(base + (int64_t)j * Hp + 4);
+    a[0] += v0.x; a[1] += v0.y; a[2] += v0.z; a[3] += v0.w;
+    a[4] += v1.x; a[5] += v1.y; a[6] += v1.z; a[7] += v1.w;
   }
   uint16_t* o = out + (int64_t)t * ld_out + h;
-  o[0] = f32_to_bf16(acc.x);
-  if (h + 1 < H) o[1] = f32_to_bf16(acc.y);
-  if (h + 2 < H) o[2] = f32_to_bf16(acc.z);
-  if (h + 3 < H) o[3] = f32_to_bf16(acc.w);
+  if (vec_store && h + 8 <= H) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(a[2 * i]) | ((uint32_t)f32_to_bf16(a[2 * i + 1]) << 16);
+    *(uint4*)o = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (h + i < H) o[i] = f32_to_bf16(a[i]);
+  }
 }
 
 hipError_t launch_combine(const float* y, int T, int k, int H, int Hp, uint16_t* out, int64_t ld_out,
                           hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  dim3 grid((unsigned)((H + 1023) / 1024), (unsigned)T), block(256);
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, y, k, H, Hp, out, ld_out);
+  // 16-byte stores need every row start 16-byte aligned
+  const int vec = ((uintptr_t)out % 16 == 0) && (ld_out % 8 == 0);
+  dim3 grid((unsigned)((H + 2047) / 2048), (unsigned)T), block(256);
+  hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, y, k, H, Hp, out, ld_out, vec);
   return hipGetLastError();
 }
 
