@@ -112,21 +112,34 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 }
 
 // ---------------------------------------------------------------------------
-// Permute-align: one workgroup of NW waves; wave w owns the token range
-// [w*Tw, (w+1)*Tw).  The pairs of expert e in increasing f = t*k + j are, when
-// no token lists an expert twice (what top-k routing produces), the tokens
-// that chose e in increasing t, so:
-//   pass 1: per-wave expert histograms (LDS atomics);
-//   scan:   padded counts -> offsets; per-wave cursors = offset + pairs of
-//           earlier waves;
-//   pass 2: each wave walks its tokens 64 at a time (lane = token, its k ids
-//           in registers); a 64-bit LDS mask per expert marks the lanes that
-//           chose it, and a pair's position is its cursor + popcount(mask &
-//           lanes below).
-// If some token lists an expert twice, pass 2 instead ranks pairs with a
-// ballot match loop over f order (same result definition, slower).
+// Permute-align: stable counting sort of the pairs by expert, in one launch
+// and with no scratch memory.  The tokens are cut into chunks, one per
+// workgroup.  Every workgroup histograms ALL pairs, split into those before
+// its chunk and those after it, so each one knows the global padded offsets
+// and, per expert, how many of that expert's pairs come before its chunk:
+// no workgroup waits for another.  Inside the chunk, RW ranking waves own
+// consecutive token sub-ranges.  The pairs of expert e in increasing
+// f = t*k + j are, when no token lists an expert twice (what top-k routing
+// produces), the tokens that chose e in increasing t, so:
+//   histogram: pairs outside the chunk by all waves (flat in f, coalesced),
+//              the chunk's pairs per ranking wave (LDS atomics);
+//   scan:      padded counts -> offsets; per-wave cursors = offset + pairs
+//              before the chunk + pairs of earlier ranking waves;
+//   fill:      padding sentinels, block experts and the tail past the last
+//              segment, shared out over every wave of the grid;
+//   rank:      each ranking wave walks its tokens 64 at a time (lane = token,
+//              its k ids in registers); a 64-bit LDS mask per expert marks the
+//              lanes that chose it, and a pair's position is its cursor +
+//              popcount(mask & lanes below).
+// If some token of a chunk lists an expert twice, that chunk's pairs are
+// instead ranked with a ballot match loop over f order (same result, slower).
+// The histogram of the pairs outside the chunk costs every workgroup O(P), so
+// the number of chunks is capped.
 // ---------------------------------------------------------------------------
 constexpr int kMaxTopK = 16;
+constexpr int kPermWaves = 16;      // waves per workgroup
+constexpr int kPermRankWaves = 4;   // of which rank the chunk's pairs
+constexpr int kPermMaxChunks = 256;
 
 template <int NW>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch /* [NW] */, int& total) {
@@ -151,97 +164,127 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch /* [NW] 
   return base + incl - v;
 }
 
-template <int NW>
+// LDS written by some lanes of a wave is read by other lanes of the same
+// wave: a wave's LDS operations complete in order, so ordering the compiler's
+// view is all that is needed.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NW, int RW>
 __global__ __launch_bounds__(64 * NW) void permute_align_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                                int BM, int nb, int32_t* __restrict__ sorted_ids,
+                                                                int BM, int nb, int Tc,
+                                                                int32_t* __restrict__ sorted_ids,
                                                                 int32_t* __restrict__ block_expert,
                                                                 int32_t* __restrict__ offsets,
                                                                 int32_t* __restrict__ npp) {
   constexpr int NT = 64 * NW;
+  static_assert(NT >= 1024, "one thread per expert in the scan");
+  static_assert(RW <= NW, "ranking waves are a subset");
   extern __shared__ __align__(16) unsigned char perm_smem[];
-  int32_t* cur = (int32_t*)perm_smem;                     // [NW][E] pair counts, then positions
-  uint32_t* mask = (uint32_t*)(cur + NW * E);             // [NW][E][2] lane masks (lo, hi)
-  int32_t* scratch = (int32_t*)(mask + NW * E * 2);       // [NW] + duplicate flag
+  int32_t* before = (int32_t*)perm_smem;          // [E] pairs before the chunk; then the expert's pair count
+  int32_t* after = before + E;                    // [E] pairs after the chunk; then the segment offset
+  int32_t* cur = after + E;                       // [RW][E] per-wave chunk counts; then cursors
+  uint32_t* mask = (uint32_t*)(cur + RW * E);     // [RW][E][2] lane masks (lo, hi)
+  int32_t* scratch = (int32_t*)(mask + RW * E * 2);  // [NW] scan partials + duplicate flag
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = T * k;
+  const int tb = min(T, (int)blockIdx.x * Tc), te = min(T, tb + Tc);
+  const int fb = tb * k, fe = te * k;
+  const int Tw = (Tc + RW - 1) / RW;
+  const int w_begin = min(te, tb + wave * Tw), w_end = min(te, w_begin + Tw);  // used by ranking waves
 
-  for (int i = tid; i < NW * E; i += NT) {
-    cur[i] = 0;
-    mask[2 * i] = 0;
-    mask[2 * i + 1] = 0;
-  }
+  for (int i = tid; i < (2 + 3 * RW) * E; i += NT) before[i] = 0;
   if (tid == 0) scratch[NW] = 0;
   __syncthreads();
 
-  const int Tw = (T + NW - 1) / NW;
-  const int t_begin = wave * Tw;
-  const int t_end = min(T, t_begin + Tw);
-
-  // pass 1: histograms; detect a token that lists an expert twice
+  // pairs outside the chunk, flat in f, U loads in flight per thread
+  constexpr int U = 16;
+  const int n_out = P - (fe - fb);
+  for (int base = tid; base < n_out; base += NT * U) {
+    int ev[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * NT;
+      ev[u] = (i < n_out) ? ids[i < fb ? i : i + (fe - fb)] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = ev[u];
+      if (e >= 0 && e < E) atomicAdd((base + u * NT < fb) ? &before[e] : &after[e], 1);
+    }
+  }
+  // the chunk's pairs, per ranking wave; detect a token that lists an expert twice
   bool dup = false;
-  for (int t = t_begin + lane; t < t_end; t += 64) {
-    int ex[kMaxTopK];
+  if (wave < RW) {
+    for (int t = w_begin + lane; t < w_end; t += 64) {
+      int ex[kMaxTopK];
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) ex[j] = (j < k) ? ids[(size_t)t * k + j] : -1;
+      for (int j = 0; j < kMaxTopK; ++j) ex[j] = (j < k) ? ids[(size_t)t * k + j] : -1;
 #pragma unroll
-    for (int j = 0; j < kMaxTopK; ++j) {
-      const int e = ex[j];
-      if (j >= k || e < 0 || e >= E) continue;
-      atomicAdd(&cur[wave * E + e], 1);
+      for (int j = 0; j < kMaxTopK; ++j) {
+        const int e = ex[j];
+        if (j >= k || e < 0 || e >= E) continue;
+        atomicAdd(&cur[wave * E + e], 1);
 #pragma unroll
-      for (int j2 = 0; j2 < j; ++j2) dup |= (ex[j2] == e);
+        for (int j2 = 0; j2 < j; ++j2) dup |= (ex[j2] == e);
+      }
     }
   }
   if (dup) scratch[NW] = 1;
   __syncthreads();
   const bool any_dup = scratch[NW] != 0;
 
-  // scan of padded counts (E <= 1024)
-  constexpr int EPT = (1024 + NT - 1) / NT;
-  int cnt[EPT], pc[EPT];
-  int local = 0;
+  // scan of padded counts: thread e owns expert e (E <= NT)
+  const int e_own = tid;
+  int cnt = 0;
+  if (e_own < E) {
+    cnt = before[e_own] + after[e_own];
 #pragma unroll
-  for (int q = 0; q < EPT; ++q) {
-    int e = tid * EPT + q;
-    int c = 0;
-    if (e < E)
-      for (int w = 0; w < NW; ++w) c += cur[w * E + e];
-    cnt[q] = c;
-    pc[q] = ((c + BM - 1) / BM) * BM;
-    local += pc[q];
+    for (int w = 0; w < RW; ++w) cnt += cur[w * E + e_own];
   }
+  const int pc = ((cnt + BM - 1) / BM) * BM;
   int total;
-  int off = block_exclusive_scan<NW>(local, scratch, total);
+  const int off = block_exclusive_scan<NW>(pc, scratch, total);
+  if (e_own < E) {
+    int c0 = off + before[e_own];
 #pragma unroll
-  for (int q = 0; q < EPT; ++q) {
-    int e = tid * EPT + q;
-    if (e < E) {
-      offsets[e] = off;
-      int base = off;
-      for (int w = 0; w < NW; ++w) {
-        const int c = cur[w * E + e];
-        cur[w * E + e] = base;  // only this thread touches expert e
-        base += c;
-      }
-      for (int r = off + cnt[q]; r < off + pc[q]; ++r) sorted_ids[r] = P;
-      for (int b = off / BM; b < (off + pc[q]) / BM; ++b) block_expert[b] = e;
+    for (int w = 0; w < RW; ++w) {
+      const int c = cur[w * E + e_own];
+      cur[w * E + e_own] = c0;  // only this thread touches expert e_own
+      c0 += c;
     }
-    off += pc[q];
+    before[e_own] = cnt;
+    after[e_own] = off;
+    if (blockIdx.x == 0) offsets[e_own] = off;
   }
-  if (tid == 0) {
+  if (blockIdx.x == 0 && tid == 0) {
     offsets[E] = total;
     *npp = total;
   }
-  for (int r = total + tid; r < nb * BM; r += NT) sorted_ids[r] = P;
-  for (int b = total / BM + tid; b < nb; b += NT) block_expert[b] = -1;
   __syncthreads();
 
+  // padding sentinels and block experts, one expert per wave of the grid
+  const int gw = blockIdx.x * NW + wave, n_waves = gridDim.x * NW;
+  for (int e = gw; e < E; e += n_waves) {
+    const int c = before[e], o = after[e], p = ((c + BM - 1) / BM) * BM;
+    for (int r = o + c + lane; r < o + p; r += 64) sorted_ids[r] = P;
+    for (int b = o / BM + lane; b < (o + p) / BM; b += 64) block_expert[b] = e;
+  }
+  const int gt = blockIdx.x * NT + tid, n_threads = gridDim.x * NT;
+  for (int r = total + gt; r < nb * BM; r += n_threads) sorted_ids[r] = P;
+  for (int b = total / BM + gt; b < nb; b += n_threads) block_expert[b] = -1;
+
+  if (wave >= RW) return;  // no workgroup barrier below
+  int32_t* wcur = cur + wave * E;
+  uint32_t* wmask = mask + wave * E * 2;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   if (!any_dup) {
-    const int rounds = (Tw + 63) / 64;
-    for (int r = 0; r < rounds; ++r) {
-      const int t = t_begin + r * 64 + lane;
-      const bool live = t < t_end;
+    for (int t0 = w_begin; t0 < w_end; t0 += 64) {
+      const int t = t0 + lane;
+      const bool live = t < w_end;
       int ex[kMaxTopK];
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j) {
@@ -250,34 +293,33 @@ __global__ __launch_bounds__(64 * NW) void permute_align_kernel(const int32_t* _
       }
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j)
-        if (ex[j] >= 0) atomicOr(&mask[(wave * E + ex[j]) * 2 + (lane >> 5)], 1u << (lane & 31));
-      __syncthreads();
+        if (ex[j] >= 0) atomicOr(&wmask[ex[j] * 2 + (lane >> 5)], 1u << (lane & 31));
+      wave_lds_sync();
       uint64_t m[kMaxTopK];
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j) {
         m[j] = 0;
         if (ex[j] >= 0) {
-          const uint2 mm = *(const uint2*)&mask[(wave * E + ex[j]) * 2];
+          const uint2 mm = *(const uint2*)&wmask[ex[j] * 2];
           m[j] = (uint64_t)mm.x | ((uint64_t)mm.y << 32);
-          sorted_ids[cur[wave * E + ex[j]] + __popcll(m[j] & lt_mask)] = t * k + j;
+          sorted_ids[wcur[ex[j]] + __popcll(m[j] & lt_mask)] = t * k + j;
         }
       }
-      __syncthreads();
+      wave_lds_sync();
 #pragma unroll
       for (int j = 0; j < kMaxTopK; ++j) {
         if (ex[j] >= 0 && (m[j] & lt_mask) == 0) {  // the expert's first lane
-          cur[wave * E + ex[j]] += __popcll(m[j]);
-          *(uint2*)&mask[(wave * E + ex[j]) * 2] = make_uint2(0u, 0u);
+          wcur[ex[j]] += __popcll(m[j]);
+          *(uint2*)&wmask[ex[j] * 2] = make_uint2(0u, 0u);
         }
       }
-      __syncthreads();
+      wave_lds_sync();
     }
   } else {
     // general order: lane = pair, in f order over the wave's token range
-    const int f_begin = t_begin * k, f_end = t_end * k;
-    const int frounds = (Tw * k + 63) / 64;
-    for (int r = 0; r < frounds; ++r) {
-      const int f = f_begin + r * 64 + lane;
+    const int f_begin = w_begin * k, f_end = w_end * k;
+    for (int f0 = f_begin; f0 < f_end; f0 += 64) {
+      const int f = f0 + lane;
       const int e = (f < f_end) ? ids[f] : -1;
       const bool valid = e >= 0 && e < E;
       uint64_t active = __ballot(valid);
@@ -295,28 +337,24 @@ __global__ __launch_bounds__(64 * NW) void permute_align_kernel(const int32_t* _
         }
         active &= ~mm;
       }
-      if (valid) sorted_ids[cur[wave * E + e] + rank] = f;
-      __syncthreads();
-      if (leader) cur[wave * E + e] += cnt_leader;
-      __syncthreads();
+      if (valid) sorted_ids[wcur[e] + rank] = f;
+      wave_lds_sync();
+      if (leader) wcur[e] += cnt_leader;
+      wave_lds_sync();
     }
   }
 }
 
 hipError_t launch_permute_align(const int32_t* ids, int T, int k, int E, int block_m, int nb, int32_t* sorted_ids,
                                 int32_t* block_expert, int32_t* offsets, int32_t* npp, hipStream_t s) {
-  // 16 waves when their per-wave tables fit in 64 KB of LDS and there are
-  // enough tokens to share out, else 4 waves.
-  const bool wide = T >= 1024 && (size_t)16 * E * 12 + 17 * 4 <= 65536;
-  if (wide) {
-    size_t smem = (size_t)16 * E * 12 + 17 * 4;
-    hipLaunchKernelGGL(permute_align_kernel<16>, dim3(1), dim3(1024), smem, s, ids, T, k, E, block_m, nb,
-                       sorted_ids, block_expert, offsets, npp);
-  } else {
-    size_t smem = (size_t)4 * E * 12 + 5 * 4;
-    hipLaunchKernelGGL(permute_align_kernel<4>, dim3(1), dim3(256), smem, s, ids, T, k, E, block_m, nb, sorted_ids,
-                       block_expert, offsets, npp);
-  }
+  constexpr int NW = kPermWaves, RW = kPermRankWaves;
+  // one chunk per 64 tokens of each ranking wave, at most kPermMaxChunks
+  int chunks = (T + RW * 64 - 1) / (RW * 64);
+  chunks = chunks < 1 ? 1 : (chunks > kPermMaxChunks ? kPermMaxChunks : chunks);
+  const int Tc = (T + chunks - 1) / chunks;
+  const size_t smem = (size_t)(2 + 3 * RW) * E * 4 + (NW + 1) * 4;  // <= 57412 B for E <= 1024
+  hipLaunchKernelGGL((permute_align_kernel<NW, RW>), dim3(chunks), dim3(64 * NW), smem, s, ids, T, k, E, block_m, nb,
+                     Tc, sorted_ids, block_expert, offsets, npp);
   return hipGetLastError();
 }
 

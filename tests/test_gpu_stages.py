@@ -104,15 +104,22 @@ def test_route_topk(T, E, k):
                                            (300, 8, 2, 32, False), (0, 8, 2, 16, False),
                                            (1000, 1024, 16, 16, False), (17, 1, 1, 128, False),
                                            (513, 16, 4, 16, True), (200, 8, 4, 16, "dup"),
-                                           (3000, 64, 8, 32, "dup"), (100, 16, 3, 64, "bad")])
+                                           (3000, 64, 8, 32, "dup"), (100, 16, 3, 64, "bad"),
+                                           (2000, 288, 8, 128, "dup1"), (70000, 288, 8, 128, False),
+                                           (70001, 64, 2, 16, True)])
 def test_permute_align_bitexact(T, E, k, BM, skew):
     """Includes tokens that list an expert twice ("dup": the pairs keep f
-    order) and ids outside [0, E) ("bad": skipped by both sides)."""
+    order; "dup1": only a few tokens in one token chunk do), ids outside
+    [0, E) ("bad": skipped by both sides), and token counts that split into
+    the maximum number of chunks with several 64-token rounds per wave."""
     log(f"permute_align T={T} E={E} k={k} BM={BM} skew={skew}")
     rng = np.random.default_rng(T + 7 * E + BM)
     if skew == "dup":
         ids = rng.integers(0, E, (T, k)).astype(np.int32)
         ids[::3, 1] = ids[::3, 0]
+    elif skew == "dup1":
+        ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+        ids[600:605, 3] = ids[600:605, 5]
     elif skew == "bad":
         ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
         ids[::5, 0] = -1
