@@ -83,7 +83,8 @@ struct Ring {
   static constexpr int T_OFF = 16 * TILE;                        // TT token tiles
   static constexpr int TS_OFF = T_OFF + TT * TILE;               // token scales, 256 B per 64 tokens
   static constexpr int NTS = BM >= 64 ? BM / 64 : 1;
-  static constexpr int SLOT = TS_OFF + NTS * 256;
+  static constexpr int WSC_OFF = TS_OFF + NTS * 256;            // FP8: the K block's two weight scales
+  static constexpr int SLOT = WSC_OFF + 16;
   static constexpr int WS_BYTES = 16 * 256;                      // MX: one group of weight scale dwords
   static constexpr int DW = 16 * HALVES / NWAVE;                 // weight loads per wave per slot
   static constexpr int NTD = TT * HALVES;                        // token loads per slot
@@ -125,10 +126,6 @@ __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-// Uniform fp32 load through the scalar data cache (read only).
-__device__ __forceinline__ float uniform_load(const float* p) {
-  return *(const __attribute__((address_space(4))) float*)p;
-}
 
 // Per-lane source addresses of one wave's loads at K block 0.
 template <int MODE, int BM>
@@ -138,6 +135,7 @@ struct RingSrc {
   const uint8_t* t[R::DT];
   const uint8_t* ts;
   const uint8_t* ws[R::DWS > 0 ? R::DWS : 1];
+  const uint8_t* wsc;  // FP8, lanes 0 and 1 of the last wave: weight-scale row of K block 0
 };
 
 // Weight tile t16 of local tile i (0..15) of N tile nt.
@@ -154,8 +152,9 @@ __device__ __forceinline__ int ring_tile(const GemmArgs& p, int nt, int i) {
 // Loads of K block kb into `slot`.  Token scales: each wave fetches 16 of the
 // 64 scales of its token half (lanes 0..15 only), placed so that lane l of a
 // compute wave finds the scales of token tiles m = 0..3, row l % 16, in one
-// 16-byte word.  MX weight scales (one dword holds 4 K blocks) are fetched
-// only when `ws` is non-null, into that buffer.
+// 16-byte word.  FP8 weight scales: the last wave fetches the K block's two
+// fp32 block scales (lanes 0 and 1).  MX weight scales (one dword holds 4 K
+// blocks) are fetched only when `ws` is non-null, into that buffer.
 template <int MODE, int BM>
 __device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const uint8_t* slot, int wave, int kb,
                                            const uint8_t* ws) {
@@ -169,6 +168,9 @@ __device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const u
   for (int q = 0; q < R::DT; ++q)
     if (wave * R::DT + q < R::NTD) dma16<false>(src.t[q] + kb * R::AROW, base + R::T_OFF + (wave * R::DT + q) * 1024);
   if (lane < 16) dma4(src.ts + kb * 4, base + R::TS_OFF + (wave >> 2) * 256 + (wave & 3) * 64);
+  if constexpr (MODE != kQuantMx) {
+    if (wave == R::NWAVE - 1 && lane < 2) dma4(src.wsc + kb * 4, base + R::WSC_OFF);
+  }
   if constexpr (R::DWS > 0) {
     if (ws != nullptr) {
       const uint32_t wbase = __builtin_amdgcn_readfirstlane(lds_addr(ws));
@@ -349,15 +351,15 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
 // list of (M block, N tile) items, and its load ring runs on across item
 // boundaries: the first K blocks of the next item are in
 // flight while the current item finishes and writes its epilogue, so the
-// ring never drains.  Item metadata (sorted pair ids, and for GEMM2 the
-// routing weights of those pairs) also arrives by direct-to-LDS loads, one
-// item ahead, so no load the compiler would wait on sits in the stream.
+// ring never drains.  Item metadata (sorted pair ids, the block's expert,
+// and for GEMM2 the routing weights of those pairs) also arrives by
+// direct-to-LDS loads, one item ahead, and the FP8 weight scales ride with
+// their K block, so neither a load the compiler would wait on nor a scalar
+// load (whose cache misses would stall the whole workgroup) sits in the
+// stream.
 // ===========================================================================
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-__device__ __forceinline__ int uniform_load_i32(const int32_t* p) {
-  return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
 // GEMM1 epilogue: lane l holds, for token t = wt*64 + m*16 + l%16, the
@@ -476,6 +478,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   __shared__ __attribute__((aligned(1024))) uint8_t slot3[S > 3 ? R::SLOT : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t slot4[S > 4 ? R::SLOT : 16];
   __shared__ __attribute__((aligned(256))) int32_t ids_lds[NB][BM];
+  __shared__ int32_t exp_lds[NB];
   __shared__ __attribute__((aligned(256))) float wts_lds[G1 ? 1 : NB][BM];
   __shared__ float red[4][BM];
   __shared__ __attribute__((aligned(256))) uint8_t ws_buf[MODE == kQuantMx ? NWS : 1][MODE == kQuantMx ? R::WS_BYTES : 16];
@@ -509,10 +512,12 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   auto item_m = [&](int ii) { return (first + ii * nw) / p.n_tiles; };
   auto item_nt = [&](int ii) { return (first + ii * nw) % p.n_tiles; };
 
-  // sorted pair ids of item ii -> ids_lds[ii % NB] (waves 0 .. NI-1)
+  // sorted pair ids of item ii -> ids_lds[ii % NB] (waves 0 .. NI-1), its
+  // block's expert -> exp_lds[ii % NB] (lane 0 of the last wave)
   auto issue_ids = [&](int ii) {
     if (wave < NI && id_lane)
       dma4(p.sorted_ids + item_m(ii) * BM + wave * 64 + lane, lds_addr(&ids_lds[ii % NB][wave * 64]));
+    if (wave == R::NWAVE - 1 && lane == 0) dma4(p.block_expert + item_m(ii), lds_addr(&exp_lds[ii % NB]));
   };
   // GEMM2: routing weight of each row of item ii (its ids must be visible)
   auto issue_wts = [&](int ii) {
@@ -530,7 +535,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   int wts_step = -1, wts_item = 0;
   auto setup_issue = [&](int ii, int s) {
     const int m = item_m(ii), nt = item_nt(ii);
-    const int e = uniform_load_i32(p.block_expert + m);
+    const int e = __builtin_amdgcn_readfirstlane(exp_lds[ii % NB]);
 #pragma unroll
     for (int q = 0; q < R::DW; ++q) {
       const int g = wave * R::DW + q, tile = g / R::HALVES, h = g % R::HALVES;
@@ -554,6 +559,13 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
     {
       const int64_t row = row_of(ring_scale_row(wave, lane));
       rs.ts = (MODE == kQuantMx) ? (const uint8_t*)p.As + row * p.ldas : (const uint8_t*)p.As + row * p.ldas * 4;
+    }
+    if constexpr (MODE != kQuantMx) {
+      // GEMM1: the gate and the up 128-row block of the N tile; GEMM2: the
+      // N tile's two 128-row blocks (the second clamped to the last block)
+      const int NB128 = p.N / 128;
+      const int b0 = G1 ? nt : nt * 2, b1 = G1 ? p.Ip / 128 + nt : min(nt * 2 + 1, NB128 - 1);
+      rs.wsc = (const uint8_t*)((const float*)p.Bs + ((int64_t)e * NB128 + ((lane & 1) ? b1 : b0)) * KB);
     }
     if constexpr (R::DWS > 0) {
       const int KBq = (KB + 3) / 4;
@@ -590,24 +602,10 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   }
   int c_nt = 0, c_row0 = 0;
   bool active = true;
-  const float* wsr0 = nullptr;
-  const float* wsr1 = nullptr;
   auto setup_compute = [&](int ii) {
-    const int m = item_m(ii);
     c_nt = item_nt(ii);
-    c_row0 = m * BM;
+    c_row0 = item_m(ii) * BM;
     if constexpr (!G1) active = c_nt * 256 + 64 * wn < p.N;
-    if constexpr (MODE != kQuantMx) {
-      const int e = uniform_load_i32(p.block_expert + m);
-      const int NB128 = p.N / 128;
-      if constexpr (G1) {
-        wsr0 = (const float*)p.Bs + ((int64_t)e * NB128 + c_nt) * KB;
-        wsr1 = (const float*)p.Bs + ((int64_t)e * NB128 + p.Ip / 128 + c_nt) * KB;
-      } else {
-        wsr0 = (const float*)p.Bs + ((int64_t)e * NB128 + min(c_nt * 2 + (wn >> 1), NB128 - 1)) * KB;
-        wsr1 = wsr0;
-      }
-    }
   };
 
   v4f acc[MT][4];
@@ -653,12 +651,14 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   const uint8_t* c_ws = ws_buf[0];
   auto step = [&](auto dc, int s) {
     constexpr int d = decltype(dc)::value;
+    vm_wait_barrier<(S - 2) * R::D>();
     float sw0 = 0.0f, sw1 = 0.0f;
     if constexpr (MODE != kQuantMx) {
-      sw0 = uniform_load(wsr0 + c_kb);
-      sw1 = G1 ? uniform_load(wsr1 + c_kb) : sw0;
+      // GEMM1: gate and up scale; GEMM2: the scale of the wave's 128-row block
+      const float2 sc = *(const float2*)(slot(std::integral_constant<int, d>{}) + R::WSC_OFF);
+      sw0 = (G1 || (wn >> 1) == 0) ? sc.x : sc.y;
+      sw1 = sc.y;
     }
-    vm_wait_barrier<(S - 2) * R::D>();
     if (s == wts_step) issue_wts(wts_item);
     issue_next(std::integral_constant<int, (d + S - 1) % S>{}, s);
     if constexpr (MODE == kQuantMx) {
