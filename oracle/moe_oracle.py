@@ -12,6 +12,9 @@ Sources (page title and section):
        activations; OCP MXFP4 1x32; separate contiguous gate/up halves; clamped
        SwiGLU with swiglu_limit=10.0) and the contract table (padding metadata
        recorded and forwarded).
+  [P4] "[AMD] [GLM5] Opt-in prefill-only FP8 dense projection GEMM for MLA
+       q_b/o_proj (gfx950)" -- Modifications (e4m3 weights with a 128x128
+       UE8M0, i.e. power-of-two, block scale).
   [P3] FreeToken PR #270 "glm5_next: support GLM-5.3-Flash (hybrid KDA + DSA,
        mHC, NVFP4 expert offload)" -- Summary (288-expert top-8 routing; the
        clamped SwiGLU silu(min(gate, lim)) * clamp(up, -lim, lim), where an
@@ -26,7 +29,8 @@ GEMMs; every such step here is done in float32 with NumPy's IEEE operations
 rounded once to float32.
 
 Parity status per function (what pins it is in the tests):
-  route_topk, permute_align, e4m3/e2m1 code tables, quant_fp8_*, quant_mxfp4_*,
+  route_topk, permute_align, e4m3/e2m1 code tables, quant_fp8_*, quant_fp8e8_*
+  (UE8M0 scales), quant_mxfp4_*,
   gemm (dequantised fp32), swiglu_clamped, moe_forward: pinned by brute force,
   library casts, closed forms and invariants.  No function is "parity unpinned".
 """
@@ -211,6 +215,95 @@ def dequant_fp8_weight(q: np.ndarray, s: np.ndarray, block: int = 128) -> np.nda
 
 
 # ----------------------------------------------------------------------------
+# Block FP8 with UE8M0 scales: e4m3 codes, one power-of-two scale per group,
+# stored as an unsigned E8M0 exponent byte.  [P4] "[AMD] [GLM5] Opt-in
+# prefill-only FP8 dense projection GEMM for MLA q_b/o_proj (gfx950)",
+# Modifications: e4m3 weights with a 128x128 UE8M0 scale.
+# ----------------------------------------------------------------------------
+
+def ue8m0_exponent(amax):
+    """Smallest integer e with 448 * 2**e >= amax, for finite amax > 0.
+
+    Reading: the block scale amax/448 is rounded UP to a power of two, so
+    that no value of the group needs saturation (|v| / 2**e <= 448).  Exact:
+    start one below floor(log2 amax) - 8 and step up while 448 * 2**e is still
+    below amax (both sides are exact in float64).  Works elementwise."""
+    amax = np.asarray(amax, dtype=np.float64)
+    e = floor_log2(amax) - 9
+    for _ in range(3):  # 448 * 2**(E - 9) < 2**E <= amax, and 448 * 2**(E - 7) > 2**(E + 1) > amax
+        e = np.where(np.ldexp(E4M3_MAX, e) < amax, e + 1, e)
+    return e
+
+
+def ue8m0_scale_byte(amax):
+    """E8M0 byte of a UE8M0 block: ue8m0_exponent(amax) + 127 clamped to
+    [0, 254].  Reading for amax == 0 (zero rows, all-pad blocks): byte 0 with
+    all-zero codes, as for the MX scales."""
+    amax = np.asarray(amax, dtype=np.float64)
+    b = np.clip(ue8m0_exponent(np.where(amax > 0, amax, 1.0)) + 127, 0, 254)
+    return np.where(amax > 0, b, 0).astype(np.uint8)
+
+
+def _fp8_ue8m0_groups(g: np.ndarray):
+    """Groups along the last axis of float32 ``g`` -> (codes uint8 [..., G],
+    scale bytes uint8 [...]).  q = RNE_e4m3(v / 2**(b - 127)); the division by
+    a power of two is exact (done in float64), and |v| / 2**(b-127) <= 448 by
+    the choice of b, so no value saturates."""
+    g = np.asarray(g, dtype=F32).astype(np.float64)
+    amax = np.max(np.abs(g), axis=-1)
+    b = ue8m0_scale_byte(amax)
+    r = g / np.ldexp(1.0, b.astype(np.int64) - 127)[..., None]
+    q = round_to_e4m3(np.clip(r, -E4M3_MAX, E4M3_MAX))
+    q = np.where((amax > 0)[..., None], q, np.uint8(0)).astype(np.uint8)
+    return q, b
+
+
+def quant_fp8e8_rows(v: np.ndarray, group: int = 128):
+    """Per-row activation quantisation with UE8M0 scales: one e4m3 code per
+    element and one E8M0 byte per 1 x ``group`` run along the last axis.
+    Returns (q uint8 [rows, K], b uint8 [rows, K/group])."""
+    v = np.asarray(v, dtype=F32)
+    rows, K = v.shape
+    assert K % group == 0
+    q = np.zeros((rows, K), np.uint8)
+    b = np.zeros((rows, K // group), np.uint8)
+    for r0, r1 in _row_chunks(rows, K):
+        qq, bb = _fp8_ue8m0_groups(v[r0:r1].reshape(r1 - r0, K // group, group))
+        q[r0:r1] = qq.reshape(r1 - r0, K)
+        b[r0:r1] = bb
+    return q, b
+
+
+def quant_fp8e8_weight(w: np.ndarray, block: int = 128):
+    """Weights [N, K] -> (q uint8 [N, K], b uint8 [N/block, K/block]): one
+    UE8M0 scale per [128, 128] block."""
+    w = np.asarray(w, dtype=F32)
+    N, K = w.shape
+    assert N % block == 0 and K % block == 0
+    q = np.zeros((N, K), np.uint8)
+    b = np.zeros((N // block, K // block), np.uint8)
+    for i in range(N // block):
+        band = w[i * block:(i + 1) * block].reshape(block, K // block, block).transpose(1, 0, 2)
+        qq, b[i] = _fp8_ue8m0_groups(band.reshape(K // block, block * block))
+        q[i * block:(i + 1) * block] = qq.reshape(K // block, block, block).transpose(1, 0, 2).reshape(block, K)
+    return q, b
+
+
+def e8m0_to_f32(b: np.ndarray) -> np.ndarray:
+    """2**(b - 127) as float32 (exact: 2**-127 is an fp32 subnormal)."""
+    return np.ldexp(1.0, np.asarray(b, np.int64) - 127).astype(F32)
+
+
+def dequant_fp8e8_rows(q: np.ndarray, b: np.ndarray, group: int = 128) -> np.ndarray:
+    """fp32 value of each element: code value * 2**(b - 127) (exact)."""
+    return dequant_fp8_rows(q, e8m0_to_f32(b), group)
+
+
+def dequant_fp8e8_weight(q: np.ndarray, b: np.ndarray, block: int = 128) -> np.ndarray:
+    return dequant_fp8_weight(q, e8m0_to_f32(b), block)
+
+
+# ----------------------------------------------------------------------------
 # OCP MXFP4: E2M1 codes, two per byte, one E8M0 scale per 1 x 32 along K  [P1]
 # ----------------------------------------------------------------------------
 
@@ -387,6 +480,8 @@ class QuantWeights:
 
     mode "fp8":  w13 uint8 [E, 2Ip, Hp], s13 float32 [E, 2Ip/128, Hp/128];
                  w2  uint8 [E, Hp, Ip],  s2  float32 [E, Hp/128, Ip/128].
+    mode "fp8_ue8m0": as "fp8" with uint8 E8M0 scale bytes in place of the
+                 float32 scales.
     mode "mxfp4": w13 uint8 [E, 2Ip, Hp/2], s13 uint8 [E, 2Ip, Hp/32];
                   w2  uint8 [E, Hp, Ip/2],  s2  uint8 [E, Hp, Ip/32].
     Gate rows are [0, Ip) and up rows [Ip, 2Ip) of w13 (separate contiguous
@@ -407,6 +502,12 @@ def quantize_weights(mode: str, w13: np.ndarray, w2: np.ndarray) -> QuantWeights
             a, b = quant_fp8_weight(w13[e]); q13.append(a); s13.append(b)
             a, b = quant_fp8_weight(w2[e]); q2.append(a); s2.append(b)
         return QuantWeights(mode, np.stack(q13), np.stack(s13), np.stack(q2), np.stack(s2))
+    if mode == "fp8_ue8m0":
+        q13, s13, q2, s2 = [], [], [], []
+        for e in range(E):
+            a, b = quant_fp8e8_weight(w13[e]); q13.append(a); s13.append(b)
+            a, b = quant_fp8e8_weight(w2[e]); q2.append(a); s2.append(b)
+        return QuantWeights(mode, np.stack(q13), np.stack(s13), np.stack(q2), np.stack(s2))
     if mode == "mxfp4":
         q13, s13, q2, s2 = [], [], [], []
         for e in range(E):
@@ -420,16 +521,31 @@ def dequant_expert(W: QuantWeights, e: int):
     """fp32 w13[e] [2Ip, Hp] and w2[e] [Hp, Ip]."""
     if W.mode == "fp8":
         return dequant_fp8_weight(W.w13[e], W.s13[e]), dequant_fp8_weight(W.w2[e], W.s2[e])
+    if W.mode == "fp8_ue8m0":
+        return dequant_fp8e8_weight(W.w13[e], W.s13[e]), dequant_fp8e8_weight(W.w2[e], W.s2[e])
     return dequant_mxfp4_rows(W.w13[e], W.s13[e]), dequant_mxfp4_rows(W.w2[e], W.s2[e])
 
 
 def quant_act(mode: str, v: np.ndarray):
-    """Dynamic activation quantisation of float32 rows: FP8 1x128 or MXFP4 1x32."""
-    return quant_fp8_rows(v, 128) if mode == "fp8" else quant_mxfp4_rows(v)
+    """Dynamic activation quantisation of float32 rows: FP8 1x128 (fp32 or
+    UE8M0 scales) or MXFP4 1x32."""
+    if mode == "fp8":
+        return quant_fp8_rows(v, 128)
+    if mode == "fp8_ue8m0":
+        return quant_fp8e8_rows(v, 128)
+    if mode == "mxfp4":
+        return quant_mxfp4_rows(v)
+    raise ValueError(mode)
 
 
 def dequant_act(mode: str, q: np.ndarray, s: np.ndarray) -> np.ndarray:
-    return dequant_fp8_rows(q, s, 128) if mode == "fp8" else dequant_mxfp4_rows(q, s)
+    if mode == "fp8":
+        return dequant_fp8_rows(q, s, 128)
+    if mode == "fp8_ue8m0":
+        return dequant_fp8e8_rows(q, s, 128)
+    if mode == "mxfp4":
+        return dequant_mxfp4_rows(q, s)
+    raise ValueError(mode)
 
 
 def pad_cols(v: np.ndarray, cols: int) -> np.ndarray:

@@ -245,3 +245,123 @@ def test_mxfp4_error_bound():
     d = O.dequant_mxfp4_rows(p, b)
     unit = np.repeat(np.exp2(b.astype(np.float64) - 127), 32, axis=1)
     assert np.all(np.abs(d - v) <= 2 * unit)
+
+
+# ------------------------------------------------------ FP8 with UE8M0 -----
+# "[AMD] [GLM5] Opt-in prefill-only FP8 dense projection GEMM for MLA
+# q_b/o_proj (gfx950)", Modifications: e4m3 with a 128x128 UE8M0 scale.  The
+# reading pinned here: the scale is 2^e with e the smallest integer such
+# that 448 * 2^e >= amax, stored as the E8M0 byte e + 127.
+
+def _ue8m0_exponent_exact(amax: float) -> int:
+    """Smallest e with 448 * 2^e >= amax, by exact rational comparison."""
+    from fractions import Fraction
+    a = Fraction(float(amax))
+    e = 0
+    while Fraction(448) * Fraction(2) ** e < a:
+        e += 1
+    while Fraction(448) * Fraction(2) ** (e - 1) >= a:
+        e -= 1
+    return e
+
+
+def _ue8m0_amax_cases():
+    rng = np.random.default_rng(30)
+    vals = []
+    for e in range(-149, 128):
+        for m in (1.0, 1.5, 1.75, 1.7500001, 1.7499999, 1.9999999, 1.0000001):
+            x = np.float32(np.ldexp(m, e))
+            if x > 0 and np.isfinite(x):
+                vals.append(x)
+    for k in range(-140, 119):  # exactly 448 * 2^k and its fp32 neighbours
+        x = np.float32(np.ldexp(448.0, k))
+        if x > 0 and np.isfinite(x):
+            vals += [x, np.nextafter(x, np.float32(np.inf)), np.nextafter(x, np.float32(0))]
+    vals += list(np.exp2(rng.uniform(-140, 127, 2000)).astype(np.float32))
+    return [v for v in vals if v > 0 and np.isfinite(v)]
+
+
+def test_ue8m0_exponent_is_minimal_by_exact_comparison():
+    cases = _ue8m0_amax_cases()
+    got = O.ue8m0_exponent(np.array(cases, np.float32))
+    for a, e in zip(cases, got):
+        assert int(e) == _ue8m0_exponent_exact(a), a
+
+
+def test_ue8m0_byte_examples_and_clamp():
+    # amax 448 -> 2^0 (byte 127); just above 448 -> 2^1; 224 -> 2^-1; 1.0 -> 2^-8
+    assert int(O.ue8m0_scale_byte(448.0)) == 127
+    assert int(O.ue8m0_scale_byte(np.nextafter(np.float32(448), np.float32(1e9)))) == 128
+    assert int(O.ue8m0_scale_byte(224.0)) == 126
+    assert int(O.ue8m0_scale_byte(1.0)) == 127 - 8
+    assert int(O.ue8m0_scale_byte(1.75)) == 127 - 8     # 448 * 2^-8 = 1.75 exactly
+    assert int(O.ue8m0_scale_byte(1.76)) == 127 - 7
+    # tiny amax: the exponent is below -127 and the byte clamps to 0 (2^-127)
+    assert int(O.ue8m0_scale_byte(np.float32(1e-40))) == 0
+    assert int(O.ue8m0_scale_byte(0.0)) == 0
+
+
+def test_fp8e8_group_quantiser_invariants():
+    rng = np.random.default_rng(31)
+    v = (rng.standard_normal((64, 512)) * np.exp2(rng.integers(-30, 30, (64, 1)))).astype(np.float32)
+    v[3, 128:256] = 0.0
+    v[5, :128] = -0.0
+    v[7, 0] = -0.0
+    v[9] *= np.float32(1e-38)   # subnormal amax
+    q, b = O.quant_fp8e8_rows(v, 128)
+    assert q.shape == (64, 512) and b.shape == (64, 4) and b.dtype == np.uint8
+    assert b[3, 1] == 0 and np.all(q[3, 128:256] == 0)
+    assert b[5, 0] == 0 and np.all(q[5, :128] == 0)
+    assert q[7, 0] == 0x80
+    amax = np.abs(v.reshape(64, 4, 128)).max(-1).astype(np.float64)
+    e = b.astype(np.int64) - 127
+    nz = amax > 0
+    # power-of-two scale just large enough: amax in (224 * 2^e, 448 * 2^e]
+    # (unless the byte clamped at 0)
+    hi = np.ldexp(448.0, e)
+    assert np.all(amax[nz] <= hi[nz])
+    unclamped = nz & (b > 0)
+    assert np.all(amax[unclamped] > hi[unclamped] / 2)
+    # the group's largest magnitude code lies in [0x76 (224), 0x7E (448)]
+    qg = (q.reshape(64, 4, 128) & 0x7F).max(-1)
+    assert np.all((qg[unclamped] >= 0x76) & (qg[unclamped] <= 0x7E))
+    # each code is torch's RNE cast of v / 2^e, which is exact in fp32 here
+    r = (v.reshape(64, 4, 128).astype(np.float64) / np.ldexp(1.0, e)[..., None])
+    assert np.all(np.abs(r) <= 448)
+    ref = _torch_e4m3(r.astype(np.float32).reshape(64, 512))
+    mask = np.repeat(nz, 128, axis=1)
+    assert np.array_equal(q[mask], ref[mask])
+
+
+def test_fp8e8_dequant_exact_and_round_trip():
+    rng = np.random.default_rng(32)
+    v = (rng.standard_normal((16, 384)) * np.exp2(rng.integers(-20, 20, (16, 1)))).astype(np.float32)
+    q, b = O.quant_fp8e8_rows(v, 128)
+    d = O.dequant_fp8e8_rows(q, b, 128)
+    tv = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = tv * np.repeat(np.exp2(b.astype(np.float64) - 127), 128, axis=1)
+    assert np.array_equal(d.astype(np.float64), ref)
+    # re-quantising the dequantised values gives back the same bits wherever
+    # the group's largest code is above 224 (a largest code of exactly 224
+    # halves the next scale)
+    q2, b2 = O.quant_fp8e8_rows(d, 128)
+    keep = (q.reshape(16, 3, 128) & 0x7F).max(-1) > 0x76
+    assert np.array_equal(b2[keep], b[keep])
+    assert np.array_equal(q2.reshape(16, 3, 128)[keep], q.reshape(16, 3, 128)[keep])
+    # error bound: half a code step at the top binade, 16 * 2^e
+    assert np.all(np.abs(d - v) <= np.repeat(np.exp2(b.astype(np.float64) - 127), 128, axis=1) * 16)
+
+
+def test_fp8e8_weight_blocks_are_independent_groups():
+    rng = np.random.default_rng(33)
+    w = (rng.standard_normal((256, 384)) * 0.02).astype(np.float32)
+    w[128:, 256:] *= 1000
+    w[:128, 128:256] = 0
+    q, b = O.quant_fp8e8_weight(w)
+    assert b.shape == (2, 3) and b[0, 1] == 0
+    for i in range(2):
+        for j in range(3):
+            blk = w[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128]
+            qb, bb = O.quant_fp8e8_rows(blk.reshape(1, -1), 128 * 128)
+            assert bb[0, 0] == b[i, j]
+            assert np.array_equal(qb.reshape(128, 128), q[i * 128:(i + 1) * 128, j * 128:(j + 1) * 128])

@@ -24,7 +24,7 @@ def _gamma(K):
     return K * u / (1 - K * u)
 
 
-@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
 def test_dequant_gemm_brute_force_4x32x128(mode):
     rng = np.random.default_rng(20)
     a = rng.standard_normal((4, 128)).astype(np.float32)
@@ -38,6 +38,14 @@ def test_dequant_gemm_brute_force_4x32x128(mode):
         # brute force: decode every code by table, scale, multiply in fp64
         A = [[float(np.float32(tab[qa[i, kk]] * sa[i, 0])) for kk in range(128)] for i in range(4)]
         B = [[float(np.float32(tab[qb[j, kk]] * sb[0, 0])) for kk in range(128)] for j in range(32)]
+    elif mode == "fp8_ue8m0":
+        qa, ba = O.quant_fp8e8_rows(a, 128)
+        qb, bb = O.quant_fp8e8_weight(np.pad(b, ((0, 96), (0, 0))))
+        ad = O.dequant_fp8e8_rows(qa, ba)
+        bd = O.dequant_fp8e8_weight(qb, bb)[:32]
+        tab = O.e4m3_value_table()
+        A = [[tab[qa[i, kk]] * 2.0 ** (int(ba[i, 0]) - 127) for kk in range(128)] for i in range(4)]
+        B = [[tab[qb[j, kk]] * 2.0 ** (int(bb[0, 0]) - 127) for kk in range(128)] for j in range(32)]
     else:
         pa, ba = O.quant_mxfp4_rows(a)
         pb, bb = O.quant_mxfp4_rows(b)
@@ -110,7 +118,7 @@ def _close_rows(a, b, rel=1e-5):
     return bool(np.all(np.abs(a - b).max(axis=1) <= rel * rms))
 
 
-@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
 def test_single_expert_top1_equals_dense_ffn(mode):
     wl = TINY.with_(E=1, top_k=1, mode=mode, T=12)
     Q = _quantised(wl)
@@ -127,7 +135,7 @@ def test_single_expert_top1_equals_dense_ffn(mode):
     assert np.array_equal(out, y)
 
 
-@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
 def test_zero_input_gives_zero_output(mode):
     wl = TINY.with_(mode=mode)
     Q = _quantised(wl)
@@ -136,7 +144,7 @@ def test_zero_input_gives_zero_output(mode):
     assert np.all(out == 0)
 
 
-@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
 def test_padding_is_invisible(mode):
     wl = TINY.with_(mode=mode)
     wlp = wl.with_(Hp=wl.H + 128, Ip=wl.I + 128)
@@ -169,7 +177,7 @@ def test_token_subset_equals_full_rows():
     assert _close_rows(full[[3, 0, 11]], sub)
 
 
-@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
 def test_layer_brute_force_tiny(mode):
     """The whole layer written out with Python loops in fp64 from the stage
     definitions (own routing sort, own dot products, own SwiGLU); only the
