@@ -24,7 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
-MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "mxfp4": 10100.0}   # dense, TFLOP/s
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp8_ue8m0": 5000.0, "mxfp4": 10100.0}   # dense, TFLOP/s
 
 
 def parse():
@@ -65,11 +65,12 @@ def algorithmic_bytes(wl, ids, M):
     active = int(np.count_nonzero(counts))
     Hp, Ip = wl.Hp, wl.Ip
     P = wl.T * wl.top_k
-    if wl.mode == "fp8":
-        w13 = 2 * Ip * Hp + (2 * Ip // 128) * (Hp // 128) * 4
-        w2 = Hp * Ip + (Hp // 128) * (Ip // 128) * 4
-        xq = wl.T * (Hp + Hp // 128 * 4)
-        aq = P * (Ip + Ip // 128 * 4)
+    if wl.mode in ("fp8", "fp8_ue8m0"):
+        sb = 4 if wl.mode == "fp8" else 1   # bytes per block scale (UE8M0: one byte in HBM)
+        w13 = 2 * Ip * Hp + (2 * Ip // 128) * (Hp // 128) * sb
+        w2 = Hp * Ip + (Hp // 128) * (Ip // 128) * sb
+        xq = wl.T * (Hp + Hp // 128 * sb)
+        aq = P * (Ip + Ip // 128 * sb)
     else:
         w13 = 2 * Ip * Hp // 2 + 2 * Ip * Hp // 32
         w2 = Hp * Ip // 2 + Hp * Ip // 32
@@ -199,6 +200,9 @@ def main():
         if wl.mode == "fp8":
             xq = torch.empty(wl.T, wl.Hp, dtype=torch.uint8, device=dev)
             xs = torch.empty(wl.T, wl.Hp // 128, dtype=torch.float32, device=dev)
+        elif wl.mode == "fp8_ue8m0":
+            xq = torch.empty(wl.T, wl.Hp, dtype=torch.uint8, device=dev)
+            xs = torch.empty(wl.T, M.e8_scale_ld(wl.Hp), dtype=torch.uint8, device=dev)
         else:
             xq = torch.empty(wl.T, wl.Hp // 2, dtype=torch.uint8, device=dev)
             xs = torch.empty(wl.T, wl.Hp // 32, dtype=torch.uint8, device=dev)
@@ -269,7 +273,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3" if wl.mode == "fp8" else "fp4e2m1",
+        "dtype": "fp4e2m1" if wl.mode == "mxfp4" else "fp8e4m3",
         "data": "synthetic (seeded N(0,1) activations/logits, N(0,0.02) weights, quantised by the library)",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "Hp": wl.Hp, "Ip": wl.Ip, "E": wl.E,
                    "top_k": wl.top_k, "quant": wl.mode, "block_m": bm, "swiglu_limit": wl.swiglu_limit},

@@ -24,6 +24,9 @@
  *     mHC, NVFP4 expert offload)": Summary (288-expert top-8 routing; the
  *     clamped SwiGLU formula, an infinite limit giving plain SwiGLU; backends
  *     that cannot apply the limit are rejected).
+ *   - "[AMD] [GLM5] Opt-in prefill-only FP8 dense projection GEMM for MLA
+ *     q_b/o_proj (gfx950)": Modifications (e4m3 weights with a 128x128 UE8M0,
+ *     i.e. power-of-two, block scale).
  *
  * Conventions for every entry point:
  *   - Every pointer argument is DEVICE memory owned by the caller, except the
@@ -62,10 +65,15 @@ typedef enum {
   MOE_ERR_HIP = 7          /* a kernel launch failed */
 } moe_status_t;
 
-/* Weight/activation contracts (sglang PR #38546, Summary). */
+/* Weight/activation contracts (sglang PR #38546, Summary; UE8M0: "[AMD]
+ * [GLM5] Opt-in prefill-only FP8 dense projection GEMM for MLA q_b/o_proj
+ * (gfx950)", Modifications). */
 enum {
   MOE_QUANT_FP8_BLOCK = 1, /* w: e4m3 + fp32 scale per [128,128] block; act: e4m3 + fp32 per 1x128 */
-  MOE_QUANT_MXFP4 = 2      /* w and act: E2M1 two per byte (low nibble = even index) + E8M0 per 1x32 */
+  MOE_QUANT_MXFP4 = 2,     /* w and act: E2M1 two per byte (low nibble = even index) + E8M0 per 1x32 */
+  MOE_QUANT_FP8_UE8M0 = 3  /* w: e4m3 + UE8M0 byte per [128,128] block; act: e4m3 + UE8M0 byte per 1x128.
+                              UE8M0 scale = 2^e, e the smallest integer with 448 * 2^e >= amax of the
+                              group, stored as the byte clamp(e + 127, 0, 254) (0 when amax = 0) */
 };
 
 /* Physical order of the gate and up projections inside w13.  Only separate
@@ -120,7 +128,8 @@ size_t moe_workspace_bytes(const moe_cfg_t* cfg, int32_t T_max);
 
 /* Sizes in bytes of the intermediate aq / as buffers (rows = max_blocks *
  * block_m; FP8: aq u8 [rows, Ip], as f32 [rows, Ip/128]; MXFP4: aq u8
- * [rows, Ip/2], as u8 [rows, Ip/32]).  Returns MOE_ERR_* on a bad cfg. */
+ * [rows, Ip/2], as u8 [rows, Ip/32]; FP8_UE8M0: aq u8 [rows, Ip], as u8
+ * [rows, round_up(Ip/128, 4)]).  Returns MOE_ERR_* on a bad cfg. */
 moe_status_t moe_intermediate_bytes(const moe_cfg_t* cfg, int32_t T, size_t* aq_bytes,
                                     size_t* as_bytes);
 
@@ -160,6 +169,10 @@ moe_status_t moe_permute_align(const int32_t* ids, int32_t T, int32_t top_k, int
  *   MXFP4: q u8 [rows, cols_padded/2]; scales u8 [rows, cols_padded/32]:
  *          b = clamp(floor(log2 amax) - 2 + 127, 0, 254) (0 when amax = 0),
  *          codes = RNE_E2M1(clamp(v / 2^(b-127), +-6)).
+ *   FP8_UE8M0: q u8 [rows, cols_padded] e4m3; scales u8 [rows, lds] with
+ *          lds = round_up(cols_padded/128, 4) (rows of whole dwords; the
+ *          bytes past cols_padded/128 are written 0): b as in MOE_QUANT_*,
+ *          codes = RNE(v / 2^(b-127)) (exact scaling, no saturation needed).
  * Signs of zero are kept.  Results are bit-exact by definition. */
 moe_status_t moe_quant_act(const void* in, int32_t in_dtype, int32_t rows, int32_t cols,
                            int64_t ld_in, int32_t cols_padded, int32_t quant_mode, void* q,
@@ -170,12 +183,14 @@ moe_status_t moe_quant_act(const void* in, int32_t in_dtype, int32_t rows, int32
  *   FP8:   N % 128 == 0, K % 128 == 0; q u8 [E, N, K]; scales f32
  *          [E, N/128, K/128] (dequant multipliers), one per [128,128] block,
  *          same arithmetic as moe_quant_act with the block as the group.
- *   MXFP4: K % 128 == 0; q u8 [E, N, K/2]; scales u8 [E, N, K/32]. */
+ *   MXFP4: K % 128 == 0; q u8 [E, N, K/2]; scales u8 [E, N, K/32].
+ *   FP8_UE8M0: as FP8 with scales u8 [E, N/128, K/128] (UE8M0 bytes). */
 moe_status_t moe_quant_weights(int32_t quant_mode, const float* w, int32_t E, int32_t N,
                                int32_t K, void* q, void* scales, void* stream);
 
 /* Sizes of the TILED_V1 buffers for w13 (which = 13: N = 2*Ip, K = Hp) or
- * w2 (which = 2: N = Hp, K = Ip). */
+ * w2 (which = 2: N = Hp, K = Ip).  TILED_V1 holds FP8_UE8M0 block scales as
+ * their exact fp32 values 2^(b-127), [E, N/128, K/128]. */
 moe_status_t moe_preshuffled_bytes(const moe_cfg_t* cfg, int32_t which, size_t* w_bytes,
                                    size_t* s_bytes);
 
@@ -195,8 +210,11 @@ moe_status_t moe_preshuffle_weights(const moe_cfg_t* cfg, int32_t which, const v
  *   aq/as row (b*block_m + r) = quantise(a) per 1x128 (FP8) or 1x32 (MXFP4)
  * Pad rows (f = T*k) get all-zero codes and zero scales.
  * xq/xs: moe_quant_act output for x (FP8: u8 [T, Hp] + f32 [T, Hp/128];
- * MXFP4: u8 [T, Hp/2] + u8 [T, Hp/32]).  w13/w13_scale: TILED_V1.
- * aq/as: sizes from moe_intermediate_bytes, indexed by sorted position. */
+ * MXFP4: u8 [T, Hp/2] + u8 [T, Hp/32]; FP8_UE8M0: u8 [T, Hp] + u8
+ * [T, round_up(Hp/128, 4)]).  w13/w13_scale: TILED_V1.
+ * aq/as: sizes from moe_intermediate_bytes, indexed by sorted position, in
+ * the activation format of the mode over Ip columns (FP8_UE8M0: the scale
+ * bytes past Ip/128 in each row are unspecified). */
 moe_status_t moe_grouped_gemm1_swiglu(const moe_cfg_t* cfg, int32_t T, const void* xq,
                                       const void* xs, const int32_t* sorted_ids,
                                       const int32_t* block_expert,

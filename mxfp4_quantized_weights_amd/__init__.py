@@ -22,13 +22,20 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_
                 4: "MOE_ERR_UNSUPPORTED", 5: "MOE_ERR_LAYOUT", 6: "MOE_ERR_WORKSPACE", 7: "MOE_ERR_HIP"}
 MOE_QUANT_FP8_BLOCK = 1
 MOE_QUANT_MXFP4 = 2
+MOE_QUANT_FP8_UE8M0 = 3
 MOE_GATE_SEPARATED = 0
 MOE_GATE_INTERLEAVED = 1
 MOE_LAYOUT_CANONICAL = 0
 MOE_LAYOUT_TILED_V1 = 0x4D310001
 MOE_DTYPE_BF16 = 1
 MOE_DTYPE_F32 = 2
-QUANT_MODES = {"fp8": MOE_QUANT_FP8_BLOCK, "mxfp4": MOE_QUANT_MXFP4}
+QUANT_MODES = {"fp8": MOE_QUANT_FP8_BLOCK, "mxfp4": MOE_QUANT_MXFP4, "fp8_ue8m0": MOE_QUANT_FP8_UE8M0}
+
+
+def e8_scale_ld(cols_padded: int) -> int:
+    """Row stride in bytes of UE8M0 activation scales: one byte per 128
+    columns, rounded up to whole dwords."""
+    return (cols_padded // 128 + 3) // 4 * 4
 
 
 class MoePad(ctypes.Structure):
@@ -44,7 +51,8 @@ class MoeCfg(ctypes.Structure):
 
     @property
     def fp8(self) -> bool:
-        return self.quant_mode == MOE_QUANT_FP8_BLOCK
+        """e4m3 codes, one byte per element (block FP8 with fp32 or UE8M0 scales)."""
+        return self.quant_mode in (MOE_QUANT_FP8_BLOCK, MOE_QUANT_FP8_UE8M0)
 
 
 class MoeError(RuntimeError):
@@ -211,7 +219,9 @@ def moe_permute_align(ids: torch.Tensor, num_experts: int, block_m: int, stream=
 def moe_quant_act(x: torch.Tensor, cols_padded: int, quant: str | int, stream=None):
     """Row quantisation of bf16/f32 [rows, cols] (row stride taken from x).
     -> FP8: (q uint8 [rows, cols_padded], s float32 [rows, cols_padded/128]);
-       MXFP4: (q uint8 [rows, cols_padded/2], s uint8 [rows, cols_padded/32])."""
+       MXFP4: (q uint8 [rows, cols_padded/2], s uint8 [rows, cols_padded/32]);
+       FP8_UE8M0: (q uint8 [rows, cols_padded], s uint8 [rows, e8_scale_ld(cols_padded)]),
+       the scale bytes of group g in s[:, g], zeros past cols_padded/128."""
     qm = QUANT_MODES[quant] if isinstance(quant, str) else int(quant)
     rows, cols = x.shape
     if x.stride(1) != 1:
@@ -222,6 +232,9 @@ def moe_quant_act(x: torch.Tensor, cols_padded: int, quant: str | int, stream=No
     if qm == MOE_QUANT_FP8_BLOCK:
         q = torch.empty(rows, cols_padded, dtype=torch.uint8, device=x.device)
         s = torch.empty(rows, cols_padded // 128, dtype=torch.float32, device=x.device)
+    elif qm == MOE_QUANT_FP8_UE8M0:
+        q = torch.empty(rows, cols_padded, dtype=torch.uint8, device=x.device)
+        s = torch.empty(rows, e8_scale_ld(cols_padded), dtype=torch.uint8, device=x.device)
     else:
         q = torch.empty(rows, cols_padded // 2, dtype=torch.uint8, device=x.device)
         s = torch.empty(rows, cols_padded // 32, dtype=torch.uint8, device=x.device)
@@ -234,9 +247,10 @@ def moe_quant_weights(w: torch.Tensor, quant: str | int, stream=None):
     """Canonical quantisation of float32 [E, N, K] (already padded)."""
     qm = QUANT_MODES[quant] if isinstance(quant, str) else int(quant)
     E, N, K = w.shape
-    if qm == MOE_QUANT_FP8_BLOCK:
+    if qm in (MOE_QUANT_FP8_BLOCK, MOE_QUANT_FP8_UE8M0):
         q = torch.empty(E, N, K, dtype=torch.uint8, device=w.device)
-        s = torch.empty(E, N // 128, K // 128, dtype=torch.float32, device=w.device)
+        s = torch.empty(E, N // 128, K // 128, device=w.device,
+                        dtype=torch.float32 if qm == MOE_QUANT_FP8_BLOCK else torch.uint8)
     else:
         q = torch.empty(E, N, K // 2, dtype=torch.uint8, device=w.device)
         s = torch.empty(E, N, K // 32, dtype=torch.uint8, device=w.device)
@@ -320,12 +334,13 @@ class ExpertWeights:
         self.cfg = cfg
         E, Hp, Ip = cfg.num_experts, cfg.pad.hidden_padded, cfg.pad.inter_padded
         fp8 = cfg.fp8
+        sdt = torch.float32 if cfg.quant_mode == MOE_QUANT_FP8_BLOCK else torch.uint8
         self.device = device
         self.q13 = torch.empty(E, 2 * Ip, Hp if fp8 else Hp // 2, dtype=torch.uint8, device=device)
-        self.s13 = (torch.empty(E, 2 * Ip // 128, Hp // 128, dtype=torch.float32, device=device) if fp8
+        self.s13 = (torch.empty(E, 2 * Ip // 128, Hp // 128, dtype=sdt, device=device) if fp8
                     else torch.empty(E, 2 * Ip, Hp // 32, dtype=torch.uint8, device=device))
         self.q2 = torch.empty(E, Hp, Ip if fp8 else Ip // 2, dtype=torch.uint8, device=device)
-        self.s2 = (torch.empty(E, Hp // 128, Ip // 128, dtype=torch.float32, device=device) if fp8
+        self.s2 = (torch.empty(E, Hp // 128, Ip // 128, dtype=sdt, device=device) if fp8
                    else torch.empty(E, Hp, Ip // 32, dtype=torch.uint8, device=device))
         self.w13 = self.w13_scale = self.w2 = self.w2_scale = None
 
@@ -353,5 +368,5 @@ class ExpertWeights:
 
 
 __all__ = [n for n in dir() if n.startswith(("moe_", "MOE_", "Moe"))] + [
-    "make_cfg", "pick_block_m", "validate_cfg", "max_blocks", "workspace_bytes", "intermediate_bytes",
+    "make_cfg", "pick_block_m", "e8_scale_ld", "QUANT_MODES", "validate_cfg", "max_blocks", "workspace_bytes", "intermediate_bytes",
     "preshuffled_bytes", "ExpertWeights", "EXPORTED_SYMBOLS", "LIB_PATH", "lib"]

@@ -29,11 +29,31 @@ inline hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
 inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+inline bool known_mode(int32_t m) {
+  return m == MOE_QUANT_FP8_BLOCK || m == MOE_QUANT_MXFP4 || m == MOE_QUANT_FP8_UE8M0;
+}
+// e4m3 codes, one byte per element (block FP8 with either scale format)
+inline bool fp8_codes(int32_t m) { return m != MOE_QUANT_MXFP4; }
+
+// Bytes of one row of quantised codes and of its scales for `cols` padded
+// columns: FP8 fp32 per 128, UE8M0 one byte per 128 (rows of whole dwords),
+// MX one byte per 32.
+inline int64_t code_row_bytes(int32_t m, int64_t cols) { return fp8_codes(m) ? cols : cols / 2; }
+inline int64_t scale_row_bytes(int32_t m, int64_t cols) {
+  if (m == MOE_QUANT_FP8_BLOCK) return cols / 128 * 4;
+  if (m == MOE_QUANT_FP8_UE8M0) return moe::e8_scale_ld(cols);
+  return cols / 32;
+}
+// Scale elements per row as the GEMMs index them (floats for FP8, bytes otherwise).
+inline int64_t scale_row_elems(int32_t m, int64_t cols) {
+  return m == MOE_QUANT_FP8_BLOCK ? cols / 128 : scale_row_bytes(m, cols);
+}
+
 moe_status_t check_cfg(const moe_cfg_t* c) {
   if (!c) return MOE_ERR_NULL;
   if (c->num_experts < 1 || c->num_experts > kMaxExperts) return MOE_ERR_SHAPE;
   if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->num_experts) return MOE_ERR_SHAPE;
-  if (c->quant_mode != MOE_QUANT_FP8_BLOCK && c->quant_mode != MOE_QUANT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (!known_mode(c->quant_mode)) return MOE_ERR_UNSUPPORTED;
   if (c->gate_mode != MOE_GATE_SEPARATED) return MOE_ERR_UNSUPPORTED;
   if (c->block_m != 16 && c->block_m != 32 && c->block_m != 64 && c->block_m != 128) return MOE_ERR_UNSUPPORTED;
   if (!(c->swiglu_limit > 0.0f)) return MOE_ERR_UNSUPPORTED;  // rejects NaN, 0, negatives
@@ -70,17 +90,17 @@ Layout layout_for(const moe_cfg_t* c, int32_t T) {
   const int32_t nb = max_blocks(P, c->num_experts, c->block_m);
   const int64_t rows = (int64_t)nb * c->block_m;
   const int64_t Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
-  const bool fp8 = c->quant_mode == MOE_QUANT_FP8_BLOCK;
+  const int32_t m = c->quant_mode;
   L.ids = align_up(P * 4);
   L.wts = align_up(P * 4);
   L.sorted = align_up(rows * 4);
   L.bexp = align_up((size_t)nb * 4);
   L.offs = align_up((size_t)(c->num_experts + 1) * 4);
   L.npp = align_up(4);
-  L.xq = align_up(fp8 ? T * Hp : T * Hp / 2);
-  L.xs = align_up(fp8 ? T * (Hp / 128) * 4 : T * (Hp / 32));
-  L.aq = align_up(fp8 ? rows * Ip : rows * Ip / 2);
-  L.as = align_up(fp8 ? rows * (Ip / 128) * 4 : rows * (Ip / 32));
+  L.xq = align_up(T * code_row_bytes(m, Hp));
+  L.xs = align_up(T * scale_row_bytes(m, Hp));
+  L.aq = align_up(rows * code_row_bytes(m, Ip));
+  L.as = align_up(rows * scale_row_bytes(m, Ip));
   L.y = align_up(P * Hp * 4);
   L.total = L.ids + L.wts + L.sorted + L.bexp + L.offs + L.npp + L.xq + L.xs + L.aq + L.as + L.y;
   return L;
@@ -90,12 +110,12 @@ moe::GemmArgs gemm1_args(const moe_cfg_t* c, int32_t T, const void* xq, const vo
                          const int32_t* bexp, const int32_t* npp, const void* w13, const void* s13, void* aq,
                          void* as) {
   moe::GemmArgs a{};
-  const bool fp8 = c->quant_mode == MOE_QUANT_FP8_BLOCK;
+  const int32_t m = c->quant_mode;
   const int Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
   a.A = (const uint8_t*)xq;
   a.As = xs;
-  a.lda = fp8 ? Hp : Hp / 2;
-  a.ldas = fp8 ? Hp / 128 : Hp / 32;
+  a.lda = code_row_bytes(m, Hp);
+  a.ldas = scale_row_elems(m, Hp);
   a.sorted_ids = sorted;
   a.block_expert = bexp;
   a.npp = npp;
@@ -117,12 +137,12 @@ moe::GemmArgs gemm2_args(const moe_cfg_t* c, int32_t T, const void* aq, const vo
                          const int32_t* bexp, const int32_t* npp, const void* w2, const void* s2, float* y,
                          const float* topk_w) {
   moe::GemmArgs a{};
-  const bool fp8 = c->quant_mode == MOE_QUANT_FP8_BLOCK;
+  const int32_t m = c->quant_mode;
   const int Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
   a.A = (const uint8_t*)aq;
   a.As = as;
-  a.lda = fp8 ? Ip : Ip / 2;
-  a.ldas = fp8 ? Ip / 128 : Ip / 32;
+  a.lda = code_row_bytes(m, Ip);
+  a.ldas = scale_row_elems(m, Ip);
   a.sorted_ids = sorted;
   a.block_expert = bexp;
   a.npp = npp;
@@ -177,9 +197,8 @@ moe_status_t moe_intermediate_bytes(const moe_cfg_t* cfg, int32_t T, size_t* aq_
   if (!aq_bytes || !as_bytes) return MOE_ERR_NULL;
   const int64_t rows = (int64_t)max_blocks((int64_t)T * cfg->top_k, cfg->num_experts, cfg->block_m) * cfg->block_m;
   const int64_t Ip = cfg->pad.inter_padded;
-  const bool fp8 = cfg->quant_mode == MOE_QUANT_FP8_BLOCK;
-  *aq_bytes = (size_t)(fp8 ? rows * Ip : rows * Ip / 2);
-  *as_bytes = (size_t)(fp8 ? rows * (Ip / 128) * 4 : rows * (Ip / 32));
+  *aq_bytes = (size_t)(rows * code_row_bytes(cfg->quant_mode, Ip));
+  *as_bytes = (size_t)(rows * scale_row_bytes(cfg->quant_mode, Ip));
   return MOE_OK;
 }
 
@@ -209,7 +228,7 @@ moe_status_t moe_permute_align(const int32_t* ids, int32_t T, int32_t top_k, int
 moe_status_t moe_quant_act(const void* in, int32_t in_dtype, int32_t rows, int32_t cols, int64_t ld_in,
                            int32_t cols_padded, int32_t quant_mode, void* q, void* scales, void* stream) {
   if (in_dtype != MOE_DTYPE_BF16 && in_dtype != MOE_DTYPE_F32) return MOE_ERR_UNSUPPORTED;
-  if (quant_mode != MOE_QUANT_FP8_BLOCK && quant_mode != MOE_QUANT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (!known_mode(quant_mode)) return MOE_ERR_UNSUPPORTED;
   if (rows < 0 || cols < 1 || cols > cols_padded || ld_in < cols) return MOE_ERR_SHAPE;
   if (cols_padded % 128 != 0) return MOE_ERR_ALIGN;
   if (rows == 0) return MOE_OK;
@@ -220,13 +239,13 @@ moe_status_t moe_quant_act(const void* in, int32_t in_dtype, int32_t rows, int32
 
 moe_status_t moe_quant_weights(int32_t quant_mode, const float* w, int32_t E, int32_t N, int32_t K, void* q,
                                void* scales, void* stream) {
-  if (quant_mode != MOE_QUANT_FP8_BLOCK && quant_mode != MOE_QUANT_MXFP4) return MOE_ERR_UNSUPPORTED;
+  if (!known_mode(quant_mode)) return MOE_ERR_UNSUPPORTED;
   if (E < 1 || N < 1 || K < 1 || N > kMaxDim * 2 || K > kMaxDim) return MOE_ERR_SHAPE;
-  if (quant_mode == MOE_QUANT_FP8_BLOCK ? (N % 128 != 0 || K % 128 != 0) : (K % 32 != 0)) return MOE_ERR_ALIGN;
+  if (fp8_codes(quant_mode) ? (N % 128 != 0 || K % 128 != 0) : (K % 32 != 0)) return MOE_ERR_ALIGN;
   if (!w || !q || !scales) return MOE_ERR_NULL;
   hipStream_t s = as_stream(stream);
-  if (quant_mode == MOE_QUANT_FP8_BLOCK)
-    return hip_status(moe::launch_quant_weight_fp8(w, E, N, K, (uint8_t*)q, (float*)scales, s));
+  if (fp8_codes(quant_mode))
+    return hip_status(moe::launch_quant_weight_fp8(quant_mode, w, E, N, K, (uint8_t*)q, scales, s));
   // MXFP4 groups run along K: the same row quantiser as the activations
   if (K % 128 != 0) return MOE_ERR_ALIGN;
   return hip_status(moe::launch_quant_rows(w, false, (int64_t)E * N, K, K, K, moe::kQuantMx, q, scales, s));
@@ -239,7 +258,7 @@ moe_status_t moe_preshuffled_bytes(const moe_cfg_t* cfg, int32_t which, size_t* 
   if (!w_bytes || !s_bytes) return MOE_ERR_NULL;
   const int64_t E = cfg->num_experts, Hp = cfg->pad.hidden_padded, Ip = cfg->pad.inter_padded;
   const int64_t N = which == 13 ? 2 * Ip : Hp, K = which == 13 ? Hp : Ip;
-  if (cfg->quant_mode == MOE_QUANT_FP8_BLOCK) {
+  if (fp8_codes(cfg->quant_mode)) {  // UE8M0 scales are widened to fp32
     *w_bytes = (size_t)(E * N * K);
     *s_bytes = (size_t)(E * (N / 128) * (K / 128) * 4);
   } else {
@@ -258,8 +277,7 @@ moe_status_t moe_preshuffle_weights(const moe_cfg_t* cfg, int32_t which, const v
   if (!w || !s || !w_out || !s_out) return MOE_ERR_NULL;
   const int Hp = cfg->pad.hidden_padded, Ip = cfg->pad.inter_padded;
   const int N = which == 13 ? 2 * Ip : Hp, K = which == 13 ? Hp : Ip;
-  const int mode = cfg->quant_mode == MOE_QUANT_FP8_BLOCK ? moe::kQuantFp8 : moe::kQuantMx;
-  return hip_status(moe::launch_preshuffle(mode, (const uint8_t*)w, s, cfg->num_experts, N, K, (uint8_t*)w_out,
+  return hip_status(moe::launch_preshuffle(cfg->quant_mode, (const uint8_t*)w, s, cfg->num_experts, N, K, (uint8_t*)w_out,
                                            s_out, as_stream(stream)));
 }
 
@@ -275,7 +293,7 @@ moe_status_t moe_grouped_gemm1_swiglu(const moe_cfg_t* cfg, int32_t T, const voi
   if (!xq || !xs || !sorted_ids || !block_expert || !num_post_padded || !w13 || !w13_scale || !aq || !as)
     return MOE_ERR_NULL;
   const int32_t nb = max_blocks((int64_t)T * cfg->top_k, cfg->num_experts, cfg->block_m);
-  const int mode = cfg->quant_mode == MOE_QUANT_FP8_BLOCK ? moe::kQuantFp8 : moe::kQuantMx;
+  const int mode = cfg->quant_mode;
   moe::GemmArgs a = gemm1_args(cfg, T, xq, xs, sorted_ids, block_expert, num_post_padded, w13, w13_scale, aq, as);
   return hip_status(moe::launch_gemm1(mode, cfg->block_m, nb, a, as_stream(stream)));
 }
@@ -298,7 +316,7 @@ moe_status_t moe_grouped_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const vo
   const size_t ybytes = align_up((size_t)P * cfg->pad.hidden_padded * 4);
   if (ws_bytes < ybytes) return MOE_ERR_WORKSPACE;
   const int32_t nb = max_blocks(P, cfg->num_experts, cfg->block_m);
-  const int mode = cfg->quant_mode == MOE_QUANT_FP8_BLOCK ? moe::kQuantFp8 : moe::kQuantMx;
+  const int mode = cfg->quant_mode;
   hipStream_t s = as_stream(stream);
   float* y = (float*)ws;
   moe::GemmArgs a = gemm2_args(cfg, T, aq, as, sorted_ids, block_expert, num_post_padded, w2, w2_scale, y, topk_w);
@@ -338,7 +356,7 @@ moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, in
   const int E = cfg->num_experts, k = cfg->top_k, BM = cfg->block_m;
   const int64_t P = (int64_t)T * k;
   const int32_t nb = max_blocks(P, E, BM);
-  const int mode = cfg->quant_mode == MOE_QUANT_FP8_BLOCK ? moe::kQuantFp8 : moe::kQuantMx;
+  const int mode = cfg->quant_mode;
   hipError_t e;
   if ((e = moe::launch_route_topk(router_logits, T, E, k, ids, wts, s)) != hipSuccess) return MOE_ERR_HIP;
   if ((e = moe::launch_permute_align(ids, T, k, E, BM, nb, sorted, bexp, offs, npp, s)) != hipSuccess)

@@ -22,12 +22,31 @@
 //        operands to f16 and uses the f16 MFMA (exact fp32 sums); GEMM2 uses
 //        the FP8 MFMA directly.
 //   MX:  the scaled MFMA applies the E8M0 scales of both operands itself.
+//   UE8M0 FP8 ("[AMD] [GLM5] Opt-in prefill-only FP8 dense projection GEMM
+//        for MLA q_b/o_proj (gfx950)", Modifications: 128x128 UE8M0 weight
+//        scales; 1x128 UE8M0 activation scales here): GEMM1 as block FP8
+//        (f16 MFMA, promotion by the exact power-of-two scale product) with
+//        UE8M0 re-quantisation; GEMM2 on the scaled FP8 MFMA, which applies
+//        both power-of-two scales itself, so there is no promotion at all.
 #include <utility>
 
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
+
+// Operand modes of the GEMM kernels (template parameter MODE).
+constexpr int kGemmFp8 = 1;     // FP8 MFMA, fp32 promotion per K block, fp32 activation scales
+constexpr int kGemmMx = 2;      // scaled FP4 MFMA, E8M0 scales per 1x32
+constexpr int kGemmFp8F16 = 3;  // FP8 widened to f16, f16 MFMA, fp32 promotion, fp32 activation scales
+constexpr int kGemmE8F16 = 4;   // as kGemmFp8F16 with UE8M0 activation-scale bytes
+constexpr int kGemmE8 = 5;      // scaled FP8 MFMA with UE8M0 bytes for both operands, no promotion
+static_assert(kGemmMx == kQuantMx, "MX tiles are sized by the quant mode");
+
+// Activation scales arrive as E8M0 bytes (a dword holds 4 K blocks).
+constexpr bool e8_tokens(int mode) { return mode == kGemmE8F16 || mode == kGemmE8; }
+// FP8 operands widened to f16 for the f16 MFMA.
+constexpr bool f16_path(int mode) { return mode == kGemmFp8F16 || mode == kGemmE8F16; }
 
 // The lane's 32 FP8 bytes as four f16 operands: step st holds bytes
 // 8st..8st+7, i.e. K = 32*(lane/16) + 8st + i for both A and B.
@@ -76,9 +95,9 @@ struct Ring {
   static constexpr int NTH = NWAVE * 64;
   static constexpr int MT = BM >= 64 ? 4 : BM / 16;              // token tiles per wave
   static constexpr int TT = BM / 16;                             // token tiles per slot
-  static constexpr int TILE = (MODE == kQuantMx) ? 1024 : 2048;  // one 16 x 128 operand tile
+  static constexpr int TILE = (MODE == kGemmMx) ? 1024 : 2048;  // one 16 x 128 operand tile
   static constexpr int HALVES = TILE / 1024;
-  static constexpr int AROW = (MODE == kQuantMx) ? 64 : 128;     // token bytes per K block
+  static constexpr int AROW = (MODE == kGemmMx) ? 64 : 128;     // token bytes per K block
   static constexpr int W_OFF = 0;                                // 16 weight tiles
   static constexpr int T_OFF = 16 * TILE;                        // TT token tiles
   static constexpr int TS_OFF = T_OFF + TT * TILE;               // token scales, 256 B per 64 tokens
@@ -89,7 +108,7 @@ struct Ring {
   static constexpr int DW = 16 * HALVES / NWAVE;                 // weight loads per wave per slot
   static constexpr int NTD = TT * HALVES;                        // token loads per slot
   static constexpr int DT = (NTD + NWAVE - 1) / NWAVE;           // ... per wave (BM < 64: waves < NTD)
-  static constexpr int DWS = (MODE == kQuantMx) ? 16 / NWAVE : 0;  // every 4th K block only
+  static constexpr int DWS = (MODE == kGemmMx) ? 16 / NWAVE : 0;  // every 4th K block only
   // loads every wave issues in every K block (waits use this minimum; waves
   // that issue more only wait longer)
   static constexpr int D = DW + NTD / NWAVE + 1;
@@ -167,8 +186,10 @@ __device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const u
 #pragma unroll
   for (int q = 0; q < R::DT; ++q)
     if (wave * R::DT + q < R::NTD) dma16<false>(src.t[q] + kb * R::AROW, base + R::T_OFF + (wave * R::DT + q) * 1024);
-  if (lane < 16) dma4(src.ts + kb * 4, base + R::TS_OFF + (wave >> 2) * 256 + (wave & 3) * 64);
-  if constexpr (MODE != kQuantMx) {
+  // token scales: fp32 per K block, or the E8M0 dword of K blocks kb & ~3 .. +3
+  const int ts_off = e8_tokens(MODE) ? (kb & ~3) : kb * 4;
+  if (lane < 16) dma4(src.ts + ts_off, base + R::TS_OFF + (wave >> 2) * 256 + (wave & 3) * 64);
+  if constexpr (MODE != kGemmMx) {
     if (wave == R::NWAVE - 1 && lane < 2) dma4(src.wsc + kb * 4, base + R::WSC_OFF);
   }
   if constexpr (R::DWS > 0) {
@@ -224,7 +245,7 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
   const uint8_t* tl = tt + lane * 16;
   const uint8_t* tsl = slot + R::TS_OFF + wt * 256 + (lane & 15) * 16;
   constexpr int MT = R::MT;
-  if constexpr (MODE == kQuantMx) {
+  if constexpr (MODE == kGemmMx) {
     const uint4 tsd = *(const uint4*)tsl;
     const int sh = 8 * (lane >> 4);
     const int st[4] = {(int)((tsd.x >> sh) & 0xFFu), (int)((tsd.y >> sh) & 0xFFu), (int)((tsd.z >> sh) & 0xFFu),
@@ -245,10 +266,37 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
       for (int j = 0; j < 4; ++j) acc[m][j] = mfma_fp4_scaled_t<0>(w[j], t, acc[m][j], sw[j], st[m]);
     }
   } else {
-    const float4 ts = *(const float4*)tsl;
-    const float tsc[4] = {ts.x, ts.y, ts.z, ts.w};
+    // token scales of tiles m = 0..3 (row lane % 16): fp32, or E8M0 bytes
+    // (byte kb % 4 of each dword) and their exact fp32 values
+    float tsc[4];
+    int tsb[4];
+    if constexpr (e8_tokens(MODE)) {
+      const uint4 tw = *(const uint4*)tsl;
+      const int sh = 8 * (kb & 3);
+      const uint32_t w4[4] = {tw.x, tw.y, tw.z, tw.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        tsb[m] = (int)((w4[m] >> sh) & 0xFFu);
+        tsc[m] = e8m0_value((uint32_t)tsb[m]);
+      }
+    } else {
+      const float4 ts = *(const float4*)tsl;
+      tsc[0] = ts.x; tsc[1] = ts.y; tsc[2] = ts.z; tsc[3] = ts.w;
+    }
     // GEMM1: tiles 0,1 are gate rows (scale sw0), 2,3 up rows (sw1); GEMM2: all sw0
-    if constexpr (MODE == kQuantFp8) {
+    if constexpr (MODE == kGemmE8) {
+      // power-of-two weight scale as its E8M0 byte (2^-127 is 0x00400000 -> 0)
+      const int swb = (int)(__float_as_uint(sw0) >> 23);
+      v8i w[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = lds_frag32(wl + tiles[j] * R::TILE);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const v8i t = lds_tok32(tt + m * R::TILE, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[m][j] = mfma_fp8_scaled(w[j], t, acc[m][j], swb, tsb[m]);
+      }
+    } else if constexpr (MODE == kGemmFp8) {
       v8i w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) w[j] = lds_frag32(wl + tiles[j] * R::TILE);
@@ -375,6 +423,7 @@ __device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&
   constexpr int MT = Ring<MODE, BM>::MT;
   const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
   const float L = p.limit;
+  constexpr bool MXQ = MODE == kGemmMx, E8Q = MODE == kGemmE8F16;
   float av[MT][2][4];
   float tmax[MT];
 #pragma unroll
@@ -393,27 +442,41 @@ __device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     tmax[m] = mx;
   }
-  if constexpr (MODE != kQuantMx) {
+  if constexpr (!MXQ) {
     if (q == 0) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) red[wn][wt * 64 + m * 16 + c16] = tmax[m];
     }
     lds_barrier();
     const int nsc = p.Ip / 128;
+    const int64_t ld_e8 = (nsc + 3) / 4 * 4;  // UE8M0 scale rows: whole dwords
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int t = wt * 64 + m * 16 + c16;
       const float amax = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
-      const float s = amax / kE4M3Max;
       uint8_t* row = p.aq + (int64_t)(row0 + t) * p.Ip + nt * 128 + 32 * wn + 4 * q;
+      if constexpr (E8Q) {
+        const uint32_t b = ue8m0_byte(amax);
+        const float inv = e8m0_inverse(b);
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        uint32_t packed = 0;
+        for (int jj = 0; jj < 2; ++jj) {
+          uint32_t packed = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) packed |= ((amax > 0.0f) ? fp8_quant(av[m][jj][i], s) : 0u) << (8 * i);
-        *(uint32_t*)(row + 16 * jj) = packed;
+          for (int i = 0; i < 4; ++i) packed |= ((amax > 0.0f) ? fp8e8_quant(av[m][jj][i], inv) : 0u) << (8 * i);
+          *(uint32_t*)(row + 16 * jj) = packed;
+        }
+        if (wn == 0 && q == 0) ((uint8_t*)p.as)[(int64_t)(row0 + t) * ld_e8 + nt] = (uint8_t)b;
+      } else {
+        const float s = amax / kE4M3Max;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          uint32_t packed = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) packed |= ((amax > 0.0f) ? fp8_quant(av[m][jj][i], s) : 0u) << (8 * i);
+          *(uint32_t*)(row + 16 * jj) = packed;
+        }
+        if (wn == 0 && q == 0) ((float*)p.as)[(int64_t)(row0 + t) * nsc + nt] = (amax > 0.0f) ? s : 0.0f;
       }
-      if (wn == 0 && q == 0) ((float*)p.as)[(int64_t)(row0 + t) * nsc + nt] = (amax > 0.0f) ? s : 0.0f;
     }
   } else {
     const int nsc = p.Ip / 32;
@@ -481,7 +544,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   __shared__ int32_t exp_lds[NB];
   __shared__ __attribute__((aligned(256))) float wts_lds[G1 ? 1 : NB][BM];
   __shared__ float red[4][BM];
-  __shared__ __attribute__((aligned(256))) uint8_t ws_buf[MODE == kQuantMx ? NWS : 1][MODE == kQuantMx ? R::WS_BYTES : 16];
+  __shared__ __attribute__((aligned(256))) uint8_t ws_buf[MODE == kGemmMx ? NWS : 1][MODE == kGemmMx ? R::WS_BYTES : 16];
   auto slot = [&](auto ic) -> uint8_t* {
     constexpr int i = decltype(ic)::value;
     if constexpr (i == 0) return slot0;
@@ -558,9 +621,10 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
     }
     {
       const int64_t row = row_of(ring_scale_row(wave, lane));
-      rs.ts = (MODE == kQuantMx) ? (const uint8_t*)p.As + row * p.ldas : (const uint8_t*)p.As + row * p.ldas * 4;
+      rs.ts = (MODE == kGemmMx || e8_tokens(MODE)) ? (const uint8_t*)p.As + row * p.ldas
+                                                     : (const uint8_t*)p.As + row * p.ldas * 4;
     }
-    if constexpr (MODE != kQuantMx) {
+    if constexpr (MODE != kGemmMx) {
       // GEMM1: the gate and the up 128-row block of the N tile; GEMM2: the
       // N tile's two 128-row blocks (the second clamped to the last block)
       const int NB128 = p.N / 128;
@@ -621,7 +685,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   auto issue_next = [&](auto slot_c, int s) {
     if (i_ii < n_my) {
       const uint8_t* ws = nullptr;
-      if constexpr (MODE == kQuantMx) {
+      if constexpr (MODE == kGemmMx) {
         if ((i_kb & 3) == 0) ws = ws_buf[(i_grp++) % NWS];
       }
       ring_issue<MODE, BM>(rs, slot(slot_c), wave, i_kb, ws);
@@ -653,7 +717,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
     constexpr int d = decltype(dc)::value;
     vm_wait_barrier<(S - 2) * R::D>();
     float sw0 = 0.0f, sw1 = 0.0f;
-    if constexpr (MODE != kQuantMx) {
+    if constexpr (MODE != kGemmMx) {
       // GEMM1: gate and up scale; GEMM2: the scale of the wave's 128-row block
       const float2 sc = *(const float2*)(slot(std::integral_constant<int, d>{}) + R::WSC_OFF);
       sw0 = (G1 || (wn >> 1) == 0) ? sc.x : sc.y;
@@ -661,7 +725,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
     }
     if (s == wts_step) issue_wts(wts_item);
     issue_next(std::integral_constant<int, (d + S - 1) % S>{}, s);
-    if constexpr (MODE == kQuantMx) {
+    if constexpr (MODE == kGemmMx) {
       if ((c_kb & 3) == 0) c_ws = ws_buf[(c_grp++) % NWS];
     }
     if (active)
@@ -714,8 +778,8 @@ static int device_cus() {
 
 template <int MODE, bool G1>
 static hipError_t launch_gemm_mode(int block_m, int nb, const GemmArgs& a, hipStream_t s) {
-  constexpr int SR = (MODE == kQuantMx) ? MOE_RING_S_MX : MOE_RING_S_FP8;    // block_m 64 / 128
-  constexpr int SD = (MODE == kQuantMx) ? MOE_RING_S_MX : MOE_RING_S_SMALL;  // block_m 16 / 32
+  constexpr int SR = (MODE == kGemmMx) ? MOE_RING_S_MX : MOE_RING_S_FP8;    // block_m 64 / 128
+  constexpr int SD = (MODE == kGemmMx) ? MOE_RING_S_MX : MOE_RING_S_SMALL;  // block_m 16 / 32
   // One workgroup per CU (the ring's LDS use allows no more), fewer when
   // there are fewer items; a multiple of kXcds so that every XCD gets the
   // same number of workgroups.
@@ -740,17 +804,24 @@ static hipError_t launch_gemm_mode(int block_m, int nb, const GemmArgs& a, hipSt
 }
 
 // GEMM1's output is re-quantised, so its sum must be fp32-exact: block FP8
-// runs on the f16 MFMA (FP8 storage, exact widening in registers).
+// (either scale format) runs on the f16 MFMA (FP8 storage, exact widening in
+// registers).
 hipError_t launch_gemm1(int mode, int block_m, int nb, const GemmArgs& a, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
-  return mode == kQuantFp8 ? launch_gemm_mode<kQuantFp8F16, true>(block_m, nb, a, s)
-                           : launch_gemm_mode<kQuantMx, true>(block_m, nb, a, s);
+  switch (mode) {
+    case kQuantFp8: return launch_gemm_mode<kGemmFp8F16, true>(block_m, nb, a, s);
+    case kQuantFp8E8: return launch_gemm_mode<kGemmE8F16, true>(block_m, nb, a, s);
+    default: return launch_gemm_mode<kGemmMx, true>(block_m, nb, a, s);
+  }
 }
 
 hipError_t launch_gemm2(int mode, int block_m, int nb, const GemmArgs& a, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
-  return mode == kQuantFp8 ? launch_gemm_mode<kQuantFp8, false>(block_m, nb, a, s)
-                           : launch_gemm_mode<kQuantMx, false>(block_m, nb, a, s);
+  switch (mode) {
+    case kQuantFp8: return launch_gemm_mode<kGemmFp8, false>(block_m, nb, a, s);
+    case kQuantFp8E8: return launch_gemm_mode<kGemmE8, false>(block_m, nb, a, s);
+    default: return launch_gemm_mode<kGemmMx, false>(block_m, nb, a, s);
+  }
 }
 
 // out[t, h] = bf16(sum_j y[t*k + j, h]) with the slot sum in order j = 0..k-1.

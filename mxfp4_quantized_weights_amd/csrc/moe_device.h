@@ -79,6 +79,45 @@ __device__ __forceinline__ float e8m0_inverse(uint32_t b) {
   return __uint_as_float((254u - b) << 23);
 }
 
+// 2^(b - 127) as fp32 for an E8M0 byte b in [0, 254]; b = 0 is the fp32
+// subnormal 2^-127.
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+  return __uint_as_float(b ? (b << 23) : 0x00400000u);
+}
+
+// UE8M0 block scale ("[AMD] [GLM5] Opt-in prefill-only FP8 dense projection
+// GEMM for MLA q_b/o_proj (gfx950)", Modifications: e4m3 with a 128x128 UE8M0
+// scale): 2^e with e the smallest integer such that 448 * 2^e >= amax,
+// biased by 127 and clamped to [0, 254]; 0 for amax == 0.  With amax =
+// 1.m * 2^E, 448 * 2^e = 1.75 * 2^(e+8), so e = E - 8 when 1.m <= 1.75
+// (mantissa field <= 0x600000), else E - 7.  Subnormal amax is normalised
+// first.
+__device__ __forceinline__ uint32_t ue8m0_byte(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  if (u == 0u) return 0u;
+  int E;
+  uint32_t mant;
+  const uint32_t ef = u >> 23;
+  if (ef) {
+    E = (int)ef - 127;
+    mant = u & 0x7FFFFFu;
+  } else {
+    const int p = 31 - __builtin_clz(u);
+    E = p - 149;
+    mant = (u << (23 - p)) & 0x7FFFFFu;
+  }
+  const int b = E - 8 + (mant > 0x600000u ? 1 : 0) + 127;
+  return (uint32_t)(b < 0 ? 0 : (b > 254 ? 254 : b));
+}
+
+// e4m3 code of v in a UE8M0 group with scale byte b (inv = 2^(127 - b)):
+// the scaling is exact, and |v| * inv <= 448 by the choice of b.
+__device__ __forceinline__ uint32_t fp8e8_quant(float v, float inv) {
+  float r = v * inv;
+  r = fminf(fmaxf(r, -kE4M3Max), kE4M3Max);
+  return e4m3_code(r);
+}
+
 // fp32 -> bf16 bits, round to nearest even.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -138,6 +177,13 @@ __device__ __forceinline__ float group_max(float v) {
 // column; the result lane l holds C[4*(l/16) + i][l % 16], i = 0..3.
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// 16x16x128 FP8 MFMA with per-lane E8M0 scales: sa scales lane l's 32 A
+// values (row l % 16), sb its 32 B values; a power-of-two block scale is
+// applied exactly inside the instruction.
+__device__ __forceinline__ v4f mfma_fp8_scaled(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
 // Two e4m3 values (bytes 0,1 or 2,3 of w) to two f16 values.  Exact: every

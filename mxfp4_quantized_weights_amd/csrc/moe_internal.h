@@ -9,11 +9,14 @@
 
 namespace moe {
 
-constexpr int kQuantFp8 = 1;
-constexpr int kQuantMx = 2;
-// GEMM operand mode: FP8 storage, operands widened to f16 for an MFMA whose
-// internal sum is exact to fp32 precision (internal to the GEMM kernels).
-constexpr int kQuantFp8F16 = 3;
+// Quantisation contracts (the values of MOE_QUANT_* in include/moe.h).
+constexpr int kQuantFp8 = 1;    // e4m3, fp32 scales (128x128 weights, 1x128 activations)
+constexpr int kQuantMx = 2;     // E2M1 + E8M0 per 1x32
+constexpr int kQuantFp8E8 = 3;  // e4m3, UE8M0 scale bytes (128x128 weights, 1x128 activations)
+
+// Row stride in bytes of UE8M0 activation-scale rows: one byte per 128
+// columns, rounded up to whole dwords so that the GEMMs load aligned words.
+inline int64_t e8_scale_ld(int64_t cols_padded) { return (cols_padded / 128 + 3) / 4 * 4; }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);
@@ -26,7 +29,9 @@ hipError_t launch_permute_align(const int32_t* ids, int T, int k, int E, int blo
 hipError_t launch_quant_rows(const void* in, bool in_is_bf16, int64_t rows, int cols, int64_t ld_in,
                              int cols_padded, int mode, void* q, void* scales, hipStream_t s);
 
-hipError_t launch_quant_weight_fp8(const float* w, int E, int N, int K, uint8_t* q, float* scales,
+// Block FP8 weights, one scale per [128, 128] block: fp32 (kQuantFp8) or a
+// UE8M0 byte (kQuantFp8E8).
+hipError_t launch_quant_weight_fp8(int mode, const float* w, int E, int N, int K, uint8_t* q, void* scales,
                                    hipStream_t s);
 
 hipError_t launch_preshuffle(int mode, const uint8_t* w, const void* sc, int E, int N, int K,
@@ -36,14 +41,14 @@ struct GemmArgs {
   const uint8_t* A;       // GEMM1: quantised x [T, ...]; GEMM2: aq [rows, ...]
   const void* As;         // activation scales
   int64_t lda;            // bytes per A row
-  int64_t ldas;           // scale elements per A row (FP8: floats, MX: bytes)
+  int64_t ldas;           // scale elements per A row (FP8: floats; MX, UE8M0: bytes)
   const int32_t* sorted_ids;
   const int32_t* block_expert;
   const int32_t* npp;
   int32_t top_k;
   int32_t num_pairs;
   const uint8_t* B;       // TILED_V1 weights
-  const void* Bs;         // FP8: canonical f32 block scales; MX: tiled scale dwords
+  const void* Bs;         // FP8, UE8M0: f32 block scales [E, N/128, K/128]; MX: tiled scale dwords
   int32_t N;              // weight rows per expert (padded)
   int32_t K;              // reduction length (padded)
   int32_t n_tiles;        // N-tiles per M-block

@@ -11,6 +11,11 @@
 // MXFP4 group (32): b = clamp(floor(log2 amax) - 2 + 127, 0, 254) (0 for
 //                   amax = 0), q = RNE_E2M1(clamp(v * 2^(127 - b), +-6)),
 //                   element 2i in the low nibble of byte i.
+// UE8M0 FP8 group:  ("[AMD] [GLM5] Opt-in prefill-only FP8 dense projection
+//                   GEMM for MLA q_b/o_proj (gfx950)", Modifications) scale
+//                   2^e, e smallest with 448 * 2^e >= amax, stored as the
+//                   byte b = clamp(e + 127, 0, 254) (0 for amax = 0);
+//                   q = RNE(v * 2^(127 - b)).
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -49,6 +54,8 @@ __device__ __forceinline__ void load8(const void* in, int64_t row, int64_t ld, i
 
 // A wave quantises four 128-column units (16 lanes each, 8 elements per
 // lane); a unit is one FP8 group or four MX groups of 4 lanes.
+// UE8M0 scale rows are e8_scale_ld(cols_padded) bytes long; the bytes past
+// the last group are written as zero.
 template <bool BF16, bool VEC, int MODE>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ in, int64_t rows, int cols,
                                                          int64_t ld_in, int cols_padded,
@@ -86,6 +93,25 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
             make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
         if ((lane & 15) == 0) ((float*)scales)[row * units + g] = s;
       }
+    } else if constexpr (MODE == kQuantFp8E8) {
+      a = group_max<16>(a);
+      const uint32_t b = ue8m0_byte(a);
+      const float inv = e8m0_inverse(b);
+      uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (a > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = fp8e8_quant(v[i], inv);
+      }
+      if (live) {
+        *(uint2*)(q + row * (int64_t)cols_padded + col) =
+            make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+        const int64_t lds = (units + 3) / 4 * 4;
+        uint8_t* srow = (uint8_t*)scales + row * lds;
+        if ((lane & 15) == 0) srow[g] = (uint8_t)b;
+        if ((lane & 15) == 1 && g == units - 1) {
+          for (int i = units; i < lds; ++i) srow[i] = 0;
+        }
+      }
     } else {
       a = group_max<4>(a);
       const uint32_t b = e8m0_byte(a);
@@ -106,6 +132,9 @@ static void launch_quant_rows_t(dim3 grid, hipStream_t s, const void* in, int64_
                                 int cols_padded, int mode, uint8_t* q, void* scales) {
   if (mode == kQuantFp8)
     hipLaunchKernelGGL((quant_rows_kernel<BF16, VEC, kQuantFp8>), grid, dim3(256), 0, s, in, rows, cols, ld_in,
+                       cols_padded, q, scales);
+  else if (mode == kQuantFp8E8)
+    hipLaunchKernelGGL((quant_rows_kernel<BF16, VEC, kQuantFp8E8>), grid, dim3(256), 0, s, in, rows, cols, ld_in,
                        cols_padded, q, scales);
   else
     hipLaunchKernelGGL((quant_rows_kernel<BF16, VEC, kQuantMx>), grid, dim3(256), 0, s, in, rows, cols, ld_in,
@@ -133,9 +162,10 @@ hipError_t launch_quant_rows(const void* in, bool in_is_bf16, int64_t rows, int 
 }
 
 // One workgroup per [128, 128] block; thread t covers row t/2, columns
-// 64*(t%2) .. +64.
+// 64*(t%2) .. +64.  E8: UE8M0 scale bytes instead of fp32 scales.
+template <bool E8>
 __global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const float* __restrict__ w, int N, int K,
-                                                               uint8_t* __restrict__ q, float* __restrict__ scales) {
+                                                               uint8_t* __restrict__ q, void* __restrict__ scales) {
   __shared__ float red[4];
   const int nbk = K / 128, nbn = N / 128;
   const int64_t blk = blockIdx.x;
@@ -159,24 +189,43 @@ __global__ __launch_bounds__(256) void quant_weight_fp8_kernel(const float* __re
   if ((t & 63) == 0) red[t >> 6] = a;
   __syncthreads();
   a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float s = (a > 0.0f) ? a / kE4M3Max : 0.0f;
   uint32_t* dst = (uint32_t*)(q + (e * N + r) * (int64_t)K + c0);
+  const int64_t si = (e * nbn + bn) * nbk + bk;
+  if constexpr (E8) {
+    const uint32_t b = ue8m0_byte(a);
+    const float inv = e8m0_inverse(b);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    uint32_t word = 0;
-    if (a > 0.0f) {
-      word = fp8_quant(v[i].x, s) | (fp8_quant(v[i].y, s) << 8) | (fp8_quant(v[i].z, s) << 16) |
-             (fp8_quant(v[i].w, s) << 24);
+    for (int i = 0; i < 16; ++i) {
+      uint32_t word = 0;
+      if (a > 0.0f) {
+        word = fp8e8_quant(v[i].x, inv) | (fp8e8_quant(v[i].y, inv) << 8) | (fp8e8_quant(v[i].z, inv) << 16) |
+               (fp8e8_quant(v[i].w, inv) << 24);
+      }
+      dst[i] = word;
     }
-    dst[i] = word;
+    if (t == 0) ((uint8_t*)scales)[si] = (uint8_t)b;
+  } else {
+    const float s = (a > 0.0f) ? a / kE4M3Max : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t word = 0;
+      if (a > 0.0f) {
+        word = fp8_quant(v[i].x, s) | (fp8_quant(v[i].y, s) << 8) | (fp8_quant(v[i].z, s) << 16) |
+               (fp8_quant(v[i].w, s) << 24);
+      }
+      dst[i] = word;
+    }
+    if (t == 0) ((float*)scales)[si] = s;
   }
-  if (t == 0) scales[(e * nbn + bn) * nbk + bk] = s;
 }
 
-hipError_t launch_quant_weight_fp8(const float* w, int E, int N, int K, uint8_t* q, float* scales,
+hipError_t launch_quant_weight_fp8(int mode, const float* w, int E, int N, int K, uint8_t* q, void* scales,
                                    hipStream_t s) {
   int64_t blocks = (int64_t)E * (N / 128) * (K / 128);
-  hipLaunchKernelGGL(quant_weight_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w, N, K, q, scales);
+  if (mode == kQuantFp8E8)
+    hipLaunchKernelGGL(quant_weight_fp8_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, w, N, K, q, scales);
+  else
+    hipLaunchKernelGGL(quant_weight_fp8_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, w, N, K, q, scales);
   return hipGetLastError();
 }
 
@@ -187,6 +236,8 @@ hipError_t launch_quant_weight_fp8(const float* w, int E, int N, int K, uint8_t*
 //   FP8: tile = 2048 bytes, [h (2)][lane (64)][16 bytes]: half h holds the
 //        lane's K bytes 16h .. 16h+15, so each 16-byte wave load is 1 KB
 //        contiguous.  Block scales stay canonical f32 [E, N/128, K/128].
+//   UE8M0 FP8: the same tiles; the scale bytes are widened to their exact
+//        fp32 values 2^(b-127) in the canonical [E, N/128, K/128] order.
 //   MX:  tile = 1024 bytes, [lane (64)][16 bytes] (32 packed E2M1).  Scales:
 //        per (expert, nt) and group of 4 K blocks, [lane (64)][4 bytes], byte
 //        i = E8M0 of K block 4q+i for the lane's row and 32-group; missing K
@@ -251,6 +302,12 @@ __global__ __launch_bounds__(256) void preshuffle_mx_scale_kernel(const uint8_t*
   }
 }
 
+__global__ __launch_bounds__(256) void e8m0_to_f32_kernel(const uint8_t* __restrict__ in, int64_t n,
+                                                          float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    out[i] = e8m0_value(in[i]);
+}
+
 __global__ __launch_bounds__(256) void copy_words_kernel(const uint32_t* __restrict__ in, int64_t n,
                                                          uint32_t* __restrict__ out) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) out[i] = in[i];
@@ -266,12 +323,16 @@ static unsigned grid_for(int64_t items) {
 hipError_t launch_preshuffle(int mode, const uint8_t* w, const void* sc, int E, int N, int K,
                              uint8_t* w_out, void* s_out, hipStream_t s) {
   const int64_t KB = K / 128, NT = N / 16;
-  if (mode == kQuantFp8) {
+  if (mode == kQuantFp8 || mode == kQuantFp8E8) {
     int64_t chunks = (int64_t)E * NT * KB * 128;
     hipLaunchKernelGGL(preshuffle_fp8_kernel, dim3(grid_for(chunks)), dim3(256), 0, s, w, chunks, N, K, w_out);
     int64_t words = (int64_t)E * (N / 128) * KB;
-    hipLaunchKernelGGL(copy_words_kernel, dim3(grid_for(words)), dim3(256), 0, s, (const uint32_t*)sc, words,
-                       (uint32_t*)s_out);
+    if (mode == kQuantFp8E8)
+      hipLaunchKernelGGL(e8m0_to_f32_kernel, dim3(grid_for(words)), dim3(256), 0, s, (const uint8_t*)sc, words,
+                         (float*)s_out);
+    else
+      hipLaunchKernelGGL(copy_words_kernel, dim3(grid_for(words)), dim3(256), 0, s, (const uint32_t*)sc, words,
+                         (uint32_t*)s_out);
   } else {
     int64_t chunks = (int64_t)E * NT * KB * 64;
     hipLaunchKernelGGL(preshuffle_mx_kernel, dim3(grid_for(chunks)), dim3(256), 0, s, w, chunks, N, K, w_out);

@@ -13,7 +13,7 @@ import torch
 import oracle as O
 import workloads as W
 
-TOL = {"fp8": 2e-2, "mxfp4": 6e-2}
+TOL = {"fp8": 2e-2, "fp8_ue8m0": 2e-2, "mxfp4": 6e-2}
 
 
 def log(msg: str):
@@ -92,6 +92,20 @@ def requant_tie_allowance(stages, Q: O.QuantWeights, mode: str, hidden: int, eps
                     continue
                 s = np.float32(amax / np.float32(448.0))
                 delta[g0:g0 + 128] = _tie_deltas(grp / s, g8, eps) * float(s)
+        elif mode == "fp8_ue8m0":
+            for g0 in range(0, a.size, 128):
+                grp = a[g0:g0 + 128].astype(np.float64)
+                amax = float(np.max(np.abs(grp)))
+                if amax == 0:
+                    continue
+                sc = 2.0 ** (int(O.ue8m0_scale_byte(amax)) - 127)
+                d = _tie_deltas(grp / sc, g8, eps) * sc
+                m = np.log2(amax / 448.0)
+                if abs(m - np.round(m)) <= eps:
+                    # amax sits at a power-of-two boundary of the scale: every
+                    # code may move by one step of the larger scale
+                    d = np.maximum(d, 2.0 * sc * 32.0 * (np.abs(grp) > 0))
+                delta[g0:g0 + 128] = d
         else:
             for g0 in range(0, a.size, 32):
                 grp = a[g0:g0 + 32].astype(np.float64)

@@ -68,6 +68,7 @@ def status(c):
 def test_valid_configs():
     assert status(cfg()) == OK
     assert status(cfg(quant="mxfp4")) == OK
+    assert status(cfg(quant="fp8_ue8m0")) == OK
     assert status(cfg(hidden=4000, inter=1000, hidden_padded=4096, inter_padded=1024)) == OK
     assert status(cfg(swiglu_limit=math.inf)) == OK
     for bm in (16, 32, 64, 128):
@@ -79,7 +80,8 @@ def test_valid_configs():
 @pytest.mark.parametrize("kw,code", [
     (dict(gate_mode=M.MOE_GATE_INTERLEAVED), UNSUP),
     (dict(gate_mode=7), UNSUP),
-    (dict(quant=3), UNSUP),
+    (dict(quant=4), UNSUP),
+    (dict(quant=0), UNSUP),
     (dict(block_m=48), UNSUP),
     (dict(block_m=256), UNSUP),
     (dict(swiglu_limit=0.0), UNSUP),
@@ -162,6 +164,8 @@ def test_stage_entry_points_validate_before_launch():
     assert lib.moe_quant_weights(1, FAKE, 2, 100, 128, FAKE, FAKE, None) == ALIGN
     assert lib.moe_quant_weights(2, FAKE, 2, 100, 96, FAKE, FAKE, None) == ALIGN
     assert lib.moe_quant_weights(7, FAKE, 2, 128, 128, FAKE, FAKE, None) == UNSUP
+    assert lib.moe_quant_weights(3, FAKE, 2, 128, 96, FAKE, FAKE, None) == ALIGN
+    assert lib.moe_quant_act(FAKE, 1, 4, 100, 100, 100, 3, FAKE, FAKE, None) == ALIGN
     c = cfg()
     assert lib.moe_preshuffle_weights(ctypes.byref(c), 3, FAKE, FAKE, FAKE, FAKE, None) == SHAPE
     assert lib.moe_preshuffle_weights(ctypes.byref(c), 13, None, FAKE, FAKE, FAKE, None) == NULL
@@ -183,6 +187,14 @@ def test_block_and_buffer_sizes():
     assert (aq, as_) == (rows * 1024, rows * 8 * 4)
     c = cfg(quant="mxfp4", block_m=128)
     assert M.intermediate_bytes(c, 4096) == (rows * 512, rows * 32)
+    # UE8M0: one scale byte per 128 columns, rows rounded up to whole dwords
+    c = cfg(quant="fp8_ue8m0", block_m=128)
+    assert M.intermediate_bytes(c, 4096) == (rows * 1024, rows * 8)
+    c = cfg(quant="fp8_ue8m0", block_m=128, inter=128)
+    assert M.intermediate_bytes(c, 4096) == (rows * 128, rows * 4)
+    assert M.e8_scale_ld(128) == 4 and M.e8_scale_ld(4096) == 32 and M.e8_scale_ld(4224) == 36
+    # TILED_V1 keeps UE8M0 block scales as fp32 values
+    assert M.preshuffled_bytes(cfg(quant="fp8_ue8m0"), 13) == M.preshuffled_bytes(cfg(), 13)
     assert M.preshuffled_bytes(cfg(), 13) == (288 * 2048 * 4096, 288 * 16 * 32 * 4)
     assert M.preshuffled_bytes(cfg(), 2) == (288 * 4096 * 1024, 288 * 32 * 8 * 4)
     assert M.preshuffled_bytes(cfg(quant="mxfp4"), 13) == (288 * 2048 * 2048, 288 * 128 * 8 * 64 * 4)

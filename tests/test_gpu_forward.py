@@ -94,6 +94,14 @@ CASES = {
     "short_k_fp8_bm128": (SHORT_K, 128),
     "short_k_fp8_bm16": (SHORT_K.with_(T=512), 16),
     "short_k_mxfp4_bm128": (SHORT_K.with_(mode="mxfp4"), 128),
+    # block FP8 with UE8M0 (power-of-two) scales
+    "tiny_ue8m0": (TINY.with_(mode="fp8_ue8m0"), None),
+    "mid_ue8m0_bm16": (MID.with_(mode="fp8_ue8m0"), 16),
+    "mid_ue8m0_bm128": (MID.with_(mode="fp8_ue8m0"), 128),
+    "padded_ue8m0": (W.Workload("pad", T=96, H=400, I=200, E=8, top_k=3, mode="fp8_ue8m0", Hp=512, Ip=256), 32),
+    "stream_ue8m0_bm128": (STREAM.with_(mode="fp8_ue8m0"), 128),
+    "short_k_ue8m0_bm128": (SHORT_K.with_(mode="fp8_ue8m0"), 128),
+    "short_k_ue8m0_bm16": (SHORT_K.with_(T=512, mode="fp8_ue8m0"), 16),
 }
 
 
@@ -113,7 +121,7 @@ def test_forward_with_row_strides():
     assert_rows_close(bf16_to_f32(out), _oracle(wl, x, lg), wl.mode, "strided")
 
 
-@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
 def test_forward_zero_input(mode):
     wl = MID.with_(T=33, mode=mode)
     cfg = M.make_cfg(wl.E, wl.top_k, mode, wl.H, wl.I, block_m=16)
@@ -134,7 +142,7 @@ def test_forward_zero_tokens():
     assert out.shape == (0, wl.H)
 
 
-@pytest.mark.parametrize("mode", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
 def test_forward_repeatable_and_equal_to_stages(mode):
     """Two runs give identical bits, and moe_forward equals the stage entry
     points called one by one."""

@@ -47,7 +47,8 @@ def _weights(cfg, wl):
 
 
 @pytest.mark.parametrize("name", ["decode_fp8", "prefill_fp8", "skewed_padded_fp8", "prefill_mxfp4", "tp4_decode_fp8",
-                                  "tp8_prefill_fp8", "tp4_prefill_mxfp4", "shared_expert_fp8", "shared_expert_mxfp4"])
+                                  "tp8_prefill_fp8", "tp4_prefill_mxfp4", "shared_expert_fp8", "shared_expert_mxfp4",
+                                  "decode_fp8_ue8m0", "prefill_fp8_ue8m0"])
 def test_fullsize_sampled(name):
     wl = W.WORKLOADS[name]
     bm = M.pick_block_m(wl.T, wl.E, wl.top_k)

@@ -35,7 +35,7 @@ class Workload:
     I: int
     E: int
     top_k: int
-    mode: str  # "fp8" or "mxfp4"
+    mode: str  # "fp8", "fp8_ue8m0" or "mxfp4"
     Hp: int = 0
     Ip: int = 0
     swiglu_limit: float = 10.0
@@ -97,6 +97,10 @@ WORKLOADS = {
                                   outlier_frac=0.01),
     "shared_expert_mxfp4": Workload("shared_expert_mxfp4", T=64, H=4096, I=1024, E=1, top_k=1,
                                     mode="mxfp4"),
+    # block FP8 with UE8M0 (power-of-two) weight and activation scales
+    "decode_fp8_ue8m0": Workload("decode_fp8_ue8m0", T=64, H=4096, I=1024, E=288, top_k=8, mode="fp8_ue8m0"),
+    "prefill_fp8_ue8m0": Workload("prefill_fp8_ue8m0", T=4096, H=4096, I=1024, E=288, top_k=8,
+                                  mode="fp8_ue8m0", outlier_frac=0.01),
 }
 
 
