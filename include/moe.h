@@ -123,7 +123,10 @@ moe_status_t moe_validate_cfg(const moe_cfg_t* cfg);
 int32_t moe_max_blocks(int32_t num_pairs, int32_t num_experts, int32_t block_m);
 
 /* Bytes of scratch that moe_forward needs for up to T_max tokens (0 if the
- * configuration is invalid).  Also enough for moe_grouped_gemm2_combine. */
+ * configuration is invalid; non-decreasing in T_max).  Also enough for
+ * moe_grouped_gemm2_combine.  The per-pair fp32 GEMM2 rows it holds are
+ * capped near 1 GiB: larger batches run GEMM2 and the combine in column
+ * chunks over one reused buffer. */
 size_t moe_workspace_bytes(const moe_cfg_t* cfg, int32_t T_max);
 
 /* Sizes in bytes of the intermediate aq / as buffers (rows = max_blocks *

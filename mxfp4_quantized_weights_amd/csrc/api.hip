@@ -101,7 +101,7 @@ Layout layout_for(const moe_cfg_t* c, int32_t T) {
   L.xs = align_up(T * scale_row_bytes(m, Hp));
   L.aq = align_up(rows * code_row_bytes(m, Ip));
   L.as = align_up(rows * scale_row_bytes(m, Ip));
-  L.y = align_up(P * Hp * 4);
+  L.y = align_up(moe::y_reserve_bytes(P, Hp));
   L.total = L.ids + L.wts + L.sorted + L.bexp + L.offs + L.npp + L.xq + L.xs + L.aq + L.as + L.y;
   return L;
 }
@@ -158,6 +158,28 @@ moe::GemmArgs gemm2_args(const moe_cfg_t* c, int32_t T, const void* aq, const vo
   a.y = y;
   a.topk_w = topk_w;
   return a;
+}
+
+// GEMM2 and the combine, one column chunk of y at a time (see y_chunk_cols).
+hipError_t gemm2_and_combine(const moe_cfg_t* c, int32_t T, moe::GemmArgs a, int32_t nb, void* out_bf16,
+                             int64_t ld_out, hipStream_t s) {
+  const int64_t P = (int64_t)T * c->top_k;
+  const int Hp = c->pad.hidden_padded, H = c->pad.hidden;
+  const int64_t W = moe::y_chunk_cols(P, Hp);
+  a.ldy = W;
+  for (int c0 = 0; c0 < Hp; c0 += (int)W) {
+    const int wc = (int)(Hp - c0 < W ? Hp - c0 : W);
+    a.nt0 = c0 / 256;
+    a.n_tiles = (wc + 255) / 256;
+    hipError_t e = moe::launch_gemm2(c->quant_mode, c->block_m, nb, a, s);
+    if (e != hipSuccess) return e;
+    const int cols = H - c0 < wc ? H - c0 : wc;
+    if (cols > 0) {
+      e = moe::launch_combine(a.y, T, c->top_k, c0, cols, W, (uint16_t*)out_bf16, ld_out, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -313,17 +335,13 @@ moe_status_t moe_grouped_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const vo
       !ws)
     return MOE_ERR_NULL;
   const int64_t P = (int64_t)T * cfg->top_k;
-  const size_t ybytes = align_up((size_t)P * cfg->pad.hidden_padded * 4);
+  const size_t ybytes = align_up((size_t)moe::y_reserve_bytes(P, cfg->pad.hidden_padded));
   if (ws_bytes < ybytes) return MOE_ERR_WORKSPACE;
   const int32_t nb = max_blocks(P, cfg->num_experts, cfg->block_m);
-  const int mode = cfg->quant_mode;
   hipStream_t s = as_stream(stream);
   float* y = (float*)ws;
   moe::GemmArgs a = gemm2_args(cfg, T, aq, as, sorted_ids, block_expert, num_post_padded, w2, w2_scale, y, topk_w);
-  hipError_t e = moe::launch_gemm2(mode, cfg->block_m, nb, a, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_combine(y, T, cfg->top_k, cfg->pad.hidden, cfg->pad.hidden_padded,
-                                        (uint16_t*)out_bf16, ld_out, s));
+  return hip_status(gemm2_and_combine(cfg, T, a, nb, out_bf16, ld_out, s));
 }
 
 moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, int64_t ld_x, const float* router_logits,
@@ -367,9 +385,7 @@ moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, in
   moe::GemmArgs a1 = gemm1_args(cfg, T, xq, xs, sorted, bexp, npp, w13, w13_scale, aq, as);
   if ((e = moe::launch_gemm1(mode, BM, nb, a1, s)) != hipSuccess) return MOE_ERR_HIP;
   moe::GemmArgs a2 = gemm2_args(cfg, T, aq, as, sorted, bexp, npp, w2, w2_scale, y, wts);
-  if ((e = moe::launch_gemm2(mode, BM, nb, a2, s)) != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_combine(y, T, k, cfg->pad.hidden, cfg->pad.hidden_padded, (uint16_t*)out_bf16, ld_out,
-                                        s));
+  return hip_status(gemm2_and_combine(cfg, T, a2, nb, out_bf16, ld_out, s));
 }
 
 }  // extern "C"

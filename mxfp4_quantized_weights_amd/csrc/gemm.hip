@@ -499,7 +499,8 @@ __device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&
 }
 
 // GEMM2 epilogue: y[pair, 4 consecutive columns] = routing weight * C per
-// lane and weight tile; routing weights from LDS.
+// lane and weight tile; routing weights from LDS.  y holds the columns of
+// this launch's N tiles (from nt0).
 template <int MT>
 __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&acc)[MT][4], const int32_t* sid,
                                                  const float* wts, int nt, int wt, int wn) {
@@ -510,7 +511,7 @@ __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&
     const int s = sid[t];
     if (s < p.num_pairs) {
       const float w = wts[t];
-      float* yrow = p.y + (int64_t)s * p.N + nt * 256 + 64 * wn + 4 * q;
+      float* yrow = p.y + (int64_t)s * p.ldy + (nt - p.nt0) * 256 + 64 * wn + 4 * q;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const v4f v = acc[m][j];
@@ -521,8 +522,9 @@ __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&
 }
 
 // Any K works.  Item metadata of item ii+1 is loaded when the loads of item ii
-// start; when an item has fewer than S-1 K blocks that is too late for the
-// ring's own waits to cover it, and the kernel then waits for it explicitly.
+// start; when an item has fewer than S K blocks that is too late for the
+// ring's own waits to cover it (the S-1 K blocks of the prologue are issued
+// without waits), and the kernel then waits for it explicitly.
 template <int MODE, int BM, bool G1, int S>
 __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(GemmArgs p) {
   using R = Ring<MODE, BM>;
@@ -571,9 +573,12 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   const int KB = p.K / 128;
   const int NT16 = p.N / 16;
   const int total = n_my * KB;
-  const bool short_items = KB < S - 1;
+  // Items of fewer than S K blocks finish inside the prologue (which issues
+  // S-1 K blocks without waiting) or within S-1 steps of the next item's
+  // metadata loads: their metadata is waited for explicitly.
+  const bool short_items = KB < S;
   auto item_m = [&](int ii) { return (first + ii * nw) / p.n_tiles; };
-  auto item_nt = [&](int ii) { return (first + ii * nw) % p.n_tiles; };
+  auto item_nt = [&](int ii) { return p.nt0 + (first + ii * nw) % p.n_tiles; };
 
   // sorted pair ids of item ii -> ids_lds[ii % NB] (waves 0 .. NI-1), its
   // block's expert -> exp_lds[ii % NB] (lane 0 of the last wave)
@@ -824,31 +829,32 @@ hipError_t launch_gemm2(int mode, int block_m, int nb, const GemmArgs& a, hipStr
   }
 }
 
-// out[t, h] = bf16(sum_j y[t*k + j, h]) with the slot sum in order j = 0..k-1.
-// 8 columns per thread (two 16-byte non-temporal loads per slot: y is read
-// once); the 8 bf16 results go out as one 16-byte store when the row stride
-// allows it.  Columns h .. h+7 stay inside the padded row (Hp is a multiple of
-// 128), only those below H are stored.
+// out[t, c0 + h] = bf16(sum_j y[t*k + j, h]) with the slot sum in order
+// j = 0..k-1, for h < cols (a column chunk of the output).  8 columns per
+// thread (two 16-byte non-temporal loads per slot: y is read once); the 8
+// bf16 results go out as one 16-byte store when the row stride allows it.
+// Columns h .. h+7 stay inside the y rows GEMM2 wrote (the chunk width is a
+// multiple of 256, or all Hp), only those below `cols` are stored.
 __device__ __forceinline__ float4 load_nt4(const float* p) {
   typedef float f4 __attribute__((ext_vector_type(4)));
   const f4 v = __builtin_nontemporal_load((const f4*)p);
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int k, int H, int Hp,
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int k, int cols, int64_t ldy,
                                                       uint16_t* __restrict__ out, int64_t ld_out, int vec_store) {
   const int t = blockIdx.y;
   const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (h >= H) return;
-  const float* base = y + (int64_t)t * k * Hp + h;
+  if (h >= cols) return;
+  const float* base = y + (int64_t)t * k * ldy + h;
   float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   for (int j = 0; j < k; ++j) {
-    const float4 v0 = load_nt4(base + (int64_t)j * Hp), v1 = load_nt4(base + (int64_t)j * Hp + 4);
+    const float4 v0 = load_nt4(base + (int64_t)j * ldy), v1 = load_nt4(base + (int64_t)j * ldy + 4);
     a[0] += v0.x; a[1] += v0.y; a[2] += v0.z; a[3] += v0.w;
     a[4] += v1.x; a[5] += v1.y; a[6] += v1.z; a[7] += v1.w;
   }
   uint16_t* o = out + (int64_t)t * ld_out + h;
-  if (vec_store && h + 8 <= H) {
+  if (vec_store && h + 8 <= cols) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(a[2 * i]) | ((uint32_t)f32_to_bf16(a[2 * i + 1]) << 16);
@@ -856,17 +862,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (h + i < H) o[i] = f32_to_bf16(a[i]);
+      if (h + i < cols) o[i] = f32_to_bf16(a[i]);
   }
 }
 
-hipError_t launch_combine(const float* y, int T, int k, int H, int Hp, uint16_t* out, int64_t ld_out,
-                          hipStream_t s) {
-  if (T <= 0) return hipSuccess;
+hipError_t launch_combine(const float* y, int T, int k, int c0, int cols, int64_t ldy, uint16_t* out,
+                          int64_t ld_out, hipStream_t s) {
+  if (T <= 0 || cols <= 0) return hipSuccess;
+  uint16_t* o = out + c0;
   // 16-byte stores need every row start 16-byte aligned
-  const int vec = ((uintptr_t)out % 16 == 0) && (ld_out % 8 == 0);
-  dim3 grid((unsigned)((H + 2047) / 2048), (unsigned)T), block(256);
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, y, k, H, Hp, out, ld_out, vec);
+  const int vec = ((uintptr_t)o % 16 == 0) && (ld_out % 8 == 0);
+  dim3 grid((unsigned)((cols + 2047) / 2048), (unsigned)T), block(256);
+  hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, y, k, cols, ldy, o, ld_out, vec);
   return hipGetLastError();
 }
 

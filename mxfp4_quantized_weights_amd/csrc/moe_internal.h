@@ -56,14 +56,43 @@ struct GemmArgs {
   void* as;
   int32_t Ip;
   float limit;
-  float* y;               // GEMM2 output: weighted per-pair rows [P, N]
+  float* y;               // GEMM2 output: weighted per-pair rows [P, ldy], columns nt0*256 ..
   const float* topk_w;    // [P]
+  int32_t nt0;            // GEMM2: first 256-column N tile of this launch (items cover n_tiles tiles)
+  int64_t ldy;            // GEMM2: row stride of y in floats
 };
+
+// Columns of the per-pair GEMM2 rows y kept at once: all Hp when P * Hp
+// fp32 values fit in kYChunkBytes, else the largest multiple of 256 that
+// does (at least 256).  GEMM2 and the combine then run once per column chunk
+// on the same y buffer, which bounds the workspace of very large batches.
+// Chunks cost time (each re-runs GEMM2's item list and its tail, and the
+// memory-side cache does not keep a 64-128 MiB chunk between GEMM2 and the
+// combine), so the cap is set high: a 4096-token, 288-expert top-8 layer
+// (512 MiB of y) runs in one piece.
+#ifndef MOE_Y_CHUNK_BYTES
+#define MOE_Y_CHUNK_BYTES (1ll << 30)
+#endif
+constexpr int64_t kYChunkBytes = MOE_Y_CHUNK_BYTES;
+inline int64_t y_chunk_cols(int64_t pairs, int64_t Hp) {
+  if (pairs <= 0 || pairs * Hp * 4 <= kYChunkBytes) return Hp;
+  int64_t w = kYChunkBytes / (pairs * 4) / 256 * 256;
+  return w < 256 ? 256 : (w > Hp ? Hp : w);
+}
+// Bytes reserved for y: at least pairs * y_chunk_cols * 4, and non-decreasing
+// in `pairs`, so a workspace sized for T_max tokens fits every T <= T_max.
+inline int64_t y_reserve_bytes(int64_t pairs, int64_t Hp) {
+  const int64_t full = pairs * Hp * 4;
+  const int64_t capped = full < kYChunkBytes ? full : kYChunkBytes;
+  const int64_t used = pairs * y_chunk_cols(pairs, Hp) * 4;
+  return used > capped ? used : capped;
+}
 
 hipError_t launch_gemm1(int mode, int block_m, int nb, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2(int mode, int block_m, int nb, const GemmArgs& a, hipStream_t s);
 
-hipError_t launch_combine(const float* y, int T, int k, int H, int Hp, uint16_t* out, int64_t ld_out,
-                          hipStream_t s);
+// out[t, c0 + h] for h < cols from y rows [T*k, ldy] (pair t*k + j).
+hipError_t launch_combine(const float* y, int T, int k, int c0, int cols, int64_t ldy, uint16_t* out,
+                          int64_t ld_out, hipStream_t s);
 
 }  // namespace moe

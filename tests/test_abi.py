@@ -202,6 +202,13 @@ def test_block_and_buffer_sizes():
     # workspace grows with T and covers the GEMM2 rows for gemm2_combine
     assert M.workspace_bytes(cfg(), 1) < M.workspace_bytes(cfg(), 64) < M.workspace_bytes(cfg(), 4096)
     assert M.workspace_bytes(cfg(), 64) >= 64 * 8 * 4096 * 4
+    # ... never shrinks as T grows (a workspace for T_max serves every T <= T_max),
+    # and large batches keep the per-pair rows in column chunks of a capped buffer
+    for q in ("fp8", "mxfp4", "fp8_ue8m0"):
+        c = cfg(quant=q, block_m=128)
+        sizes = [M.workspace_bytes(c, T) for T in range(1, 40000, 97)]
+        assert all(b >= a for a, b in zip(sizes, sizes[1:]))
+    assert M.workspace_bytes(cfg(block_m=128), 16384) < 16384 * 8 * 4096 * 4
 
 
 def test_pick_block_m():

@@ -65,6 +65,10 @@ TINY = W.WORKLOADS["tiny_fp8"]
 MID = W.Workload("mid", T=200, H=512, I=384, E=16, top_k=4, mode="fp8", outlier_frac=0.01)
 STREAM = W.Workload("stream", T=2048, H=1536, I=1024, E=8, top_k=4, mode="fp8", outlier_frac=0.01)
 SHORT_K = W.Workload("short_k", T=2048, H=2048, I=128, E=8, top_k=4, mode="fp8", outlier_frac=0.01)
+# more per-pair GEMM2 rows than one y chunk holds (P * Hp * 4 > 1 GiB):
+# GEMM2 + combine run per column chunk (2048 columns, then a ragged
+# 128-column tail of which 52 are real)
+CHUNKED = W.Workload("chunked", T=16384, H=2100, I=256, E=8, top_k=8, mode="fp8", Hp=2176, outlier_frac=0.01)
 
 CASES = {
     "tiny_fp8": (TINY, None),
@@ -94,6 +98,13 @@ CASES = {
     "short_k_fp8_bm128": (SHORT_K, 128),
     "short_k_fp8_bm16": (SHORT_K.with_(T=512), 16),
     "short_k_mxfp4_bm128": (SHORT_K.with_(mode="mxfp4"), 128),
+    # items of exactly S-1 K blocks (S = ring depth: 3 for FP8 at block_m
+    # 64/128, 4 at 16/32, 5 for MX) with many items per workgroup: the first
+    # item ends inside the ring's prologue
+    "ring_edge_fp8_bm128": (W.Workload("edge", T=2048, H=256, I=256, E=8, top_k=8, mode="fp8"), 128),
+    "ring_edge_fp8_bm16": (W.Workload("edge", T=2048, H=384, I=384, E=8, top_k=8, mode="fp8"), 16),
+    "ring_edge_mxfp4_bm64": (W.Workload("edge", T=2048, H=512, I=512, E=8, top_k=8, mode="mxfp4"), 64),
+    "ring_edge_ue8m0_bm64": (W.Workload("edge", T=2048, H=256, I=256, E=8, top_k=8, mode="fp8_ue8m0"), 64),
     # block FP8 with UE8M0 (power-of-two) scales
     "tiny_ue8m0": (TINY.with_(mode="fp8_ue8m0"), None),
     "mid_ue8m0_bm16": (MID.with_(mode="fp8_ue8m0"), 16),
@@ -119,6 +130,30 @@ def test_forward_with_row_strides():
     log(f"forward strided: {W.describe(wl)}")
     _, _, x, lg, out = _run(wl, 16, ld_pad=72)
     assert_rows_close(bf16_to_f32(out), _oracle(wl, x, lg), wl.mode, "strided")
+
+
+@pytest.mark.parametrize("mode,bm", [("fp8", 128), ("mxfp4", 64), ("fp8_ue8m0", 128)])
+def test_chunked_gemm2_combine(mode, bm):
+    """Column-chunked GEMM2 + combine (with an output row stride): moe_forward
+    equals the stage entry points bit for bit, and sampled rows (first, last,
+    and spread over the batch) match the oracle."""
+    wl = CHUNKED.with_(mode=mode)
+    log(f"chunked: {W.describe(wl)} block_m={bm}")
+    cfg, ew, x, lg, out = _run(wl, bm, ld_pad=40)
+    xd, lgd = x.cuda(), lg.cuda()
+    ids, wts = M.moe_route_topk(lgd, wl.top_k)
+    sid, bexp, offs, npp = M.moe_permute_align(ids, wl.E, bm)
+    xq, xs = M.moe_quant_act(xd, wl.Hp, wl.mode)
+    aq, as_ = M.moe_grouped_gemm1_swiglu(cfg, wl.T, xq, xs, sid, bexp, npp, ew.w13, ew.w13_scale)
+    out3 = M.moe_grouped_gemm2_combine(cfg, wl.T, aq, as_, sid, bexp, npp, ew.w2, ew.w2_scale, wts)
+    torch.cuda.synchronize()
+    assert torch.equal(out.contiguous().view(torch.int16), out3.view(torch.int16))
+    toks = sorted({0, wl.T - 1, *range(5, wl.T, 2711)})
+    Q = oracle_weights_cpu(wl)
+    ref, st = O.moe_forward(x.float().numpy(), lg.numpy(), Q, wl.top_k, wl.swiglu_limit, wl.H, wl.I, tokens=toks,
+                            return_stages=True)
+    tie = requant_tie_allowance(st, Q, wl.mode, wl.H)
+    assert_rows_close(bf16_to_f32(out)[toks], ref, wl.mode, "chunked", allowance=tie)
 
 
 @pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
