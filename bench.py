@@ -185,7 +185,10 @@ def main():
     nbytes = algorithmic_bytes(wl, ids_h, M)
     kern = {}
     if not args.no_breakdown:
-        names = ["route_topk", "permute_align", "quant_act", "gemm1_swiglu", "gemm2_combine"]
+        # the stages moe_forward runs: the front end (routing, permutation,
+        # quantisation of x; one launch for small batches), GEMM1, GEMM2 +
+        # combine
+        names = ["front_end", "gemm1_swiglu", "gemm2_combine"]
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
         aq_b, as_b = M.intermediate_bytes(cfg, wl.T)
         nb = M.max_blocks(wl.T * wl.top_k, wl.E, bm)
@@ -197,37 +200,24 @@ def main():
         lib = M.lib()
         cfgp = ctypes.byref(cfg)
         sp = stream.cuda_stream
-        if wl.mode == "fp8":
-            xq = torch.empty(wl.T, wl.Hp, dtype=torch.uint8, device=dev)
-            xs = torch.empty(wl.T, wl.Hp // 128, dtype=torch.float32, device=dev)
-        elif wl.mode == "fp8_ue8m0":
-            xq = torch.empty(wl.T, wl.Hp, dtype=torch.uint8, device=dev)
-            xs = torch.empty(wl.T, M.e8_scale_ld(wl.Hp), dtype=torch.uint8, device=dev)
-        else:
-            xq = torch.empty(wl.T, wl.Hp // 2, dtype=torch.uint8, device=dev)
-            xs = torch.empty(wl.T, wl.Hp // 32, dtype=torch.uint8, device=dev)
+        xq, xs = M._act_buffers(cfg.quant_mode, wl.T, wl.Hp, dev)
         aq = torch.empty(aq_b, dtype=torch.uint8, device=dev)
         as_ = torch.empty(as_b, dtype=torch.uint8, device=dev)
-        qm = cfg.quant_mode
 
         def staged(evs):
             evs[0].record(stream)
-            lib.moe_route_topk(lg.data_ptr(), wl.T, wl.E, wl.top_k, ids.data_ptr(), wts.data_ptr(), sp)
+            lib.moe_route_permute_quant(cfgp, wl.T, lg.data_ptr(), x.data_ptr(), wl.H, ids.data_ptr(),
+                                        wts.data_ptr(), sid.data_ptr(), bexp.data_ptr(), offs.data_ptr(),
+                                        npp.data_ptr(), xq.data_ptr(), xs.data_ptr(), sp)
             evs[1].record(stream)
-            lib.moe_permute_align(ids.data_ptr(), wl.T, wl.top_k, wl.E, bm, sid.data_ptr(), bexp.data_ptr(),
-                                  offs.data_ptr(), npp.data_ptr(), sp)
-            evs[2].record(stream)
-            lib.moe_quant_act(x.data_ptr(), M.MOE_DTYPE_BF16, wl.T, wl.H, wl.H, wl.Hp, qm, xq.data_ptr(),
-                              xs.data_ptr(), sp)
-            evs[3].record(stream)
             lib.moe_grouped_gemm1_swiglu(cfgp, wl.T, xq.data_ptr(), xs.data_ptr(), sid.data_ptr(), bexp.data_ptr(),
                                          npp.data_ptr(), w13.data_ptr(), s13.data_ptr(), aq.data_ptr(),
                                          as_.data_ptr(), sp)
-            evs[4].record(stream)
+            evs[2].record(stream)
             lib.moe_grouped_gemm2_combine(cfgp, wl.T, aq.data_ptr(), as_.data_ptr(), sid.data_ptr(),
                                           bexp.data_ptr(), npp.data_ptr(), w2.data_ptr(), s2.data_ptr(),
                                           wts.data_ptr(), out.data_ptr(), wl.H, ws.data_ptr(), ws.numel(), sp)
-            evs[5].record(stream)
+            evs[3].record(stream)
 
         for i in range(min(args.warmup, args.steps)):
             staged(ev[i])

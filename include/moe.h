@@ -181,6 +181,19 @@ moe_status_t moe_quant_act(const void* in, int32_t in_dtype, int32_t rows, int32
                            int64_t ld_in, int32_t cols_padded, int32_t quant_mode, void* q,
                            void* scales, void* stream);
 
+/* Steps 1-3 of the layer in as few launches as the batch allows: top-k
+ * routing, the padded permutation and the quantisation of x, with exactly
+ * the results of moe_route_topk + moe_permute_align + moe_quant_act (x bf16,
+ * hidden = cfg->pad.hidden valid columns, row stride ld_x, quantised to
+ * cfg->pad.hidden_padded columns in cfg->quant_mode).  Up to 64 tokens it
+ * is two launches: routing and quantisation side by side, then a
+ * one-workgroup permutation.  Outputs as the three entry points (sizes from
+ * moe_max_blocks, moe_quant_act); all are device buffers of the caller. */
+moe_status_t moe_route_permute_quant(const moe_cfg_t* cfg, int32_t T, const float* router_logits,
+                                     const void* x_bf16, int64_t ld_x, int32_t* ids, float* weights,
+                                     int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                                     int32_t* num_post_padded, void* xq, void* xs, void* stream);
+
 /* Offline weight quantisation into the CANONICAL layout.  w: f32 [E, N, K]
  * row-major (already zero-padded).
  *   FP8:   N % 128 == 0, K % 128 == 0; q u8 [E, N, K]; scales f32

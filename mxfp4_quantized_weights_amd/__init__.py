@@ -82,6 +82,7 @@ _SIGS = {
     "moe_permute_align": (ctypes.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]),
     "moe_quant_act": (ctypes.c_int, [_P, _I32, _I32, _I32, _I64, _I32, _I32, _P, _P, _P]),
     "moe_quant_weights": (ctypes.c_int, [_I32, _P, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_route_permute_quant": (ctypes.c_int, [_CFGP, _I32, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_preshuffled_bytes": (ctypes.c_int, [_CFGP, _I32, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "moe_preshuffle_weights": (ctypes.c_int, [_CFGP, _I32, _P, _P, _P, _P, _P]),
     "moe_grouped_gemm1_swiglu": (ctypes.c_int, [_CFGP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -229,18 +230,47 @@ def moe_quant_act(x: torch.Tensor, cols_padded: int, quant: str | int, stream=No
     dt = {torch.bfloat16: MOE_DTYPE_BF16, torch.float32: MOE_DTYPE_F32}.get(x.dtype)
     if dt is None:
         raise ValueError("x must be bf16 or f32")
-    if qm == MOE_QUANT_FP8_BLOCK:
-        q = torch.empty(rows, cols_padded, dtype=torch.uint8, device=x.device)
-        s = torch.empty(rows, cols_padded // 128, dtype=torch.float32, device=x.device)
-    elif qm == MOE_QUANT_FP8_UE8M0:
-        q = torch.empty(rows, cols_padded, dtype=torch.uint8, device=x.device)
-        s = torch.empty(rows, e8_scale_ld(cols_padded), dtype=torch.uint8, device=x.device)
-    else:
-        q = torch.empty(rows, cols_padded // 2, dtype=torch.uint8, device=x.device)
-        s = torch.empty(rows, cols_padded // 32, dtype=torch.uint8, device=x.device)
+    q, s = _act_buffers(qm, rows, cols_padded, x.device)
     _check(_lib.moe_quant_act(_dev(x, None, "x", contiguous=False), dt, rows, cols, x.stride(0), cols_padded,
                               qm, q.data_ptr(), s.data_ptr(), _stream(stream)), "moe_quant_act")
     return q, s
+
+
+def _act_buffers(qm: int, rows: int, cols_padded: int, device):
+    """Quantised-activation outputs of moe_quant_act's layout."""
+    if qm == MOE_QUANT_FP8_BLOCK:
+        return (torch.empty(rows, cols_padded, dtype=torch.uint8, device=device),
+                torch.empty(rows, cols_padded // 128, dtype=torch.float32, device=device))
+    if qm == MOE_QUANT_FP8_UE8M0:
+        return (torch.empty(rows, cols_padded, dtype=torch.uint8, device=device),
+                torch.empty(rows, e8_scale_ld(cols_padded), dtype=torch.uint8, device=device))
+    return (torch.empty(rows, cols_padded // 2, dtype=torch.uint8, device=device),
+            torch.empty(rows, cols_padded // 32, dtype=torch.uint8, device=device))
+
+
+def moe_route_permute_quant(cfg: MoeCfg, x: torch.Tensor, logits: torch.Tensor, stream=None):
+    """Routing + permutation + quantisation of bf16 x [T, H] in as few launches
+    as the batch allows.  -> (ids, weights, sorted_ids, block_expert,
+    expert_offsets, num_post_padded, xq, xs), as the three stage calls."""
+    T = x.shape[0]
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    E, k, bm = cfg.num_experts, cfg.top_k, cfg.block_m
+    dev = x.device
+    nb = max_blocks(T * k, E, bm)
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    sorted_ids = torch.empty(max(nb * bm, 1), dtype=torch.int32, device=dev)
+    block_expert = torch.empty(max(nb, 1), dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    npp = torch.empty(1, dtype=torch.int32, device=dev)
+    xq, xs = _act_buffers(cfg.quant_mode, T, cfg.pad.hidden_padded, dev)
+    _check(_lib.moe_route_permute_quant(ctypes.byref(cfg), T, _dev(logits, torch.float32, "router_logits"),
+                                        _dev(x, torch.bfloat16, "x", contiguous=False), x.stride(0),
+                                        ids.data_ptr(), w.data_ptr(), sorted_ids.data_ptr(), block_expert.data_ptr(),
+                                        offsets.data_ptr(), npp.data_ptr(), xq.data_ptr(), xs.data_ptr(),
+                                        _stream(stream)), "moe_route_permute_quant")
+    return ids, w, sorted_ids[:nb * bm], block_expert[:nb], offsets, npp, xq, xs
 
 
 def moe_quant_weights(w: torch.Tensor, quant: str | int, stream=None):

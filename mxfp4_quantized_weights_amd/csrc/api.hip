@@ -160,6 +160,23 @@ moe::GemmArgs gemm2_args(const moe_cfg_t* c, int32_t T, const void* aq, const vo
   return a;
 }
 
+// Routing, permutation and quantisation of x: two launches for decode-sized
+// batches, else the three stage kernels.
+hipError_t front_end(const moe_cfg_t* c, int32_t T, const float* logits, const void* x, int64_t ld_x, int32_t* ids,
+                     float* wts, int32_t* sorted, int32_t* bexp, int32_t* offs, int32_t* npp, void* xq, void* xs,
+                     hipStream_t s) {
+  const int E = c->num_experts, k = c->top_k, BM = c->block_m;
+  const int32_t nb = max_blocks((int64_t)T * k, E, BM);
+  const int H = c->pad.hidden, Hp = c->pad.hidden_padded, mode = c->quant_mode;
+  if (moe::front_small_ok(T, E, k))
+    return moe::launch_front_small(logits, T, E, k, ids, wts, BM, nb, sorted, bexp, offs, npp, x, H, ld_x, Hp, mode,
+                                   xq, xs, s);
+  hipError_t e = moe::launch_route_topk(logits, T, E, k, ids, wts, s);
+  if (e != hipSuccess) return e;
+  if ((e = moe::launch_permute_align(ids, T, k, E, BM, nb, sorted, bexp, offs, npp, s)) != hipSuccess) return e;
+  return moe::launch_quant_rows(x, true, T, H, ld_x, Hp, mode, xq, xs, s);
+}
+
 // GEMM2 and the combine, one column chunk of y at a time (see y_chunk_cols).
 hipError_t gemm2_and_combine(const moe_cfg_t* c, int32_t T, moe::GemmArgs a, int32_t nb, void* out_bf16,
                              int64_t ld_out, hipStream_t s) {
@@ -257,6 +274,22 @@ moe_status_t moe_quant_act(const void* in, int32_t in_dtype, int32_t rows, int32
   if (!in || !q || !scales) return MOE_ERR_NULL;
   return hip_status(moe::launch_quant_rows(in, in_dtype == MOE_DTYPE_BF16, rows, cols, ld_in, cols_padded,
                                            quant_mode, q, scales, as_stream(stream)));
+}
+
+moe_status_t moe_route_permute_quant(const moe_cfg_t* cfg, int32_t T, const float* router_logits,
+                                     const void* x_bf16, int64_t ld_x, int32_t* ids, float* weights,
+                                     int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                                     int32_t* num_post_padded, void* xq, void* xs, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
+  if (ld_x < cfg->pad.hidden) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!router_logits || !x_bf16 || !ids || !weights || !sorted_ids || !block_expert || !expert_offsets ||
+      !num_post_padded || !xq || !xs)
+    return MOE_ERR_NULL;
+  return hip_status(front_end(cfg, T, router_logits, x_bf16, ld_x, ids, weights, sorted_ids, block_expert,
+                              expert_offsets, num_post_padded, xq, xs, as_stream(stream)));
 }
 
 moe_status_t moe_quant_weights(int32_t quant_mode, const float* w, int32_t E, int32_t N, int32_t K, void* q,
@@ -376,10 +409,7 @@ moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, in
   const int32_t nb = max_blocks(P, E, BM);
   const int mode = cfg->quant_mode;
   hipError_t e;
-  if ((e = moe::launch_route_topk(router_logits, T, E, k, ids, wts, s)) != hipSuccess) return MOE_ERR_HIP;
-  if ((e = moe::launch_permute_align(ids, T, k, E, BM, nb, sorted, bexp, offs, npp, s)) != hipSuccess)
-    return MOE_ERR_HIP;
-  if ((e = moe::launch_quant_rows(x_bf16, true, T, cfg->pad.hidden, ld_x, cfg->pad.hidden_padded, mode, xq, xs, s)) !=
+  if ((e = front_end(cfg, T, router_logits, x_bf16, ld_x, ids, wts, sorted, bexp, offs, npp, xq, xs, s)) !=
       hipSuccess)
     return MOE_ERR_HIP;
   moe::GemmArgs a1 = gemm1_args(cfg, T, xq, xs, sorted, bexp, npp, w13, w13_scale, aq, as);

@@ -235,9 +235,13 @@ __device__ __forceinline__ v4f mfma_fp4_scaled_t(const v8i& w, const v8i& t, v4f
 
 // One K block of the wave's 4 token tiles x 4 weight tiles from slot `slot`.
 // acc[m][j][i] = C[token (wt*4+m)*16 + lane%16][weight row 16*tile_j + 4*(lane/16) + i].
+// Only the first `mv` token tiles hold real rows (an expert's last block is
+// padded); the others are skipped (mv is wave-uniform, 1..MT), except in the
+// scheduled f16 path of 4 token tiles.
 template <int MODE, int BM, bool G1>
 __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t* ws, const int (&tiles)[4], int wt,
-                                             int kb, float sw0, float sw1, v4f (&acc)[Ring<MODE, BM>::MT][4]) {
+                                             int kb, float sw0, float sw1, int mv,
+                                             v4f (&acc)[Ring<MODE, BM>::MT][4]) {
   using R = Ring<MODE, BM>;
   const int lane = threadIdx.x & 63;
   const uint8_t* wl = slot + R::W_OFF + lane * 16;
@@ -261,9 +265,11 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const v8i t = lds_frag16(tl + m * R::TILE);
+      if (m < mv) {
+        const v8i t = lds_frag16(tl + m * R::TILE);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[m][j] = mfma_fp4_scaled_t<0>(w[j], t, acc[m][j], sw[j], st[m]);
+        for (int j = 0; j < 4; ++j) acc[m][j] = mfma_fp4_scaled_t<0>(w[j], t, acc[m][j], sw[j], st[m]);
+      }
     }
   } else {
     // token scales of tiles m = 0..3 (row lane % 16): fp32, or E8M0 bytes
@@ -292,9 +298,11 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
       for (int j = 0; j < 4; ++j) w[j] = lds_frag32(wl + tiles[j] * R::TILE);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const v8i t = lds_tok32(tt + m * R::TILE, lane);
+        if (m < mv) {
+          const v8i t = lds_tok32(tt + m * R::TILE, lane);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[m][j] = mfma_fp8_scaled(w[j], t, acc[m][j], swb, tsb[m]);
+          for (int j = 0; j < 4; ++j) acc[m][j] = mfma_fp8_scaled(w[j], t, acc[m][j], swb, tsb[m]);
+        }
       }
     } else if constexpr (MODE == kGemmFp8) {
       v8i w[4];
@@ -302,31 +310,36 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
       for (int j = 0; j < 4; ++j) w[j] = lds_frag32(wl + tiles[j] * R::TILE);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        const v8i t = lds_tok32(tt + m * R::TILE, lane);
+        if (m < mv) {
+          const v8i t = lds_tok32(tt + m * R::TILE, lane);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float s = tsc[m] * ((G1 && j >= 2) ? sw1 : sw0);
-          const v4f c = mfma_fp8(w[j], t, v4f{0.0f, 0.0f, 0.0f, 0.0f});
+          for (int j = 0; j < 4; ++j) {
+            const float s = tsc[m] * ((G1 && j >= 2) ? sw1 : sw0);
+            const v4f c = mfma_fp8(w[j], t, v4f{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(c[i], s, acc[m][j][i]);
+            for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(c[i], s, acc[m][j][i]);
+          }
         }
       }
     } else if constexpr (MT < 4) {
+      // plain order: every weight tile widened once, then the token tiles
       v8h wh[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) widen_fp8(lds_frag32(wl + tiles[j] * R::TILE), wh[j]);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        v8h th[4];
-        widen_fp8(lds_tok32(tt + m * R::TILE, lane), th);
+        if (m < mv) {
+          v8h th[4];
+          widen_fp8(lds_tok32(tt + m * R::TILE, lane), th);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float s = tsc[m] * ((G1 && j >= 2) ? sw1 : sw0);
-          v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          for (int j = 0; j < 4; ++j) {
+            const float s = tsc[m] * ((G1 && j >= 2) ? sw1 : sw0);
+            v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int k = 0; k < 4; ++k) c = mfma_f16(wh[j][k], th[k], c);
+            for (int k = 0; k < 4; ++k) c = mfma_f16(wh[j][k], th[k], c);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(c[i], s, acc[m][j][i]);
+            for (int i = 0; i < 4; ++i) acc[m][j][i] = fmaf(c[i], s, acc[m][j][i]);
+          }
         }
       }
     } else {
@@ -334,7 +347,9 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
       // token) tiles are visited in an order that needs a new operand only
       // every other tile, and each operand is widened during the MFMAs of the
       // tiles before its first use, so the MFMA and VALU pipes overlap.
-      // raw fragments are read from LDS two tiles before they are widened
+      // raw fragments are read from LDS two tiles before they are widened.
+      // All 4 token tiles are computed even when some are padding: branching
+      // inside this schedule costs more than the skipped tiles save.
       v8i wraw[4], traw[4];
       wraw[0] = lds_frag32(wl + tiles[0] * R::TILE);
       wraw[1] = lds_frag32(wl + tiles[1] * R::TILE);
@@ -669,12 +684,19 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
 #pragma unroll
     for (int j = 0; j < 4; ++j) tiles[j] = 4 * wn + j;
   }
-  int c_nt = 0, c_row0 = 0;
+  int c_nt = 0, c_row0 = 0, c_mv = MT;
   bool active = true;
   auto setup_compute = [&](int ii) {
     c_nt = item_nt(ii);
     c_row0 = item_m(ii) * BM;
     if constexpr (!G1) active = c_nt * 256 + 64 * wn < p.N;
+    // real rows are a prefix of the block: count the wave's token tiles
+    // that start with one
+    const int32_t* ids = ids_lds[ii % NB];
+    int mv = 0;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) mv += ids[wt * 64 + m * 16] < p.num_pairs ? 1 : 0;
+    c_mv = __builtin_amdgcn_readfirstlane(mv);
   };
 
   v4f acc[MT][4];
@@ -733,8 +755,8 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
     if constexpr (MODE == kGemmMx) {
       if ((c_kb & 3) == 0) c_ws = ws_buf[(c_grp++) % NWS];
     }
-    if (active)
-      ring_compute<MODE, BM, G1>(slot(std::integral_constant<int, d>{}), c_ws, tiles, wt, c_kb, sw0, sw1, acc);
+    if (active && c_mv > 0)
+      ring_compute<MODE, BM, G1>(slot(std::integral_constant<int, d>{}), c_ws, tiles, wt, c_kb, sw0, sw1, c_mv, acc);
     if (++c_kb == KB) {
       const int32_t* ids = ids_lds[c_ii % NB];
       if constexpr (G1) {

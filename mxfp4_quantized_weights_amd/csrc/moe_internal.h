@@ -25,6 +25,15 @@ hipError_t launch_permute_align(const int32_t* ids, int T, int k, int E, int blo
                                 int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets,
                                 int32_t* npp, hipStream_t s);
 
+// Routing, permutation and quantisation of bf16 x in two launches, for
+// batches where front_small_ok(T, E, k) holds (same results as the three
+// stage launchers for routing output, which never repeats an expert).
+bool front_small_ok(int T, int E, int k);
+hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t* ids, float* w, int block_m, int nb,
+                              int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets, int32_t* npp,
+                              const void* x_bf16, int H, int64_t ld_x, int Hp, int mode, void* xq, void* xs,
+                              hipStream_t s);
+
 // in_is_bf16: element type of `in`; rows x cols valid, row stride ld_in elements.
 hipError_t launch_quant_rows(const void* in, bool in_is_bf16, int64_t rows, int cols, int64_t ld_in,
                              int cols_padded, int mode, void* q, void* scales, hipStream_t s);

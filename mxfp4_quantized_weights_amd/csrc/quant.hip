@@ -18,113 +18,16 @@
 //                   q = RNE(v * 2^(127 - b)).
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_quant_rows.h"
 
 namespace moe {
 
-// Eight consecutive elements of one row as fp32 (zeros past `cols`).  VEC:
-// the row start and stride allow 16-byte loads.
-template <bool BF16, bool VEC>
-__device__ __forceinline__ void load8(const void* in, int64_t row, int64_t ld, int col, int cols, float (&v)[8]) {
-  if (BF16) {
-    const uint16_t* p = (const uint16_t*)in + row * ld + col;
-    if (VEC && col + 8 <= cols) {
-      const uint4 w = *(const uint4*)p;
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(u[i] << 16);
-        v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (col + i < cols) ? bf16_to_f32(p[i]) : 0.0f;
-    }
-  } else {
-    const float* p = (const float*)in + row * ld + col;
-    if (VEC && col + 8 <= cols) {
-      const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (col + i < cols) ? p[i] : 0.0f;
-    }
-  }
-}
-
-// A wave quantises four 128-column units (16 lanes each, 8 elements per
-// lane); a unit is one FP8 group or four MX groups of 4 lanes.
-// UE8M0 scale rows are e8_scale_ld(cols_padded) bytes long; the bytes past
-// the last group are written as zero.
 template <bool BF16, bool VEC, int MODE>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ in, int64_t rows, int cols,
                                                          int64_t ld_in, int cols_padded,
                                                          uint8_t* __restrict__ q, void* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
-  const int units = cols_padded / 128;
-  const int64_t total = rows * units;
-  const int64_t stride = (int64_t)gridDim.x * 16;
-  for (int64_t u = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4); u - (lane >> 4) < total;
-       u += stride) {
-    const bool live = u < total;
-    const int64_t row = live ? u / units : 0;
-    const int g = live ? (int)(u % units) : 0;
-    const int col = g * 128 + (lane & 15) * 8;
-    float v[8];
-    if (live) {
-      load8<BF16, VEC>(in, row, ld_in, col, cols, v);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-    }
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
-    if constexpr (MODE == kQuantFp8) {
-      a = group_max<16>(a);
-      uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      const float s = (a > 0.0f) ? a / kE4M3Max : 0.0f;
-      if (a > 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = fp8_quant(v[i], s);
-      }
-      if (live) {
-        *(uint2*)(q + row * (int64_t)cols_padded + col) =
-            make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
-        if ((lane & 15) == 0) ((float*)scales)[row * units + g] = s;
-      }
-    } else if constexpr (MODE == kQuantFp8E8) {
-      a = group_max<16>(a);
-      const uint32_t b = ue8m0_byte(a);
-      const float inv = e8m0_inverse(b);
-      uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (a > 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = fp8e8_quant(v[i], inv);
-      }
-      if (live) {
-        *(uint2*)(q + row * (int64_t)cols_padded + col) =
-            make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
-        const int64_t lds = (units + 3) / 4 * 4;
-        uint8_t* srow = (uint8_t*)scales + row * lds;
-        if ((lane & 15) == 0) srow[g] = (uint8_t)b;
-        if ((lane & 15) == 1 && g == units - 1) {
-          for (int i = units; i < lds; ++i) srow[i] = 0;
-        }
-      }
-    } else {
-      a = group_max<4>(a);
-      const uint32_t b = e8m0_byte(a);
-      const float inv = e8m0_inverse(b);
-      uint32_t w = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w |= mx_quant(v[i], inv) << (4 * i);
-      if (live) {
-        *(uint32_t*)(q + row * (int64_t)(cols_padded / 2) + col / 2) = w;
-        if ((lane & 3) == 0) ((uint8_t*)scales)[row * (int64_t)(cols_padded / 32) + col / 32] = (uint8_t)b;
-      }
-    }
-  }
+  quant_rows_body<BF16, VEC, MODE>(in, rows, cols, ld_in, cols_padded, q, scales,
+                                   (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), (int64_t)gridDim.x * 4);
 }
 
 template <bool BF16, bool VEC>

@@ -9,6 +9,7 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "moe_quant_rows.h"
 
 namespace moe {
 
@@ -42,16 +43,14 @@ __device__ __forceinline__ void wave_argmax(float& v, int& id) {
   id = __builtin_amdgcn_readlane(id, 63);
 }
 
-// One wave per token.  Each lane holds the logits of experts lane + 64*i;
-// k rounds of a wave-wide argmax pick the experts in slot order.  NaN logits
-// compare as -inf.  The softmax denominator is summed in slot order.
+// Top-k of one token by one wave.  Each lane holds the logits of experts
+// lane + 64*i; k rounds of a wave-wide argmax pick the experts in slot order.
+// NaN logits compare as -inf.  The softmax denominator is summed in slot
+// order.  Lane j < k writes slot j to ids[j], w[j] and, if given, ids2[j].
 template <int VPL>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
-                                                         int32_t* __restrict__ ids, float* __restrict__ w) {
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int32_t* ids, float* w,
+                                            int32_t* ids2) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
   float v[VPL];
   uint32_t avail = 0;
 #pragma unroll
@@ -88,9 +87,19 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   float sum = 0.0f;
   for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_e;
-    w[(size_t)t * k + lane] = ex / sum;
+    ids[lane] = my_e;
+    w[lane] = ex / sum;
+    if (ids2) ids2[lane] = my_e;
   }
+}
+
+// One wave per token.
+template <int VPL>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                         int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  route_token<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
@@ -173,17 +182,17 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The work of one workgroup: chunk `chunk` of `nchunks` (token chunks of Tc).
+// `ids` may point to global memory or to LDS.  perm_smem: permute_smem_bytes.
 template <int NW, int RW>
-__global__ __launch_bounds__(64 * NW) void permute_align_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                                int BM, int nb, int Tc,
-                                                                int32_t* __restrict__ sorted_ids,
-                                                                int32_t* __restrict__ block_expert,
-                                                                int32_t* __restrict__ offsets,
-                                                                int32_t* __restrict__ npp) {
+__device__ __forceinline__ void permute_align_body(const int32_t* ids, int T, int k, int E, int BM, int nb, int Tc,
+                                                   int chunk, int nchunks, int32_t* __restrict__ sorted_ids,
+                                                   int32_t* __restrict__ block_expert,
+                                                   int32_t* __restrict__ offsets, int32_t* __restrict__ npp,
+                                                   unsigned char* perm_smem) {
   constexpr int NT = 64 * NW;
   static_assert(NT >= 1024, "one thread per expert in the scan");
   static_assert(RW <= NW, "ranking waves are a subset");
-  extern __shared__ __align__(16) unsigned char perm_smem[];
   int32_t* before = (int32_t*)perm_smem;          // [E] pairs before the chunk; then the expert's pair count
   int32_t* after = before + E;                    // [E] pairs after the chunk; then the segment offset
   int32_t* cur = after + E;                       // [RW][E] per-wave chunk counts; then cursors
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(64 * NW) void permute_align_kernel(const int32_t* _
   int32_t* scratch = (int32_t*)(mask + RW * E * 2);  // [NW] scan partials + duplicate flag
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int P = T * k;
-  const int tb = min(T, (int)blockIdx.x * Tc), te = min(T, tb + Tc);
+  const int tb = min(T, chunk * Tc), te = min(T, tb + Tc);
   const int fb = tb * k, fe = te * k;
   const int Tw = (Tc + RW - 1) / RW;
   const int w_begin = min(te, tb + wave * Tw), w_end = min(te, w_begin + Tw);  // used by ranking waves
@@ -258,22 +267,22 @@ __global__ __launch_bounds__(64 * NW) void permute_align_kernel(const int32_t* _
     }
     before[e_own] = cnt;
     after[e_own] = off;
-    if (blockIdx.x == 0) offsets[e_own] = off;
+    if (chunk == 0) offsets[e_own] = off;
   }
-  if (blockIdx.x == 0 && tid == 0) {
+  if (chunk == 0 && tid == 0) {
     offsets[E] = total;
     *npp = total;
   }
   __syncthreads();
 
   // padding sentinels and block experts, one expert per wave of the grid
-  const int gw = blockIdx.x * NW + wave, n_waves = gridDim.x * NW;
+  const int gw = chunk * NW + wave, n_waves = nchunks * NW;
   for (int e = gw; e < E; e += n_waves) {
     const int c = before[e], o = after[e], p = ((c + BM - 1) / BM) * BM;
     for (int r = o + c + lane; r < o + p; r += 64) sorted_ids[r] = P;
     for (int b = o / BM + lane; b < (o + p) / BM; b += 64) block_expert[b] = e;
   }
-  const int gt = blockIdx.x * NT + tid, n_threads = gridDim.x * NT;
+  const int gt = chunk * NT + tid, n_threads = nchunks * NT;
   for (int r = total + gt; r < nb * BM; r += n_threads) sorted_ids[r] = P;
   for (int b = total / BM + gt; b < nb; b += n_threads) block_expert[b] = -1;
 
@@ -345,6 +354,20 @@ __global__ __launch_bounds__(64 * NW) void permute_align_kernel(const int32_t* _
   }
 }
 
+inline size_t permute_smem_bytes(int E) { return (size_t)(2 + 3 * kPermRankWaves) * E * 4 + (kPermWaves + 1) * 4; }
+
+template <int NW, int RW>
+__global__ __launch_bounds__(64 * NW) void permute_align_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                                int BM, int nb, int Tc,
+                                                                int32_t* __restrict__ sorted_ids,
+                                                                int32_t* __restrict__ block_expert,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ npp) {
+  extern __shared__ __align__(16) unsigned char perm_smem[];
+  permute_align_body<NW, RW>(ids, T, k, E, BM, nb, Tc, blockIdx.x, gridDim.x, sorted_ids, block_expert, offsets, npp,
+                             perm_smem);
+}
+
 hipError_t launch_permute_align(const int32_t* ids, int T, int k, int E, int block_m, int nb, int32_t* sorted_ids,
                                 int32_t* block_expert, int32_t* offsets, int32_t* npp, hipStream_t s) {
   constexpr int NW = kPermWaves, RW = kPermRankWaves;
@@ -352,9 +375,129 @@ hipError_t launch_permute_align(const int32_t* ids, int T, int k, int E, int blo
   int chunks = (T + RW * 64 - 1) / (RW * 64);
   chunks = chunks < 1 ? 1 : (chunks > kPermMaxChunks ? kPermMaxChunks : chunks);
   const int Tc = (T + chunks - 1) / chunks;
-  const size_t smem = (size_t)(2 + 3 * RW) * E * 4 + (NW + 1) * 4;  // <= 57412 B for E <= 1024
+  const size_t smem = permute_smem_bytes(E);  // <= 57412 B for E <= 1024
   hipLaunchKernelGGL((permute_align_kernel<NW, RW>), dim3(chunks), dim3(64 * NW), smem, s, ids, T, k, E, block_m, nb,
                      Tc, sorted_ids, block_expert, offsets, npp);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Small-batch front end (T <= 64 tokens): two launches instead of three.
+//   route_quant_kernel: workgroups 0 .. nr-1 route 4 tokens each (one wave
+//             per token, route_token), the others quantise the rows of x;
+//             the two parts share no data.
+//   permute_small_kernel: one workgroup.  Routing never gives a token the
+//             same expert twice, so one 64-bit LDS word per expert marks the
+//             tokens that chose it (T <= 64); a pair's stable rank in its
+//             expert's segment is the number of marked tokens below its own,
+//             and the expert's count the number of marks.  A block scan of
+//             the padded counts gives the offsets; each expert's thread
+//             writes its padding sentinels and block ids, then every pair
+//             its sorted position (the layout of permute_align_kernel).
+// ---------------------------------------------------------------------------
+constexpr int kSmallT = 64;
+
+template <int VPL, int MODE>
+__global__ __launch_bounds__(256) void route_quant_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                          int32_t* __restrict__ ids, float* __restrict__ w, int nr,
+                                                          const void* __restrict__ x, int H, int64_t ld_x, int Hp,
+                                                          uint8_t* __restrict__ xq, void* __restrict__ xs, int vec) {
+  const int wave = threadIdx.x >> 6;
+  if ((int)blockIdx.x < nr) {
+    const int t = blockIdx.x * 4 + wave;
+    if (t < T) route_token<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
+    return;
+  }
+  const int64_t gw = (int64_t)(blockIdx.x - nr) * 4 + wave, nw = (int64_t)(gridDim.x - nr) * 4;
+  if (vec)
+    quant_rows_body<true, true, MODE>(x, T, H, ld_x, Hp, xq, xs, gw, nw);
+  else
+    quant_rows_body<true, false, MODE>(x, T, H, ld_x, Hp, xq, xs, gw, nw);
+}
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                             int BM, int nb, int32_t* __restrict__ sorted_ids,
+                                                             int32_t* __restrict__ block_expert,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ npp) {
+  constexpr int NW = 16;
+  __shared__ uint64_t sel[1024];     // tokens that chose expert e
+  __shared__ int32_t seg[1024];      // segment offset of expert e
+  __shared__ int32_t scan_tmp[NW];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) sel[e] = 0;
+  const int P = T * k;
+  // thread f holds pair f (P <= 64 * 16)
+  const int my_e = tid < P ? ids[tid] : -1;
+  const int t = tid < P ? tid / k : 0;
+  __syncthreads();
+  if (my_e >= 0 && my_e < E) atomicOr((unsigned long long*)&sel[my_e], 1ull << t);
+  __syncthreads();
+  int cnt = 0;
+  if (tid < E) cnt = __popcll(sel[tid]);
+  const int pc = ((cnt + BM - 1) / BM) * BM;
+  int total;
+  const int off = block_exclusive_scan<NW>(pc, scan_tmp, total);
+  if (tid < E) {
+    seg[tid] = off;
+    offsets[tid] = off;
+    // the expert's padding sentinels and block ids, from its own count
+    for (int r = off + cnt; r < off + pc; ++r) sorted_ids[r] = P;
+    for (int b = off / BM; b < (off + pc) / BM; ++b) block_expert[b] = tid;
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    *npp = total;
+  }
+  // the tail past the last segment
+  for (int r = total + tid; r < nb * BM; r += 1024) sorted_ids[r] = P;
+  for (int b = total / BM + tid; b < nb; b += 1024) block_expert[b] = -1;
+  __syncthreads();
+  if (my_e >= 0 && my_e < E) {
+    const uint64_t below = (t == 0) ? 0ull : (~0ull >> (64 - t));
+    sorted_ids[seg[my_e] + __popcll(sel[my_e] & below)] = tid;
+  }
+}
+
+template <int VPL>
+static void launch_route_quant(int mode, dim3 grid, int nr, hipStream_t s, const float* logits, int T, int E, int k,
+                               int32_t* ids, float* w, const void* x, int H, int64_t ld_x, int Hp, void* xq,
+                               void* xs, int vec) {
+  uint8_t* q = (uint8_t*)xq;
+  if (mode == kQuantFp8)
+    hipLaunchKernelGGL((route_quant_kernel<VPL, kQuantFp8>), grid, dim3(256), 0, s, logits, T, E, k, ids, w, nr, x,
+                       H, ld_x, Hp, q, xs, vec);
+  else if (mode == kQuantFp8E8)
+    hipLaunchKernelGGL((route_quant_kernel<VPL, kQuantFp8E8>), grid, dim3(256), 0, s, logits, T, E, k, ids, w, nr, x,
+                       H, ld_x, Hp, q, xs, vec);
+  else
+    hipLaunchKernelGGL((route_quant_kernel<VPL, kQuantMx>), grid, dim3(256), 0, s, logits, T, E, k, ids, w, nr, x, H,
+                       ld_x, Hp, q, xs, vec);
+}
+
+bool front_small_ok(int T, int E, int k) { return T >= 1 && T <= kSmallT && E <= 1024 && k <= kMaxTopK; }
+
+hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t* ids, float* w, int block_m, int nb,
+                              int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets, int32_t* npp,
+                              const void* x_bf16, int H, int64_t ld_x, int Hp, int mode, void* xq, void* xs,
+                              hipStream_t s) {
+  const int nr = (T + 3) / 4;
+  const int64_t units = (int64_t)T * (Hp / 128);
+  int64_t qwg = (units + 15) / 16;  // 16 units per workgroup
+  if (qwg > 4096) qwg = 4096;
+  const dim3 grid((unsigned)(nr + qwg));
+  const int vec = ((uintptr_t)x_bf16 % 16 == 0) && ((ld_x * 2) % 16 == 0);
+  const int vpl = (E + 63) / 64;
+  if (vpl <= 1)
+    launch_route_quant<1>(mode, grid, nr, s, logits, T, E, k, ids, w, x_bf16, H, ld_x, Hp, xq, xs, vec);
+  else if (vpl <= 5)
+    launch_route_quant<5>(mode, grid, nr, s, logits, T, E, k, ids, w, x_bf16, H, ld_x, Hp, xq, xs, vec);
+  else
+    launch_route_quant<16>(mode, grid, nr, s, logits, T, E, k, ids, w, x_bf16, H, ld_x, Hp, xq, xs, vec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, s, ids, T, k, E, block_m, nb, sorted_ids,
+                     block_expert, offsets, npp);
   return hipGetLastError();
 }
 

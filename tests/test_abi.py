@@ -22,7 +22,11 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 LIB = os.path.join(ROOT, "mxfp4_quantized_weights_amd", "libmoe.so")
 
 if not os.path.exists(LIB):  # CPU host without a prior build: build here (cross-compile)
-    from mxfp4_quantized_weights_amd import build as _build  # noqa: E402
+    import importlib.util  # noqa: E402
+    _spec = importlib.util.spec_from_file_location("_moe_build", os.path.join(ROOT, "mxfp4_quantized_weights_amd",
+                                                                            "build.py"))
+    _build = importlib.util.module_from_spec(_spec)
+    _spec.loader.exec_module(_build)  # the package itself needs the library to import
     _build.build()
 
 import mxfp4_quantized_weights_amd as M  # noqa: E402

@@ -305,3 +305,40 @@ def test_gemm1_swiglu_stage(mode, BM):
     assert mism <= max(8, 0.01 * total)
     assert worst_scale <= 1e-3
     assert scale_moves <= 4
+
+
+@pytest.mark.parametrize("T,E,k,BM,mode,ldpad", [(1, 288, 8, 16, "fp8", 0), (7, 288, 8, 16, "mxfp4", 24),
+                                                 (64, 288, 8, 16, "fp8_ue8m0", 0), (64, 1024, 16, 32, "fp8", 8),
+                                                 (33, 8, 2, 64, "mxfp4", 0), (64, 1, 1, 128, "fp8", 0),
+                                                 (65, 288, 8, 16, "fp8", 0), (300, 64, 4, 32, "mxfp4", 0)])
+def test_route_permute_quant_equals_stages(T, E, k, BM, mode, ldpad):
+    """moe_route_permute_quant (two launches up to 64 tokens) gives exactly the
+    results of moe_route_topk + moe_permute_align + moe_quant_act, and those
+    match the oracle."""
+    log(f"route_permute_quant T={T} E={E} k={k} BM={BM} mode={mode} ldpad={ldpad}")
+    H = 400
+    cfg = M.make_cfg(E, k, mode, H, 256, block_m=BM)
+    rng = np.random.default_rng(T + E + BM)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    if T > 4:
+        lg[: T // 3] = rng.integers(-2, 3, (T // 3, E)).astype(np.float32)  # ties
+    xf = rng.standard_normal((T, H + ldpad)).astype(np.float32)
+    xf[:, 7] *= 40
+    xb = torch.from_numpy(xf).to(torch.bfloat16).cuda()
+    x = xb[:, :H]
+    lgd = torch.from_numpy(lg).cuda()
+    ids, w, sid, bexp, offs, npp, xq, xs = M.moe_route_permute_quant(cfg, x, lgd)
+    ids2, w2 = M.moe_route_topk(lgd, k)
+    sid2, bexp2, offs2, npp2 = M.moe_permute_align(ids2, E, BM)
+    xq2, xs2 = M.moe_quant_act(x, cfg.pad.hidden_padded, mode)
+    torch.cuda.synchronize()
+    for a, b in ((ids, ids2), (sid, sid2), (bexp, bexp2), (offs, offs2), (npp, npp2), (xq, xq2)):
+        assert torch.equal(a, b)
+    assert torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    assert torch.equal(xs.view(torch.uint8), xs2.view(torch.uint8))
+    ido, _ = O.route_topk(lg, k)
+    assert np.array_equal(ids.cpu().numpy(), ido)
+    so, bo, oo, no = O.permute_align(ido, E, BM)
+    assert np.array_equal(sid.cpu().numpy(), so) and int(npp.item()) == no
+    qo, _ = O.quant_act(mode, O.pad_cols(x.float().cpu().numpy(), cfg.pad.hidden_padded))
+    assert np.array_equal(xq.cpu().numpy(), qo)
