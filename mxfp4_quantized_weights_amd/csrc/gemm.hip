@@ -863,17 +863,29 @@ __device__ __forceinline__ float4 load_nt4(const float* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int k, int cols, int64_t ldy,
                                                       uint16_t* __restrict__ out, int64_t ld_out, int vec_store) {
   const int t = blockIdx.y;
   const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (h >= cols) return;
   const float* base = y + (int64_t)t * k * ldy + h;
+  // every slot's loads are issued before the first add (k <= KMAX)
+  float4 v0[KMAX], v1[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      v0[j] = load_nt4(base + (int64_t)j * ldy);
+      v1[j] = load_nt4(base + (int64_t)j * ldy + 4);
+    }
+  }
   float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = 0; j < k; ++j) {
-    const float4 v0 = load_nt4(base + (int64_t)j * ldy), v1 = load_nt4(base + (int64_t)j * ldy + 4);
-    a[0] += v0.x; a[1] += v0.y; a[2] += v0.z; a[3] += v0.w;
-    a[4] += v1.x; a[5] += v1.y; a[6] += v1.z; a[7] += v1.w;
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      a[0] += v0[j].x; a[1] += v0[j].y; a[2] += v0[j].z; a[3] += v0[j].w;
+      a[4] += v1[j].x; a[5] += v1[j].y; a[6] += v1[j].z; a[7] += v1[j].w;
+    }
   }
   uint16_t* o = out + (int64_t)t * ld_out + h;
   if (vec_store && h + 8 <= cols) {
@@ -895,7 +907,14 @@ hipError_t launch_combine(const float* y, int T, int k, int c0, int cols, int64_
   // 16-byte stores need every row start 16-byte aligned
   const int vec = ((uintptr_t)o % 16 == 0) && (ld_out % 8 == 0);
   dim3 grid((unsigned)((cols + 2047) / 2048), (unsigned)T), block(256);
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, s, y, k, cols, ldy, o, ld_out, vec);
+  if (k <= 2)
+    hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, s, y, k, cols, ldy, o, ld_out, vec);
+  else if (k <= 4)
+    hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, s, y, k, cols, ldy, o, ld_out, vec);
+  else if (k <= 8)
+    hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, y, k, cols, ldy, o, ld_out, vec);
+  else
+    hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, s, y, k, cols, ldy, o, ld_out, vec);
   return hipGetLastError();
 }
 

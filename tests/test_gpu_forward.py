@@ -177,11 +177,12 @@ def test_forward_zero_tokens():
     assert out.shape == (0, wl.H)
 
 
-@pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
-def test_forward_repeatable_and_equal_to_stages(mode):
-    """Two runs give identical bits, and moe_forward equals the stage entry
-    points called one by one."""
-    wl = MID.with_(mode=mode, T=120)
+@pytest.mark.parametrize("mode,T", [("fp8", 120), ("fp8_ue8m0", 120), ("mxfp4", 120), ("fp8", 3), ("mxfp4", 40)])
+def test_forward_repeatable_and_equal_to_stages(mode, T):
+    """Repeated runs give identical bits, and moe_forward equals the stage
+    entry points called one by one (small batches take the two-launch front
+    end inside moe_forward, the three stage kernels here)."""
+    wl = MID.with_(mode=mode, T=T)
     log(f"repeatability {W.describe(wl)}")
     cfg, ew, x, lg, out1 = _run(wl, 32)
     xd, lgd = x.cuda(), lg.cuda()
@@ -194,6 +195,8 @@ def test_forward_repeatable_and_equal_to_stages(mode):
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
     assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
+    ref, tie = _oracle_with_ties(wl, x, lg)
+    assert_rows_close(bf16_to_f32(out1), ref, wl.mode, "forward", allowance=tie)
 
 
 def test_block_m_choices_agree():
