@@ -203,6 +203,11 @@ def main():
         xq, xs = M._act_buffers(cfg.quant_mode, wl.T, wl.Hp, dev)
         aq = torch.empty(aq_b, dtype=torch.uint8, device=dev)
         as_ = torch.empty(as_b, dtype=torch.uint8, device=dev)
+        # GEMM1 with the K split moe_forward plans (small batches: GEMM1 pieces
+        # plus the SwiGLU/re-quantisation kernel)
+        ks1 = M.plan_ksplit(cfg, wl.T, 13)
+        part_b = M.splitk_bytes(cfg, wl.T, 13, ks1)
+        part = torch.empty(max(part_b, 1), dtype=torch.uint8, device=dev)
 
         def staged(evs):
             evs[0].record(stream)
@@ -210,9 +215,9 @@ def main():
                                         wts.data_ptr(), sid.data_ptr(), bexp.data_ptr(), offs.data_ptr(),
                                         npp.data_ptr(), xq.data_ptr(), xs.data_ptr(), sp)
             evs[1].record(stream)
-            lib.moe_grouped_gemm1_swiglu(cfgp, wl.T, xq.data_ptr(), xs.data_ptr(), sid.data_ptr(), bexp.data_ptr(),
-                                         npp.data_ptr(), w13.data_ptr(), s13.data_ptr(), aq.data_ptr(),
-                                         as_.data_ptr(), sp)
+            lib.moe_grouped_gemm1_swiglu_splitk(cfgp, wl.T, xq.data_ptr(), xs.data_ptr(), sid.data_ptr(),
+                                                bexp.data_ptr(), npp.data_ptr(), w13.data_ptr(), s13.data_ptr(),
+                                                aq.data_ptr(), as_.data_ptr(), ks1, part.data_ptr(), part_b, sp)
             evs[2].record(stream)
             lib.moe_grouped_gemm2_combine(cfgp, wl.T, aq.data_ptr(), as_.data_ptr(), sid.data_ptr(),
                                           bexp.data_ptr(), npp.data_ptr(), w2.data_ptr(), s2.data_ptr(),
@@ -241,7 +246,8 @@ def main():
         peak_f = MFMA_PEAK_TFLOPS[wl.mode]
         mfma_bound = flops1 / nbytes["gemm1"] > peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
         common = {"traffic": recorded_traffic(wl.name),
-                  "kernel": "moe_gemm_stream (GEMM1 + clamped SwiGLU + re-quantisation)",
+                  "kernel": ("moe_gemm_stream (GEMM1 + clamped SwiGLU + re-quantisation)" if ks1 == 1 else
+                             f"moe_gemm_stream (GEMM1, K split {ks1}) + swiglu_requant"),
                   "kernel_us": round(kern[dom], 2), "algorithmic_bytes": nbytes["gemm1"],
                   "algorithmic_flops": flops1}
         if mfma_bound:
@@ -266,7 +272,8 @@ def main():
         "dtype": "fp4e2m1" if wl.mode == "mxfp4" else "fp8e4m3",
         "data": "synthetic (seeded N(0,1) activations/logits, N(0,0.02) weights, quantised by the library)",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "Hp": wl.Hp, "Ip": wl.Ip, "E": wl.E,
-                   "top_k": wl.top_k, "quant": wl.mode, "block_m": bm, "swiglu_limit": wl.swiglu_limit},
+                   "top_k": wl.top_k, "quant": wl.mode, "block_m": bm, "swiglu_limit": wl.swiglu_limit,
+                   "ksplit": [M.plan_ksplit(cfg, wl.T, 13), M.plan_ksplit(cfg, wl.T, 2)]},
         "effective_tflops": round(tflops, 3),
         "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[wl.mode], 5),
         "layer_hbm_frac": round(nbytes["layer"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -89,6 +89,12 @@ _SIGS = {
     "moe_grouped_gemm2_combine": (ctypes.c_int, [_CFGP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
                                                  _P, _SZ, _P]),
     "moe_forward": (ctypes.c_int, [_CFGP, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _I64, _P, _SZ, _P]),
+    "moe_plan_ksplit": (_I32, [_CFGP, _I32, _I32]),
+    "moe_splitk_bytes": (_SZ, [_CFGP, _I32, _I32, _I32]),
+    "moe_grouped_gemm1_swiglu_splitk": (ctypes.c_int, [_CFGP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _P,
+                                                       _SZ, _P]),
+    "moe_grouped_gemm2_combine_splitk": (ctypes.c_int, [_CFGP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
+                                                        _I32, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -300,37 +306,58 @@ def moe_preshuffle_weights(cfg: MoeCfg, which: int, q: torch.Tensor, s: torch.Te
     return qo, so
 
 
+def plan_ksplit(cfg: MoeCfg, T: int, which: int) -> int:
+    """K split the library uses for GEMM `which` (13 or 2) at T tokens."""
+    return _lib.moe_plan_ksplit(ctypes.byref(cfg), T, which)
+
+
+def splitk_bytes(cfg: MoeCfg, T: int, which: int, ksplit: int) -> int:
+    return _lib.moe_splitk_bytes(ctypes.byref(cfg), T, which, ksplit)
+
+
 def moe_grouped_gemm1_swiglu(cfg: MoeCfg, T: int, xq, xs, sorted_ids, block_expert, npp, w13, s13,
-                             stream=None):
-    """-> (aq, as) flat uint8 buffers, rows indexed by sorted position."""
+                             ksplit: int = 1, stream=None):
+    """-> (aq, as) flat uint8 buffers, rows indexed by sorted position.
+    ksplit > 1: the K-split launch pair (fp32 partials in a scratch buffer)."""
     ab, sb = intermediate_bytes(cfg, T)
     dev = xq.device
     aq = _empty_bytes(ab, dev)
     as_ = _empty_bytes(sb, dev)
-    _check(_lib.moe_grouped_gemm1_swiglu(ctypes.byref(cfg), T, _dev(xq, None, "xq"), _dev(xs, None, "xs"),
-                                         _dev(sorted_ids, torch.int32, "sorted_ids"),
-                                         _dev(block_expert, torch.int32, "block_expert"),
-                                         _dev(npp, torch.int32, "num_post_padded"), _dev(w13, None, "w13"),
-                                         _dev(s13, None, "w13_scale"), aq.data_ptr(), as_.data_ptr(),
-                                         _stream(stream)), "moe_grouped_gemm1_swiglu")
+    args = [ctypes.byref(cfg), T, _dev(xq, None, "xq"), _dev(xs, None, "xs"),
+            _dev(sorted_ids, torch.int32, "sorted_ids"), _dev(block_expert, torch.int32, "block_expert"),
+            _dev(npp, torch.int32, "num_post_padded"), _dev(w13, None, "w13"), _dev(s13, None, "w13_scale"),
+            aq.data_ptr(), as_.data_ptr()]
+    if ksplit == 1:
+        _check(_lib.moe_grouped_gemm1_swiglu(*args, _stream(stream)), "moe_grouped_gemm1_swiglu")
+    else:
+        nbytes = splitk_bytes(cfg, T, 13, ksplit)
+        ws = _empty_bytes(max(nbytes, 1), dev)
+        _check(_lib.moe_grouped_gemm1_swiglu_splitk(*args, ksplit, ws.data_ptr(), nbytes, _stream(stream)),
+               "moe_grouped_gemm1_swiglu_splitk")
     return aq[:ab], as_[:sb]
 
 
 def moe_grouped_gemm2_combine(cfg: MoeCfg, T: int, aq, as_, sorted_ids, block_expert, npp, w2, s2, topk_w,
-                              out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+                              out: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                              ksplit: int | None = None, stream=None):
+    """ksplit None: the library's own split (moe_plan_ksplit); else that split."""
     dev = aq.device
     if out is None:
         out = torch.empty(T, cfg.pad.hidden, dtype=torch.bfloat16, device=dev)
     if ws is None:
-        ws = _empty_bytes(workspace_bytes(cfg, T), dev)
-    _check(_lib.moe_grouped_gemm2_combine(ctypes.byref(cfg), T, _dev(aq, None, "aq"), _dev(as_, None, "as"),
-                                          _dev(sorted_ids, torch.int32, "sorted_ids"),
-                                          _dev(block_expert, torch.int32, "block_expert"),
-                                          _dev(npp, torch.int32, "num_post_padded"), _dev(w2, None, "w2"),
-                                          _dev(s2, None, "w2_scale"), _dev(topk_w, torch.float32, "topk_w"),
-                                          _dev(out, torch.bfloat16, "out", contiguous=False), out.stride(0),
-                                          ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)),
-           "moe_grouped_gemm2_combine")
+        ws = _empty_bytes(workspace_bytes(cfg, T) if ksplit is None else splitk_bytes(cfg, T, 2, ksplit), dev)
+    args = [ctypes.byref(cfg), T, _dev(aq, None, "aq"), _dev(as_, None, "as"),
+            _dev(sorted_ids, torch.int32, "sorted_ids"), _dev(block_expert, torch.int32, "block_expert"),
+            _dev(npp, torch.int32, "num_post_padded"), _dev(w2, None, "w2"), _dev(s2, None, "w2_scale"),
+            _dev(topk_w, torch.float32, "topk_w"), _dev(out, torch.bfloat16, "out", contiguous=False),
+            out.stride(0)]
+    wsb = ws.numel() * ws.element_size()
+    if ksplit is None:
+        _check(_lib.moe_grouped_gemm2_combine(*args, ws.data_ptr(), wsb, _stream(stream)),
+               "moe_grouped_gemm2_combine")
+    else:
+        _check(_lib.moe_grouped_gemm2_combine_splitk(*args, ksplit, ws.data_ptr(), wsb, _stream(stream)),
+               "moe_grouped_gemm2_combine_splitk")
     return out
 
 
@@ -399,4 +426,5 @@ class ExpertWeights:
 
 __all__ = [n for n in dir() if n.startswith(("moe_", "MOE_", "Moe"))] + [
     "make_cfg", "pick_block_m", "e8_scale_ld", "QUANT_MODES", "validate_cfg", "max_blocks", "workspace_bytes", "intermediate_bytes",
+    "plan_ksplit", "splitk_bytes",
     "preshuffled_bytes", "ExpertWeights", "EXPORTED_SYMBOLS", "LIB_PATH", "lib"]

@@ -79,9 +79,56 @@ int32_t max_blocks(int64_t P, int32_t E, int32_t BM) {
   return (int32_t)(P < a ? P : a);
 }
 
+// K blocks and N tiles per block of GEMM1 (which = 13) or GEMM2 (which = 2).
+int gemm_kb(const moe_cfg_t* c, int which) {
+  return (which == 13 ? c->pad.hidden_padded : c->pad.inter_padded) / 128;
+}
+int gemm_n_tiles(const moe_cfg_t* c, int which) {
+  return which == 13 ? c->pad.inter_padded / 128 : (c->pad.hidden_padded + 255) / 256;
+}
+
+// A K split for GEMM `which` at T tokens is usable if the pieces align with
+// the scale layout and, for GEMM2, y is not column-chunked.
+bool ksplit_usable(const moe_cfg_t* c, int32_t T, int which, int ks) {
+  if (!moe::ksplit_ok(c->quant_mode, gemm_kb(c, which), ks)) return false;
+  if (ks == 1) return true;
+  const int64_t P = (int64_t)T * c->top_k;
+  if (P > moe::kSplitMaxPairs) return false;
+  return which == 13 || moe::y_chunk_cols(P, c->pad.hidden_padded) == c->pad.hidden_padded;
+}
+
+int plan_ksplit(const moe_cfg_t* c, int32_t T, int which) {
+  const int ks = moe::pick_ksplit(c->quant_mode, T, c->num_experts, c->top_k, c->block_m, gemm_kb(c, which),
+                                  gemm_n_tiles(c, which));
+  return ksplit_usable(c, T, which, ks) ? ks : 1;
+}
+
+// Scratch of a GEMM at split ks: GEMM1 the fp32 partial sums and each pair's
+// sorted row (none without a split), GEMM2 the y planes.
+size_t split_bytes(const moe_cfg_t* c, int32_t T, int which, int ks) {
+  const int64_t P = (int64_t)T * c->top_k;
+  const int64_t Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
+  if (which == 13) return ks > 1 ? align_up((size_t)(ks * P * 2 * Ip * 4 + P * 4)) : 0;
+  // unsplit: the (possibly column-chunked) y rows; split: whole planes
+  const int64_t planes = ks > 1 ? ks * P * Hp * 4 : 0, y = moe::y_reserve_bytes(P, Hp);
+  return align_up((size_t)(planes > y ? planes : y));
+}
+
+// Scratch that covers every split the library can choose for any T' <= T
+// (non-decreasing in T): the largest split times min(P, kSplitMaxPairs).
+size_t split_reserve(const moe_cfg_t* c, int32_t T, int which) {
+  const int64_t P = (int64_t)T * c->top_k;
+  const int64_t Ps = P < moe::kSplitMaxPairs ? P : moe::kSplitMaxPairs;
+  const int cap = moe::ksplit_cap(c->quant_mode, gemm_kb(c, which));
+  const int64_t Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
+  if (which == 13) return cap > 1 ? align_up((size_t)(cap * Ps * 2 * Ip * 4 + Ps * 4)) : 0;
+  const int64_t planes = cap > 1 ? cap * Ps * Hp * 4 : 0, y = moe::y_reserve_bytes(P, Hp);
+  return align_up((size_t)(planes > y ? planes : y));
+}
+
 // Sizes of the pieces of one layer's scratch, in carve order.
 struct Layout {
-  size_t ids, wts, sorted, bexp, offs, npp, xq, xs, aq, as, y, total;
+  size_t ids, wts, sorted, bexp, offs, npp, xq, xs, aq, as, part, y, total;
 };
 
 Layout layout_for(const moe_cfg_t* c, int32_t T) {
@@ -101,8 +148,9 @@ Layout layout_for(const moe_cfg_t* c, int32_t T) {
   L.xs = align_up(T * scale_row_bytes(m, Hp));
   L.aq = align_up(rows * code_row_bytes(m, Ip));
   L.as = align_up(rows * scale_row_bytes(m, Ip));
-  L.y = align_up(moe::y_reserve_bytes(P, Hp));
-  L.total = L.ids + L.wts + L.sorted + L.bexp + L.offs + L.npp + L.xq + L.xs + L.aq + L.as + L.y;
+  L.part = split_reserve(c, T, 13);
+  L.y = split_reserve(c, T, 2);
+  L.total = L.ids + L.wts + L.sorted + L.bexp + L.offs + L.npp + L.xq + L.xs + L.aq + L.as + L.part + L.y;
   return L;
 }
 
@@ -177,11 +225,36 @@ hipError_t front_end(const moe_cfg_t* c, int32_t T, const float* logits, const v
   return moe::launch_quant_rows(x, true, T, H, ld_x, Hp, mode, xq, xs, s);
 }
 
-// GEMM2 and the combine, one column chunk of y at a time (see y_chunk_cols).
-hipError_t gemm2_and_combine(const moe_cfg_t* c, int32_t T, moe::GemmArgs a, int32_t nb, void* out_bf16,
+int log2_of(int ks) { return ks >= 8 ? 3 : ks >= 4 ? 2 : ks >= 2 ? 1 : 0; }
+
+// GEMM1, with a K split: the pieces' partial sums in `part`, then the
+// SwiGLU and re-quantisation kernel.
+hipError_t run_gemm1(const moe_cfg_t* c, int32_t T, moe::GemmArgs a, int32_t nb, int ks, float* part,
+                     hipStream_t s) {
+  if (ks > 1) {
+    a.ks_log2 = log2_of(ks);
+    a.part = part;
+  }
+  hipError_t e = moe::launch_gemm1(c->quant_mode, c->block_m, nb, a, s);
+  if (e != hipSuccess || ks == 1) return e;
+  return moe::launch_swiglu_requant(c->quant_mode, part, ks, (int)((int64_t)T * c->top_k), a.Ip, a.limit, a.aq,
+                                    a.as, s);
+}
+
+// GEMM2 and the combine, one column chunk of y at a time (see y_chunk_cols);
+// with a K split, one y plane per piece (y is then never chunked).
+hipError_t gemm2_and_combine(const moe_cfg_t* c, int32_t T, moe::GemmArgs a, int32_t nb, int ks, void* out_bf16,
                              int64_t ld_out, hipStream_t s) {
   const int64_t P = (int64_t)T * c->top_k;
   const int Hp = c->pad.hidden_padded, H = c->pad.hidden;
+  if (ks > 1) {
+    a.ks_log2 = log2_of(ks);
+    a.ldy = Hp;
+    a.yplane = P * Hp;
+    hipError_t e = moe::launch_gemm2(c->quant_mode, c->block_m, nb, a, s);
+    if (e != hipSuccess) return e;
+    return moe::launch_combine(a.y, T, c->top_k, 0, H, Hp, ks, a.yplane, (uint16_t*)out_bf16, ld_out, s);
+  }
   const int64_t W = moe::y_chunk_cols(P, Hp);
   a.ldy = W;
   for (int c0 = 0; c0 < Hp; c0 += (int)W) {
@@ -192,7 +265,7 @@ hipError_t gemm2_and_combine(const moe_cfg_t* c, int32_t T, moe::GemmArgs a, int
     if (e != hipSuccess) return e;
     const int cols = H - c0 < wc ? H - c0 : wc;
     if (cols > 0) {
-      e = moe::launch_combine(a.y, T, c->top_k, c0, cols, W, (uint16_t*)out_bf16, ld_out, s);
+      e = moe::launch_combine(a.y, T, c->top_k, c0, cols, W, 1, 0, (uint16_t*)out_bf16, ld_out, s);
       if (e != hipSuccess) return e;
     }
   }
@@ -353,6 +426,50 @@ moe_status_t moe_grouped_gemm1_swiglu(const moe_cfg_t* cfg, int32_t T, const voi
   return hip_status(moe::launch_gemm1(mode, cfg->block_m, nb, a, as_stream(stream)));
 }
 
+moe_status_t moe_grouped_gemm1_swiglu_splitk(const moe_cfg_t* cfg, int32_t T, const void* xq, const void* xs,
+                                             const int32_t* sorted_ids, const int32_t* block_expert,
+                                             const int32_t* num_post_padded, const void* w13, const void* w13_scale,
+                                             void* aq, void* as, int32_t ksplit, void* ws, size_t ws_bytes,
+                                             void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
+  if ((st = check_layout(cfg)) != MOE_OK) return st;
+  if (!ksplit_usable(cfg, T, 13, ksplit)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!xq || !xs || !sorted_ids || !block_expert || !num_post_padded || !w13 || !w13_scale || !aq || !as)
+    return MOE_ERR_NULL;
+  if (ksplit > 1 && !ws) return MOE_ERR_NULL;
+  if (ws_bytes < split_bytes(cfg, T, 13, ksplit)) return MOE_ERR_WORKSPACE;
+  const int32_t nb = max_blocks((int64_t)T * cfg->top_k, cfg->num_experts, cfg->block_m);
+  moe::GemmArgs a = gemm1_args(cfg, T, xq, xs, sorted_ids, block_expert, num_post_padded, w13, w13_scale, aq, as);
+  return hip_status(run_gemm1(cfg, T, a, nb, ksplit, (float*)ws, as_stream(stream)));
+}
+
+moe_status_t moe_grouped_gemm2_combine_splitk(const moe_cfg_t* cfg, int32_t T, const void* aq, const void* as,
+                                              const int32_t* sorted_ids, const int32_t* block_expert,
+                                              const int32_t* num_post_padded, const void* w2, const void* w2_scale,
+                                              const float* topk_w, void* out_bf16, int64_t ld_out, int32_t ksplit,
+                                              void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
+  if ((st = check_layout(cfg)) != MOE_OK) return st;
+  if (ld_out < cfg->pad.hidden) return MOE_ERR_SHAPE;
+  if (!ksplit_usable(cfg, T, 2, ksplit)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!aq || !as || !sorted_ids || !block_expert || !num_post_padded || !w2 || !w2_scale || !topk_w || !out_bf16 ||
+      !ws)
+    return MOE_ERR_NULL;
+  const int64_t P = (int64_t)T * cfg->top_k;
+  if (ws_bytes < split_bytes(cfg, T, 2, ksplit)) return MOE_ERR_WORKSPACE;
+  const int32_t nb = max_blocks(P, cfg->num_experts, cfg->block_m);
+  hipStream_t s = as_stream(stream);
+  float* y = (float*)ws;
+  moe::GemmArgs a = gemm2_args(cfg, T, aq, as, sorted_ids, block_expert, num_post_padded, w2, w2_scale, y, topk_w);
+  return hip_status(gemm2_and_combine(cfg, T, a, nb, ksplit, out_bf16, ld_out, s));
+}
+
 moe_status_t moe_grouped_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const void* aq, const void* as,
                                        const int32_t* sorted_ids, const int32_t* block_expert,
                                        const int32_t* num_post_padded, const void* w2, const void* w2_scale,
@@ -361,20 +478,19 @@ moe_status_t moe_grouped_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const vo
   moe_status_t st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
-  if ((st = check_layout(cfg)) != MOE_OK) return st;
-  if (ld_out < cfg->pad.hidden) return MOE_ERR_SHAPE;
-  if (T == 0) return MOE_OK;
-  if (!aq || !as || !sorted_ids || !block_expert || !num_post_padded || !w2 || !w2_scale || !topk_w || !out_bf16 ||
-      !ws)
-    return MOE_ERR_NULL;
-  const int64_t P = (int64_t)T * cfg->top_k;
-  const size_t ybytes = align_up((size_t)moe::y_reserve_bytes(P, cfg->pad.hidden_padded));
-  if (ws_bytes < ybytes) return MOE_ERR_WORKSPACE;
-  const int32_t nb = max_blocks(P, cfg->num_experts, cfg->block_m);
-  hipStream_t s = as_stream(stream);
-  float* y = (float*)ws;
-  moe::GemmArgs a = gemm2_args(cfg, T, aq, as, sorted_ids, block_expert, num_post_padded, w2, w2_scale, y, topk_w);
-  return hip_status(gemm2_and_combine(cfg, T, a, nb, out_bf16, ld_out, s));
+  return moe_grouped_gemm2_combine_splitk(cfg, T, aq, as, sorted_ids, block_expert, num_post_padded, w2, w2_scale,
+                                          topk_w, out_bf16, ld_out, plan_ksplit(cfg, T, 2), ws, ws_bytes, stream);
+}
+
+int32_t moe_plan_ksplit(const moe_cfg_t* cfg, int32_t T, int32_t which) {
+  if (check_cfg(cfg) != MOE_OK || check_tokens(cfg, T) != MOE_OK || (which != 13 && which != 2)) return -1;
+  return plan_ksplit(cfg, T, which);
+}
+
+size_t moe_splitk_bytes(const moe_cfg_t* cfg, int32_t T, int32_t which, int32_t ksplit) {
+  if (check_cfg(cfg) != MOE_OK || check_tokens(cfg, T) != MOE_OK || (which != 13 && which != 2)) return 0;
+  if (!ksplit_usable(cfg, T, which, ksplit)) return 0;
+  return split_bytes(cfg, T, which, ksplit);
 }
 
 moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, int64_t ld_x, const float* router_logits,
@@ -401,6 +517,7 @@ moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, in
   void* xs = p; p += L.xs;
   void* aq = p; p += L.aq;
   void* as = p; p += L.as;
+  float* part = (float*)p; p += L.part;
   float* y = (float*)p;
 
   hipStream_t s = as_stream(stream);
@@ -413,9 +530,9 @@ moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, in
       hipSuccess)
     return MOE_ERR_HIP;
   moe::GemmArgs a1 = gemm1_args(cfg, T, xq, xs, sorted, bexp, npp, w13, w13_scale, aq, as);
-  if ((e = moe::launch_gemm1(mode, BM, nb, a1, s)) != hipSuccess) return MOE_ERR_HIP;
+  if ((e = run_gemm1(cfg, T, a1, nb, plan_ksplit(cfg, T, 13), part, s)) != hipSuccess) return MOE_ERR_HIP;
   moe::GemmArgs a2 = gemm2_args(cfg, T, aq, as, sorted, bexp, npp, w2, w2_scale, y, wts);
-  return hip_status(gemm2_and_combine(cfg, T, a2, nb, out_bf16, ld_out, s));
+  return hip_status(gemm2_and_combine(cfg, T, a2, nb, plan_ksplit(cfg, T, 2), out_bf16, ld_out, s));
 }
 
 }  // extern "C"

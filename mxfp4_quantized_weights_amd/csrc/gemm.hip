@@ -28,6 +28,8 @@
 //        (f16 MFMA, promotion by the exact power-of-two scale product) with
 //        UE8M0 re-quantisation; GEMM2 on the scaled FP8 MFMA, which applies
 //        both power-of-two scales itself, so there is no promotion at all.
+#include <math.h>
+
 #include <utility>
 
 #include "moe_device.h"
@@ -513,12 +515,59 @@ __device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&
   }
 }
 
+// GEMM1 epilogue of a K piece: the fp32 partial sums of the gate and up
+// columns of real rows, part[piece, pair, column] (gate columns [0, Ip), up
+// columns [Ip, 2Ip)), in the lane layout of epilogue_gemm1_s.  Piece 0 also
+// writes the zero codes and scales of the block's pad rows (this N tile's
+// columns), and piece 0 of N tile 0 the sorted row of each real pair,
+// part_row[pair] (after the partial sums: P int32).
+template <int MODE, int MT>
+__device__ __forceinline__ void epilogue_gemm1_part(const GemmArgs& p, const v4f (&acc)[MT][4], const int32_t* sid,
+                                                    int row0, int ks, int nt, int wt, int wn) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
+  const int64_t ld = 2 * (int64_t)p.Ip;
+  int32_t* part_row = (int32_t*)(p.part + ((int64_t)p.num_pairs << p.ks_log2) * ld);
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int t = wt * 64 + m * 16 + c16;
+    const int s = sid[t];
+    if (s < p.num_pairs) {
+      float* row = p.part + ((int64_t)ks * p.num_pairs + s) * ld + nt * 128 + 32 * wn + 4 * q;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const v4f g = acc[m][jj], u = acc[m][jj + 2];
+        *(float4*)(row + 16 * jj) = make_float4(g[0], g[1], g[2], g[3]);
+        *(float4*)(row + p.Ip + 16 * jj) = make_float4(u[0], u[1], u[2], u[3]);
+      }
+      if (ks == 0 && nt == 0 && wn == 0 && q == 0) part_row[s] = row0 + t;
+    } else if (ks == 0) {
+      const int64_t r = row0 + t;
+      if constexpr (MODE == kGemmMx) {
+        uint8_t* row = p.aq + r * (p.Ip / 2) + nt * 64 + 16 * wn + 2 * q;
+        *(uint16_t*)row = 0;
+        *(uint16_t*)(row + 8) = 0;
+        if (q == 0) ((uint8_t*)p.as)[r * (p.Ip / 32) + nt * 4 + wn] = 0;
+      } else {
+        uint8_t* row = p.aq + r * p.Ip + nt * 128 + 32 * wn + 4 * q;
+        *(uint32_t*)row = 0u;
+        *(uint32_t*)(row + 16) = 0u;
+        if (wn == 0 && q == 0) {
+          if constexpr (MODE == kGemmE8F16)
+            ((uint8_t*)p.as)[r * e8_scale_ld(p.Ip) + nt] = 0;
+          else
+            ((float*)p.as)[r * (p.Ip / 128) + nt] = 0.0f;
+        }
+      }
+    }
+  }
+}
+
 // GEMM2 epilogue: y[pair, 4 consecutive columns] = routing weight * C per
 // lane and weight tile; routing weights from LDS.  y holds the columns of
-// this launch's N tiles (from nt0).
+// this launch's N tiles (from nt0); a K piece writes its own plane.
 template <int MT>
 __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&acc)[MT][4], const int32_t* sid,
-                                                 const float* wts, int nt, int wt, int wn) {
+                                                 const float* wts, int ks, int nt, int wt, int wn) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -526,7 +575,7 @@ __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&
     const int s = sid[t];
     if (s < p.num_pairs) {
       const float w = wts[t];
-      float* yrow = p.y + (int64_t)s * p.ldy + (nt - p.nt0) * 256 + 64 * wn + 4 * q;
+      float* yrow = p.y + ks * p.yplane + (int64_t)s * p.ldy + (nt - p.nt0) * 256 + 64 * wn + 4 * q;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const v4f v = acc[m][j];
@@ -540,7 +589,7 @@ __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&
 // start; when an item has fewer than S K blocks that is too late for the
 // ring's own waits to cover it (the S-1 K blocks of the prologue are issued
 // without waits), and the kernel then waits for it explicitly.
-template <int MODE, int BM, bool G1, int S>
+template <int MODE, int BM, bool G1, int S, bool SPLIT>
 __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(GemmArgs p) {
   using R = Ring<MODE, BM>;
   static_assert(S >= 3 && S <= 5, "ring depth");
@@ -577,7 +626,8 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   // items of XCD x: the contiguous chunk x; workgroup j of the XCD takes
   // items j, j + nw, j + 2 nw, ... of it (nw workgroups per XCD)
   const int npp = __builtin_amdgcn_readfirstlane(*p.npp);
-  const int items = (npp / BM) * p.n_tiles;
+  const int KSL = SPLIT ? p.ks_log2 : 0;  // K pieces per item: 2^KSL
+  const int items = ((npp / BM) * p.n_tiles) << KSL;
   const int per = (items + kXcds - 1) / kXcds;
   const int lo = (blockIdx.x % kXcds) * per;
   const int hi = min(lo + per, items);
@@ -585,15 +635,18 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   const int first = lo + (int)(blockIdx.x / kXcds);
   if (first >= hi) return;
   const int n_my = (hi - first + nw - 1) / nw;
-  const int KB = p.K / 128;
+  const int KB = p.K / 128;   // K blocks of a weight row
+  const int KBI = KB >> KSL;  // K blocks of an item
   const int NT16 = p.N / 16;
-  const int total = n_my * KB;
+  const int total = n_my * KBI;
   // Items of fewer than S K blocks finish inside the prologue (which issues
   // S-1 K blocks without waiting) or within S-1 steps of the next item's
   // metadata loads: their metadata is waited for explicitly.
-  const bool short_items = KB < S;
-  auto item_m = [&](int ii) { return (first + ii * nw) / p.n_tiles; };
-  auto item_nt = [&](int ii) { return p.nt0 + (first + ii * nw) % p.n_tiles; };
+  const bool short_items = KBI < S;
+  // item -> (M block, N tile, K piece), K pieces innermost
+  auto item_m = [&](int ii) { return ((first + ii * nw) >> KSL) / p.n_tiles; };
+  auto item_nt = [&](int ii) { return p.nt0 + ((first + ii * nw) >> KSL) % p.n_tiles; };
+  auto item_ks = [&](int ii) { return (first + ii * nw) & ((1 << KSL) - 1); };
 
   // sorted pair ids of item ii -> ids_lds[ii % NB] (waves 0 .. NI-1), its
   // block's expert -> exp_lds[ii % NB] (lane 0 of the last wave)
@@ -618,11 +671,12 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   int wts_step = -1, wts_item = 0;
   auto setup_issue = [&](int ii, int s) {
     const int m = item_m(ii), nt = item_nt(ii);
+    const int kb0 = item_ks(ii) * KBI;  // first K block of the item
     const int e = __builtin_amdgcn_readfirstlane(exp_lds[ii % NB]);
 #pragma unroll
     for (int q = 0; q < R::DW; ++q) {
       const int g = wave * R::DW + q, tile = g / R::HALVES, h = g % R::HALVES;
-      rs.w[q] = p.B + (((int64_t)e * NT16 + ring_tile<G1>(p, nt, tile)) * KB) * R::TILE + h * 1024 + lane * 16;
+      rs.w[q] = p.B + (((int64_t)e * NT16 + ring_tile<G1>(p, nt, tile)) * KB + kb0) * R::TILE + h * 1024 + lane * 16;
     }
     const int32_t* ids = ids_lds[ii % NB];
     // rows past BM (the unused scale entries of a small block) read row 0 / the block's first row
@@ -637,26 +691,28 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
 #pragma unroll
     for (int q = 0; q < R::DT; ++q) {
       const int g = wave * R::DT + q, mt = g / R::HALVES, h = g % R::HALVES;
-      rs.t[q] = p.A + row_of(mt * 16 + (lane & 15)) * p.lda + h * 64 + (lane >> 4) * 16;
+      rs.t[q] = p.A + row_of(mt * 16 + (lane & 15)) * p.lda + kb0 * R::AROW + h * 64 + (lane >> 4) * 16;
     }
     {
+      // scale bytes before K block kb0: fp32 and MX 4 per K block, UE8M0 1
       const int64_t row = row_of(ring_scale_row(wave, lane));
-      rs.ts = (MODE == kGemmMx || e8_tokens(MODE)) ? (const uint8_t*)p.As + row * p.ldas
-                                                     : (const uint8_t*)p.As + row * p.ldas * 4;
+      rs.ts = (MODE == kGemmMx) ? (const uint8_t*)p.As + row * p.ldas + kb0 * 4
+              : e8_tokens(MODE) ? (const uint8_t*)p.As + row * p.ldas + kb0
+                                : (const uint8_t*)p.As + row * p.ldas * 4 + kb0 * 4;
     }
     if constexpr (MODE != kGemmMx) {
       // GEMM1: the gate and the up 128-row block of the N tile; GEMM2: the
       // N tile's two 128-row blocks (the second clamped to the last block)
       const int NB128 = p.N / 128;
       const int b0 = G1 ? nt : nt * 2, b1 = G1 ? p.Ip / 128 + nt : min(nt * 2 + 1, NB128 - 1);
-      rs.wsc = (const uint8_t*)((const float*)p.Bs + ((int64_t)e * NB128 + ((lane & 1) ? b1 : b0)) * KB);
+      rs.wsc = (const uint8_t*)((const float*)p.Bs + ((int64_t)e * NB128 + ((lane & 1) ? b1 : b0)) * KB + kb0);
     }
     if constexpr (R::DWS > 0) {
       const int KBq = (KB + 3) / 4;
 #pragma unroll
       for (int q = 0; q < R::DWS; ++q)
         rs.ws[q] = (const uint8_t*)p.Bs +
-                   ((((int64_t)e * NT16 + ring_tile<G1>(p, nt, wave * R::DWS + q)) * KBq) * 64 + lane) * 4;
+                   ((((int64_t)e * NT16 + ring_tile<G1>(p, nt, wave * R::DWS + q)) * KBq + kb0 / 4) * 64 + lane) * 4;
     }
     // metadata of the next item: ids now; GEMM2 weights S-1 steps later,
     // once the ring's waits have covered the ids (or right away after an
@@ -684,10 +740,11 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
 #pragma unroll
     for (int j = 0; j < 4; ++j) tiles[j] = 4 * wn + j;
   }
-  int c_nt = 0, c_row0 = 0, c_mv = MT;
+  int c_nt = 0, c_row0 = 0, c_mv = MT, c_ks = 0;
   bool active = true;
   auto setup_compute = [&](int ii) {
     c_nt = item_nt(ii);
+    c_ks = item_ks(ii);
     c_row0 = item_m(ii) * BM;
     if constexpr (!G1) active = c_nt * 256 + 64 * wn < p.N;
     // real rows are a prefix of the block: count the wave's token tiles
@@ -716,12 +773,12 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
         if ((i_kb & 3) == 0) ws = ws_buf[(i_grp++) % NWS];
       }
       ring_issue<MODE, BM>(rs, slot(slot_c), wave, i_kb, ws);
-      if (++i_kb == KB) {
+      if (++i_kb == KBI) {
         i_kb = 0;
         if (++i_ii < n_my) setup_issue(i_ii, s);
       }
     } else {
-      ring_issue<MODE, BM>(rs, slot(slot_c), wave, KB - 1, nullptr);  // past the end: reload, never read
+      ring_issue<MODE, BM>(rs, slot(slot_c), wave, KBI - 1, nullptr);  // past the end: reload, never read
     }
   };
 
@@ -757,12 +814,15 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
     }
     if (active && c_mv > 0)
       ring_compute<MODE, BM, G1>(slot(std::integral_constant<int, d>{}), c_ws, tiles, wt, c_kb, sw0, sw1, c_mv, acc);
-    if (++c_kb == KB) {
+    if (++c_kb == KBI) {
       const int32_t* ids = ids_lds[c_ii % NB];
       if constexpr (G1) {
-        epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
+        if constexpr (SPLIT)
+          epilogue_gemm1_part<MODE, MT>(p, acc, ids, c_row0, c_ks, c_nt, wt, wn);
+        else
+          epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
       } else {
-        if (active) epilogue_gemm2_s<MT>(p, acc, ids, wts_lds[c_ii % NB], c_nt, wt, wn);
+        if (active) epilogue_gemm2_s<MT>(p, acc, ids, wts_lds[c_ii % NB], c_ks, c_nt, wt, wn);
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m)
@@ -803,31 +863,43 @@ static int device_cus() {
   return cus[dev];
 }
 
-template <int MODE, bool G1>
-static hipError_t launch_gemm_mode(int block_m, int nb, const GemmArgs& a, hipStream_t s) {
+// Kernels with a K split (SPLIT) are separate instances, so that the plain
+// ones carry none of its per-item state.
+template <int MODE, bool G1, bool SPLIT>
+static hipError_t launch_gemm_split(int block_m, int nb, const GemmArgs& a, hipStream_t s) {
   constexpr int SR = (MODE == kGemmMx) ? MOE_RING_S_MX : MOE_RING_S_FP8;    // block_m 64 / 128
   constexpr int SD = (MODE == kGemmMx) ? MOE_RING_S_MX : MOE_RING_S_SMALL;  // block_m 16 / 32
   // One workgroup per CU (the ring's LDS use allows no more), fewer when
   // there are fewer items; a multiple of kXcds so that every XCD gets the
   // same number of workgroups.
-  const int64_t items = (int64_t)nb * a.n_tiles;
+  const int64_t items = ((int64_t)nb * a.n_tiles) << a.ks_log2;
   const int64_t wgs = (device_cus() + kXcds - 1) / kXcds * kXcds;
   const dim3 grid((unsigned)(items < wgs ? (items + kXcds - 1) / kXcds * kXcds : wgs));
   switch (block_m) {
     case 16:
-      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 16, G1, SD>), grid, dim3(Ring<MODE, 16>::NTH), 0, s, a);
+      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 16, G1, SD, SPLIT>), grid, dim3(Ring<MODE, 16>::NTH), 0, s,
+                         a);
       break;
     case 32:
-      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 32, G1, SD>), grid, dim3(Ring<MODE, 32>::NTH), 0, s, a);
+      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 32, G1, SD, SPLIT>), grid, dim3(Ring<MODE, 32>::NTH), 0, s,
+                         a);
       break;
     case 64:
-      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 64, G1, SR>), grid, dim3(Ring<MODE, 64>::NTH), 0, s, a);
+      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 64, G1, SR, SPLIT>), grid, dim3(Ring<MODE, 64>::NTH), 0, s,
+                         a);
       break;
     default:
-      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 128, G1, SR>), grid, dim3(Ring<MODE, 128>::NTH), 0, s, a);
+      hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 128, G1, SR, SPLIT>), grid, dim3(Ring<MODE, 128>::NTH), 0, s,
+                         a);
       break;
   }
   return hipGetLastError();
+}
+
+template <int MODE, bool G1>
+static hipError_t launch_gemm_mode(int block_m, int nb, const GemmArgs& a, hipStream_t s) {
+  return a.ks_log2 > 0 ? launch_gemm_split<MODE, G1, true>(block_m, nb, a, s)
+                       : launch_gemm_split<MODE, G1, false>(block_m, nb, a, s);
 }
 
 // GEMM1's output is re-quantised, so its sum must be fp32-exact: block FP8
@@ -851,8 +923,132 @@ hipError_t launch_gemm2(int mode, int block_m, int nb, const GemmArgs& a, hipStr
   }
 }
 
+// ---------------------------------------------------------------------------
+// K split for small batches.
+
+int ksplit_cap(int mode, int KB) {
+  int ks = 1;
+  while (ks < kSplitMax && ksplit_ok(mode, KB, 2 * ks)) ks *= 2;
+  return ks;
+}
+
+bool ksplit_ok(int mode, int KB, int ks) {
+  if (ks == 1) return true;
+  if (ks != 2 && ks != 4 && ks != 8) return false;
+  if (KB % ks != 0 || KB / ks < 4) return false;
+  // MX and UE8M0 scale bytes come in dwords of 4 K blocks
+  return mode == kQuantFp8 || (KB / ks) % 4 == 0;
+}
+
+int pick_ksplit(int mode, int T, int E, int k, int block_m, int KB, int n_tiles) {
+  const int64_t P = (int64_t)T * k;
+  if (P <= 0 || P > kSplitMaxPairs) return 1;
+  // expected active experts E * (1 - (1 - k/E)^T); blocks: one per active
+  // expert while an expert's share of pairs fits one block
+  const double active = (double)E * (1.0 - pow(1.0 - (double)k / E, (double)T));
+  const double share = (double)P / (active > 1.0 ? active : 1.0);
+  const double blocks = share <= block_m ? active : (double)P / block_m + 0.5 * active;
+  const double items = blocks * n_tiles;
+  // a split only pays while workgroups would otherwise sit idle: once every
+  // workgroup has an item, shorter pieces stream the same bytes per CU and
+  // add the partial sums' round trip
+  const double wgs = (double)((device_cus() + kXcds - 1) / kXcds * kXcds);
+  int ks = 1;
+  while (items * (2 * ks) <= wgs + 0.5 && ksplit_ok(mode, KB, 2 * ks)) ks *= 2;  // + 0.5: rounding of the estimate
+  return ks;
+}
+
+// One workgroup per pair f (its sorted row r from part_row, which GEMM1's
+// piece 0 wrote; the partial sums are read without waiting for it); a thread
+// owns 4 consecutive intermediate columns, so a 1x128 group is 32 threads and
+// a 1x32 group 8.  The code and scale decisions are those of
+// epilogue_gemm1_s, on the same fp32 values.  Pad rows were zeroed by GEMM1.
+template <int QMODE, int KS>
+__global__ __launch_bounds__(256) void swiglu_requant_kernel(const float* __restrict__ part, int P, int Ip, float L,
+                                                             uint8_t* __restrict__ aq, void* __restrict__ as) {
+  const int f = blockIdx.x;
+  const int64_t plane = (int64_t)P * 2 * Ip;
+  const int r = ((const int32_t*)(part + plane * KS))[f];
+  for (int c = threadIdx.x * 4; c < Ip; c += 1024) {
+    float a[4];
+    {
+      // all pieces' loads first, then the sums in piece order
+      const float* g = part + (int64_t)f * 2 * Ip + c;
+      float4 gv[KS], uv[KS];
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        gv[i] = *(const float4*)(g + i * plane);
+        uv[i] = *(const float4*)(g + i * plane + Ip);
+      }
+      float4 gs = gv[0], us = uv[0];
+#pragma unroll
+      for (int i = 1; i < KS; ++i) {
+        gs.x += gv[i].x; gs.y += gv[i].y; gs.z += gv[i].z; gs.w += gv[i].w;
+        us.x += uv[i].x; us.y += uv[i].y; us.z += uv[i].z; us.w += uv[i].w;
+      }
+      a[0] = swiglu_clamped(gs.x, us.x, L);
+      a[1] = swiglu_clamped(gs.y, us.y, L);
+      a[2] = swiglu_clamped(gs.z, us.z, L);
+      a[3] = swiglu_clamped(gs.w, us.w, L);
+    }
+    float mx = fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3])));
+    constexpr int GT = QMODE == kQuantMx ? 8 : 32;  // threads of one group
+#pragma unroll
+    for (int o = 1; o < GT; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const bool lead = (threadIdx.x & (GT - 1)) == 0;
+    if constexpr (QMODE == kQuantMx) {
+      const uint32_t b = e8m0_byte(mx);
+      const float inv = e8m0_inverse(b);
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed |= mx_quant(a[i], inv) << (4 * i);
+      *(uint16_t*)(aq + (int64_t)r * (Ip / 2) + c / 2) = (uint16_t)packed;
+      if (lead) ((uint8_t*)as)[(int64_t)r * (Ip / 32) + c / 32] = (uint8_t)b;
+    } else if constexpr (QMODE == kQuantFp8E8) {
+      const uint32_t b = ue8m0_byte(mx);
+      const float inv = e8m0_inverse(b);
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed |= ((mx > 0.0f) ? fp8e8_quant(a[i], inv) : 0u) << (8 * i);
+      *(uint32_t*)(aq + (int64_t)r * Ip + c) = packed;
+      if (lead) ((uint8_t*)as)[(int64_t)r * e8_scale_ld(Ip) + c / 128] = (uint8_t)b;
+    } else {
+      const float sc = mx / kE4M3Max;
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed |= ((mx > 0.0f) ? fp8_quant(a[i], sc) : 0u) << (8 * i);
+      *(uint32_t*)(aq + (int64_t)r * Ip + c) = packed;
+      if (lead) ((float*)as)[(int64_t)r * (Ip / 128) + c / 128] = (mx > 0.0f) ? sc : 0.0f;
+    }
+  }
+}
+
+template <int QMODE>
+static void launch_requant_mode(const float* part, int ks, int P, int Ip, float limit, uint8_t* aq, void* as,
+                                hipStream_t s) {
+  const dim3 grid((unsigned)P), block(256);
+  switch (ks) {
+    case 2: hipLaunchKernelGGL((swiglu_requant_kernel<QMODE, 2>), grid, block, 0, s, part, P, Ip, limit, aq, as); break;
+    case 4: hipLaunchKernelGGL((swiglu_requant_kernel<QMODE, 4>), grid, block, 0, s, part, P, Ip, limit, aq, as); break;
+    default: hipLaunchKernelGGL((swiglu_requant_kernel<QMODE, 8>), grid, block, 0, s, part, P, Ip, limit, aq, as); break;
+  }
+}
+
+hipError_t launch_swiglu_requant(int mode, const float* part, int ks, int P, int Ip, float limit, uint8_t* aq,
+                                 void* as, hipStream_t s) {
+  if (P <= 0) return hipSuccess;
+  if (mode == kQuantFp8)
+    launch_requant_mode<kQuantFp8>(part, ks, P, Ip, limit, aq, as, s);
+  else if (mode == kQuantFp8E8)
+    launch_requant_mode<kQuantFp8E8>(part, ks, P, Ip, limit, aq, as, s);
+  else
+    launch_requant_mode<kQuantMx>(part, ks, P, Ip, limit, aq, as, s);
+  return hipGetLastError();
+}
+
 // out[t, c0 + h] = bf16(sum_j y[t*k + j, h]) with the slot sum in order
-// j = 0..k-1, for h < cols (a column chunk of the output).  8 columns per
+// j = 0..k-1 (with K pieces: plane by plane, slots in order within each),
+// for h < cols (a column chunk of the output).  8 columns per
 // thread (two 16-byte non-temporal loads per slot: y is read once); the 8
 // bf16 results go out as one 16-byte store when the row stride allows it.
 // Columns h .. h+7 stay inside the y rows GEMM2 wrote (the chunk width is a
@@ -865,26 +1061,30 @@ __device__ __forceinline__ float4 load_nt4(const float* p) {
 
 template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int k, int cols, int64_t ldy,
-                                                      uint16_t* __restrict__ out, int64_t ld_out, int vec_store) {
+                                                      int nplanes, int64_t plane, uint16_t* __restrict__ out,
+                                                      int64_t ld_out, int vec_store) {
   const int t = blockIdx.y;
   const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (h >= cols) return;
-  const float* base = y + (int64_t)t * k * ldy + h;
-  // every slot's loads are issued before the first add (k <= KMAX)
-  float4 v0[KMAX], v1[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
-      v0[j] = load_nt4(base + (int64_t)j * ldy);
-      v1[j] = load_nt4(base + (int64_t)j * ldy + 4);
-    }
-  }
   float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  // plane by plane (K pieces of GEMM2); in a plane every slot's loads are
+  // issued before the first add (k <= KMAX)
+  for (int ps = 0; ps < nplanes; ++ps) {
+    const float* base = y + ps * plane + (int64_t)t * k * ldy + h;
+    float4 v0[KMAX], v1[KMAX];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
-      a[0] += v0[j].x; a[1] += v0[j].y; a[2] += v0[j].z; a[3] += v0[j].w;
-      a[4] += v1[j].x; a[5] += v1[j].y; a[6] += v1[j].z; a[7] += v1[j].w;
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k) {
+        v0[j] = load_nt4(base + (int64_t)j * ldy);
+        v1[j] = load_nt4(base + (int64_t)j * ldy + 4);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j < k) {
+        a[0] += v0[j].x; a[1] += v0[j].y; a[2] += v0[j].z; a[3] += v0[j].w;
+        a[4] += v1[j].x; a[5] += v1[j].y; a[6] += v1[j].z; a[7] += v1[j].w;
+      }
     }
   }
   uint16_t* o = out + (int64_t)t * ld_out + h;
@@ -900,21 +1100,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_combine(const float* y, int T, int k, int c0, int cols, int64_t ldy, uint16_t* out,
-                          int64_t ld_out, hipStream_t s) {
+hipError_t launch_combine(const float* y, int T, int k, int c0, int cols, int64_t ldy, int nplanes, int64_t plane,
+                          uint16_t* out, int64_t ld_out, hipStream_t s) {
   if (T <= 0 || cols <= 0) return hipSuccess;
   uint16_t* o = out + c0;
   // 16-byte stores need every row start 16-byte aligned
   const int vec = ((uintptr_t)o % 16 == 0) && (ld_out % 8 == 0);
   dim3 grid((unsigned)((cols + 2047) / 2048), (unsigned)T), block(256);
   if (k <= 2)
-    hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, s, y, k, cols, ldy, o, ld_out, vec);
+    hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, s, y, k, cols, ldy, nplanes, plane, o, ld_out, vec);
   else if (k <= 4)
-    hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, s, y, k, cols, ldy, o, ld_out, vec);
+    hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, s, y, k, cols, ldy, nplanes, plane, o, ld_out, vec);
   else if (k <= 8)
-    hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, y, k, cols, ldy, o, ld_out, vec);
+    hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, y, k, cols, ldy, nplanes, plane, o, ld_out, vec);
   else
-    hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, s, y, k, cols, ldy, o, ld_out, vec);
+    hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, s, y, k, cols, ldy, nplanes, plane, o, ld_out, vec);
   return hipGetLastError();
 }
 

@@ -16,7 +16,7 @@ constexpr int kQuantFp8E8 = 3;  // e4m3, UE8M0 scale bytes (128x128 weights, 1x1
 
 // Row stride in bytes of UE8M0 activation-scale rows: one byte per 128
 // columns, rounded up to whole dwords so that the GEMMs load aligned words.
-inline int64_t e8_scale_ld(int64_t cols_padded) { return (cols_padded / 128 + 3) / 4 * 4; }
+__host__ __device__ inline int64_t e8_scale_ld(int64_t cols_padded) { return (cols_padded / 128 + 3) / 4 * 4; }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);
@@ -69,7 +69,36 @@ struct GemmArgs {
   const float* topk_w;    // [P]
   int32_t nt0;            // GEMM2: first 256-column N tile of this launch (items cover n_tiles tiles)
   int64_t ldy;            // GEMM2: row stride of y in floats
+  int32_t ks_log2;        // K split: each item covers K / 2^ks_log2 of the reduction
+  float* part;            // GEMM1 with a K split: fp32 partial sums [2^ks_log2, P, 2*Ip], then int32 [P]
+  int64_t yplane;         // GEMM2 with a K split: floats between the y planes of the K pieces
 };
+
+// K split of the grouped GEMMs for small batches.  When few (M block, N tile)
+// items exist, each is cut into 2, 4 or 8 pieces along K so that every CU
+// streams weights: GEMM1 pieces store fp32 partial sums that
+// launch_swiglu_requant adds in piece order before the clamped SwiGLU and
+// the re-quantisation; GEMM2 pieces store their own y plane and the combine
+// adds the planes.  Only batches of at most kSplitMaxPairs pairs are split.
+constexpr int kSplitMaxPairs = 1024;
+constexpr int kSplitMax = 8;
+// Largest split a GEMM with KB 128-wide K blocks can take (pieces of whole
+// dwords of UE8M0/E8M0 scale bytes, i.e. multiples of 4 K blocks, for the MX
+// and UE8M0 modes; at least 4 K blocks per piece).
+int ksplit_cap(int mode, int KB);
+bool ksplit_ok(int mode, int KB, int ks);
+// The split the library uses for a GEMM of n_tiles N tiles per block and KB
+// K blocks, for T tokens: the largest whose pieces do not outnumber the
+// workgroups (one per CU), from the expected number of active experts under
+// uniform routing.  Host-only; depends on the device's CU count.
+int pick_ksplit(int mode, int T, int E, int k, int block_m, int KB, int n_tiles);
+
+// GEMM1 with a K split (ks = 2, 4 or 8), second half: for each pair f < P,
+// h = sum over pieces of part[piece, f], then the clamped SwiGLU and the
+// re-quantisation of the fused GEMM1 epilogue, into the pair's sorted row
+// (which GEMM1 stored after the partial sums; it also zeroed the pad rows).
+hipError_t launch_swiglu_requant(int mode, const float* part, int ks, int P, int Ip, float limit, uint8_t* aq,
+                                 void* as, hipStream_t s);
 
 // Columns of the per-pair GEMM2 rows y kept at once: all Hp when P * Hp
 // fp32 values fit in kYChunkBytes, else the largest multiple of 256 that
@@ -100,8 +129,9 @@ inline int64_t y_reserve_bytes(int64_t pairs, int64_t Hp) {
 hipError_t launch_gemm1(int mode, int block_m, int nb, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2(int mode, int block_m, int nb, const GemmArgs& a, hipStream_t s);
 
-// out[t, c0 + h] for h < cols from y rows [T*k, ldy] (pair t*k + j).
-hipError_t launch_combine(const float* y, int T, int k, int c0, int cols, int64_t ldy, uint16_t* out,
-                          int64_t ld_out, hipStream_t s);
+// out[t, c0 + h] for h < cols from y rows [T*k, ldy] (pair t*k + j), summed
+// over nplanes planes `plane` floats apart.
+hipError_t launch_combine(const float* y, int T, int k, int c0, int cols, int64_t ldy, int nplanes, int64_t plane,
+                          uint16_t* out, int64_t ld_out, hipStream_t s);
 
 }  // namespace moe

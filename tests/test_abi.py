@@ -221,3 +221,67 @@ def test_pick_block_m():
     assert M.pick_block_m(4096, 288, 8) == 128
     assert M.pick_block_m(600, 288, 8) == 32
     assert M.pick_block_m(2048, 288, 8) == 128
+
+
+def test_ksplit_plan_and_scratch():
+    """The K split of small batches: usable splits, the planned split (from
+    the expected number of active experts; this host has no GPU, so the
+    library assumes 256 compute units), and scratch sizes within the layer
+    workspace."""
+    c = cfg()  # 288 experts, top-8, H=4096, I=1024, block_m 16
+    # decode, one token: 8 experts x 8 N tiles = 64 GEMM1 items -> 4 pieces
+    # (256 pieces for 256 workgroups); GEMM2: 128 items -> 2 pieces
+    assert M.plan_ksplit(c, 1, 13) == 4 and M.plan_ksplit(c, 1, 2) == 2
+    # two tokens: ~15.8 experts, 126 GEMM1 items -> 2 pieces; GEMM2 none
+    assert M.plan_ksplit(c, 2, 13) == 2 and M.plan_ksplit(c, 2, 2) == 1
+    # 64 tokens: ~240 active experts, every workgroup has items: no split
+    assert M.plan_ksplit(c, 64, 13) == 1 and M.plan_ksplit(c, 64, 2) == 1
+    # a shared expert (E = 1, top-1): 8 GEMM1 items -> 8 pieces
+    assert M.plan_ksplit(cfg(num_experts=1, top_k=1, block_m=128), 64, 13) == 8
+    # above 1024 pairs: never split
+    assert M.plan_ksplit(c, 129, 13) == 1 and M.plan_ksplit(c, 4096, 2) == 1
+    assert M.plan_ksplit(c, 1, 7) == -1
+    P = 64 * 8
+    for ks in (1, 2, 4, 8):
+        assert M.splitk_bytes(c, 64, 13, ks) == (0 if ks == 1 else ks * P * 2048 * 4 + P * 4)
+    assert M.splitk_bytes(c, 64, 2, 2) == 2 * P * 4096 * 4
+    assert M.splitk_bytes(c, 64, 2, 1) == P * 4096 * 4
+    # unusable: not a power of two up to 8, pieces under 4 K blocks, or (MX,
+    # UE8M0) not whole dwords of 4 scale bytes, or too many pairs
+    assert M.splitk_bytes(c, 64, 13, 3) == 0 and M.splitk_bytes(c, 64, 13, 16) == 0
+    assert M.splitk_bytes(c, 64, 2, 4) == 0          # 2 K blocks per piece
+    assert M.splitk_bytes(c, 129, 13, 2) == 0        # 1032 pairs
+    c24 = cfg(hidden=3072)                           # 24 K blocks
+    assert M.splitk_bytes(c24, 4, 13, 4) > 0         # FP8: 6 K blocks per piece
+    for q in ("mxfp4", "fp8_ue8m0"):
+        assert M.splitk_bytes(cfg(quant=q, hidden=3072), 4, 13, 4) == 0
+        assert M.splitk_bytes(cfg(quant=q, hidden=3072), 4, 13, 2) > 0
+        assert M.plan_ksplit(cfg(quant=q, hidden=3072), 1, 13) == 2
+    # every planned split fits the layer workspace, which stays monotone
+    for q in ("fp8", "mxfp4", "fp8_ue8m0"):
+        for E, k, bm in ((288, 8, 16), (1, 1, 128), (16, 4, 32)):
+            cc = cfg(quant=q, num_experts=E, top_k=k, block_m=bm)
+            for T in (1, 2, 5, 16, 64, 128, 300):
+                need = max(M.splitk_bytes(cc, T, 2, M.plan_ksplit(cc, T, 2)),
+                           M.splitk_bytes(cc, T, 13, M.plan_ksplit(cc, T, 13)))
+                assert 0 < need <= M.workspace_bytes(cc, T)
+    # unsplit GEMM2 of a batch whose y rows are column-chunked (P * Hp * 4 > 1 GiB)
+    cc = cfg(num_experts=8, hidden=2100, inter=256, block_m=64)
+    assert 0 < M.splitk_bytes(cc, 16384, 2, 1) <= M.workspace_bytes(cc, 16384)
+    assert M.splitk_bytes(cc, 16384, 2, 1) < 16384 * 8 * 2176 * 4
+
+
+def test_ksplit_entry_points_validate_before_launch():
+    lib = M.lib()
+    c = cfg()
+    big = 1 << 40
+    args1 = [ctypes.byref(c), 4] + [FAKE] * 9
+    assert lib.moe_grouped_gemm1_swiglu_splitk(*args1, 3, FAKE, big, None) == UNSUP
+    assert lib.moe_grouped_gemm1_swiglu_splitk(*args1, 16, FAKE, big, None) == UNSUP
+    assert lib.moe_grouped_gemm1_swiglu_splitk(*args1, 2, FAKE, 1024, None) == WS
+    assert lib.moe_grouped_gemm1_swiglu_splitk(*args1, 2, None, big, None) == NULL
+    args2 = [ctypes.byref(c), 4] + [FAKE] * 9 + [4096]
+    assert lib.moe_grouped_gemm2_combine_splitk(*args2, 4, FAKE, big, None) == UNSUP
+    assert lib.moe_grouped_gemm2_combine_splitk(*args2, 2, FAKE, 1024, None) == WS
+    assert lib.moe_grouped_gemm2_combine_splitk(*args2[:-1], 100, 2, FAKE, big, None) == SHAPE
+    assert lib.moe_grouped_gemm2_combine(*args2, FAKE, 1024, None) == WS

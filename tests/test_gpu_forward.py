@@ -190,7 +190,8 @@ def test_forward_repeatable_and_equal_to_stages(mode, T):
     ids, wts = M.moe_route_topk(lgd, wl.top_k)
     sid, bexp, offs, npp = M.moe_permute_align(ids, wl.E, 32)
     xq, xs = M.moe_quant_act(xd, wl.Hp, mode)
-    aq, as_ = M.moe_grouped_gemm1_swiglu(cfg, wl.T, xq, xs, sid, bexp, npp, ew.w13, ew.w13_scale)
+    aq, as_ = M.moe_grouped_gemm1_swiglu(cfg, wl.T, xq, xs, sid, bexp, npp, ew.w13, ew.w13_scale,
+                                         ksplit=M.plan_ksplit(cfg, wl.T, 13))
     out3 = M.moe_grouped_gemm2_combine(cfg, wl.T, aq, as_, sid, bexp, npp, ew.w2, ew.w2_scale, wts)
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))

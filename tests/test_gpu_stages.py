@@ -241,7 +241,7 @@ def test_gemm1_swiglu_stage(mode, BM):
     cfg = M.make_cfg(wl.E, wl.top_k, mode, wl.H, wl.I, block_m=BM)
     x = W.activations(wl)
     lg = W.router_logits(wl)
-    from parity_util import gpu_weights, oracle_weights_cpu
+    from parity_util import check_gemm1_intermediate, gpu_weights, oracle_weights_cpu
     ew = gpu_weights(M, cfg, wl, source="cpu")
     xd, lgd = x.cuda(), lg.cuda()
     ids, wts = M.moe_route_topk(lgd, wl.top_k)
@@ -252,59 +252,7 @@ def test_gemm1_swiglu_stage(mode, BM):
     Q = oracle_weights_cpu(wl)
     _, st = O.moe_forward(x.float().numpy(), lg.numpy(), Q, wl.top_k, wl.swiglu_limit, wl.H, wl.I,
                           return_stages=True)
-    sid_h = sid.cpu().numpy()
-    P = wl.T * wl.top_k
-    rows = aq.numel() // (wl.Ip if mode != "mxfp4" else wl.Ip // 2)
-    aq_h = aq.cpu().numpy().reshape(rows, -1)
-    if mode == "fp8":
-        as_h = as_.cpu().numpy().view(np.float32).reshape(rows, -1)
-    elif mode == "fp8_ue8m0":
-        as_h = as_.cpu().numpy().reshape(rows, -1)[:, :wl.Ip // 128]
-    else:
-        as_h = as_.cpu().numpy().reshape(rows, -1)
-    total = mism = scale_moves = 0
-    worst_scale = worst_val = 0.0
-    for r in range(int(npp.item())):
-        f = int(sid_h[r])
-        if f >= P:
-            assert np.all(aq_h[r] == 0) and np.all(as_h[r] == 0), "pad rows are zero"
-            continue
-        qo, so = st["aq"][(f // wl.top_k, f % wl.top_k)]
-        if mode == "fp8":
-            # the scale is amax/448 of the fp32 intermediate: it inherits the
-            # GEMM's accumulation-order difference
-            rel = np.abs(as_h[r].astype(np.float64) - so) / np.maximum(so, 1e-30)
-            worst_scale = max(worst_scale, float(rel.max()))
-            dg = O.dequant_fp8_rows(aq_h[r][None], as_h[r][None])[0]
-            do = O.dequant_fp8_rows(qo[None], so[None])[0]
-            step = 32.0 / 448.0          # one code step at the top binade, relative to amax
-        elif mode == "fp8_ue8m0":
-            # a power-of-two scale: only an amax at a scale boundary (a tie) may
-            # move it, by one binade
-            dsc = np.abs(as_h[r].astype(np.int64) - so.astype(np.int64))
-            assert dsc.max() <= 1
-            scale_moves += int(np.count_nonzero(dsc))
-            dg = O.dequant_fp8e8_rows(aq_h[r][None], as_h[r][None])[0]
-            do = O.dequant_fp8e8_rows(qo[None], so[None])[0]
-            # one top-binade step of the larger scale, relative to the
-            # smallest amax a scale covers (224 * 2^e)
-            step = 2 * 32.0 / 224.0 if dsc.max() else 32.0 / 224.0
-        else:
-            dg = O.dequant_mxfp4_rows(aq_h[r][None], as_h[r][None])[0]
-            do = O.dequant_mxfp4_rows(qo[None], so[None])[0]
-            step = 2.0 / 4.0             # E2M1 step 2 at the top, amax >= 4 units
-        amax = np.abs(do).max()
-        total += aq_h[r].size
-        mism += int(np.count_nonzero(aq_h[r] != qo))
-        if amax > 0:
-            worst_val = max(worst_val, float(np.abs(dg - do).max() / amax) / step)
-    log(f"  intermediate: {mism} of {total} code bytes differ; worst |deq diff|/(amax*step) {worst_val:.3e}; "
-        f"worst FP8 scale rel diff {worst_scale:.2e}")
-    # accumulation-order differences move a code by at most one step at a rounding boundary
-    assert worst_val <= 1.01
-    assert mism <= max(8, 0.01 * total)
-    assert worst_scale <= 1e-3
-    assert scale_moves <= 4
+    check_gemm1_intermediate(wl, aq, as_, sid, npp, st)
 
 
 @pytest.mark.parametrize("T,E,k,BM,mode,ldpad", [(1, 288, 8, 16, "fp8", 0), (7, 288, 8, 16, "mxfp4", 24),
