@@ -83,9 +83,14 @@ enum {
 enum { MOE_GATE_SEPARATED = 0, MOE_GATE_INTERLEAVED = 1 };
 
 /* Weight layout tags.  CANONICAL is row-major [E, N, K] (what
- * moe_quant_weights writes).  TILED_V1 is the GEMM kernels' layout, written
- * only by moe_preshuffle_weights (the runner owns its preshuffle). */
-enum { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_TILED_V1 = 0x4D310001 };
+ * moe_quant_weights writes).  TILED_V2 is the GEMM kernels' layout, written
+ * only by moe_preshuffle_weights (the runner owns its preshuffle): 16-row x
+ * 128-column MFMA tiles ordered [E][N tile][K block][16 tiles], an N tile
+ * being the 256 weight rows one GEMM work item multiplies (w13: 128 gate
+ * rows and the matching 128 up rows; w2: 256 rows, a half last N tile
+ * zero-padded).  The earlier TILED_V1 tag (tiles ordered [E][N/16][K/128])
+ * is no longer accepted. */
+enum { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_TILED_V2 = 0x4D310002 };
 
 /* Element types accepted by moe_quant_act / moe_quant_weights. */
 enum { MOE_DTYPE_BF16 = 1, MOE_DTYPE_F32 = 2 };
@@ -104,7 +109,7 @@ typedef struct {
   int32_t top_k;         /* k, 1..min(16, E) */
   int32_t quant_mode;    /* MOE_QUANT_* */
   int32_t gate_mode;     /* must be MOE_GATE_SEPARATED */
-  int32_t weight_layout; /* must be MOE_LAYOUT_TILED_V1 for the GEMM entry points */
+  int32_t weight_layout; /* must be MOE_LAYOUT_TILED_V2 for the GEMM entry points */
   int32_t block_m;       /* rows per expert block: 16, 32, 64 or 128 */
   float swiglu_limit;    /* L > 0; +inf gives plain SwiGLU; NaN rejected */
   moe_pad_t pad;
@@ -206,14 +211,16 @@ moe_status_t moe_route_permute_quant(const moe_cfg_t* cfg, int32_t T, const floa
 moe_status_t moe_quant_weights(int32_t quant_mode, const float* w, int32_t E, int32_t N,
                                int32_t K, void* q, void* scales, void* stream);
 
-/* Sizes of the TILED_V1 buffers for w13 (which = 13: N = 2*Ip, K = Hp) or
- * w2 (which = 2: N = Hp, K = Ip).  TILED_V1 holds FP8_UE8M0 block scales as
- * their exact fp32 values 2^(b-127), [E, N/128, K/128]. */
+/* Sizes of the TILED_V2 buffers for w13 (which = 13: N = 2*Ip, K = Hp) or
+ * w2 (which = 2: N = Hp, K = Ip): whole N tiles, E * ceil(N/256) * (K/128)
+ * tiles of 16 (2 KB FP8 / 1 KB MXFP4 each).  Block scales of FP8 stay
+ * [E, N/128, K/128] f32 (FP8_UE8M0: the bytes' exact fp32 values
+ * 2^(b-127)); MXFP4 scales are E8M0 words [E][N tile][ceil(K/512)][16][64]. */
 moe_status_t moe_preshuffled_bytes(const moe_cfg_t* cfg, int32_t which, size_t* w_bytes,
                                    size_t* s_bytes);
 
 /* Rewrites CANONICAL quantised weights (moe_quant_weights' output for the
- * padded matrix of `which`) into TILED_V1, the only layout the GEMM entry
+ * padded matrix of `which`) into TILED_V2, the only layout the GEMM entry
  * points read (sglang PR #38546, contract table: the runner owns its
  * preshuffle).  Ignores cfg->weight_layout.  Output sizes from
  * moe_preshuffled_bytes.  In and out must not overlap. */
@@ -229,7 +236,7 @@ moe_status_t moe_preshuffle_weights(const moe_cfg_t* cfg, int32_t which, const v
  * Pad rows (f = T*k) get all-zero codes and zero scales.
  * xq/xs: moe_quant_act output for x (FP8: u8 [T, Hp] + f32 [T, Hp/128];
  * MXFP4: u8 [T, Hp/2] + u8 [T, Hp/32]; FP8_UE8M0: u8 [T, Hp] + u8
- * [T, round_up(Hp/128, 4)]).  w13/w13_scale: TILED_V1.
+ * [T, round_up(Hp/128, 4)]).  w13/w13_scale: TILED_V2.
  * aq/as: sizes from moe_intermediate_bytes, indexed by sorted position, in
  * the activation format of the mode over Ip columns (FP8_UE8M0: the scale
  * bytes past Ip/128 in each row are unspecified). */
@@ -298,7 +305,7 @@ moe_status_t moe_grouped_gemm2_combine_splitk(const moe_cfg_t* cfg, int32_t T, c
 
 /* The whole layer: route, permute, quantise x, GEMM1+SwiGLU, GEMM2+combine,
  * all on `stream` with no host synchronisation.  x: bf16 [T, ld_x] (H valid
- * columns); router_logits f32 [T, E]; weights TILED_V1; out bf16 [T, ld_out].
+ * columns); router_logits f32 [T, E]; weights TILED_V2; out bf16 [T, ld_out].
  * ws: at least moe_workspace_bytes(cfg, T) bytes. */
 moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, int64_t ld_x,
                          const float* router_logits, const void* w13, const void* w13_scale,

@@ -26,7 +26,7 @@ MOE_QUANT_FP8_UE8M0 = 3
 MOE_GATE_SEPARATED = 0
 MOE_GATE_INTERLEAVED = 1
 MOE_LAYOUT_CANONICAL = 0
-MOE_LAYOUT_TILED_V1 = 0x4D310001
+MOE_LAYOUT_TILED_V2 = 0x4D310002
 MOE_DTYPE_BF16 = 1
 MOE_DTYPE_F32 = 2
 QUANT_MODES = {"fp8": MOE_QUANT_FP8_BLOCK, "mxfp4": MOE_QUANT_MXFP4, "fp8_ue8m0": MOE_QUANT_FP8_UE8M0}
@@ -122,7 +122,7 @@ def lib() -> ctypes.CDLL:
 def make_cfg(num_experts: int, top_k: int, quant: str | int, hidden: int, inter: int,
              hidden_padded: int | None = None, inter_padded: int | None = None, block_m: int = 16,
              swiglu_limit: float = 10.0, gate_mode: int = MOE_GATE_SEPARATED,
-             weight_layout: int = MOE_LAYOUT_TILED_V1, validate: bool = True) -> MoeCfg:
+             weight_layout: int = MOE_LAYOUT_TILED_V2, validate: bool = True) -> MoeCfg:
     """Builds (and by default validates) a moe_cfg_t."""
     qm = QUANT_MODES[quant] if isinstance(quant, str) else int(quant)
     hp = hidden_padded if hidden_padded is not None else -(-hidden // 128) * 128
@@ -296,7 +296,7 @@ def moe_quant_weights(w: torch.Tensor, quant: str | int, stream=None):
 
 
 def moe_preshuffle_weights(cfg: MoeCfg, which: int, q: torch.Tensor, s: torch.Tensor, stream=None):
-    """CANONICAL -> TILED_V1 for w13 (which=13) or w2 (which=2); flat uint8 outputs."""
+    """CANONICAL -> TILED_V2 for w13 (which=13) or w2 (which=2); flat uint8 outputs."""
     wb, sb = preshuffled_bytes(cfg, which)
     qo = torch.empty(wb, dtype=torch.uint8, device=q.device)
     so = torch.empty(sb, dtype=torch.uint8, device=q.device)
@@ -412,7 +412,7 @@ class ExpertWeights:
         self.s2[first:first + n] = s
 
     def finalize(self):
-        """Preshuffles the canonical buffers into TILED_V1 (and keeps both)."""
+        """Preshuffles the canonical buffers into TILED_V2 (and keeps both)."""
         self.w13, self.w13_scale = moe_preshuffle_weights(self.cfg, 13, self.q13, self.s13)
         self.w2, self.w2_scale = moe_preshuffle_weights(self.cfg, 2, self.q2, self.s2)
         return self

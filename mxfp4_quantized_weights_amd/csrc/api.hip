@@ -71,7 +71,7 @@ moe_status_t check_tokens(const moe_cfg_t* c, int32_t T) {
 }
 
 moe_status_t check_layout(const moe_cfg_t* c) {
-  return c->weight_layout == MOE_LAYOUT_TILED_V1 ? MOE_OK : MOE_ERR_LAYOUT;
+  return c->weight_layout == MOE_LAYOUT_TILED_V2 ? MOE_OK : MOE_ERR_LAYOUT;
 }
 
 int32_t max_blocks(int64_t P, int32_t E, int32_t BM) {
@@ -173,6 +173,7 @@ moe::GemmArgs gemm1_args(const moe_cfg_t* c, int32_t T, const void* xq, const vo
   a.Bs = s13;
   a.N = 2 * Ip;
   a.K = Hp;
+  a.tile_run = moe::tile_run(c->quant_mode, 13);
   a.n_tiles = Ip / 128;
   a.aq = (uint8_t*)aq;
   a.as = as;
@@ -200,6 +201,7 @@ moe::GemmArgs gemm2_args(const moe_cfg_t* c, int32_t T, const void* aq, const vo
   a.Bs = s2;
   a.N = Hp;
   a.K = Ip;
+  a.tile_run = moe::tile_run(c->quant_mode, 2);
   a.n_tiles = (Hp + 255) / 256;
   a.Ip = Ip;
   a.limit = c->swiglu_limit;
@@ -386,13 +388,14 @@ moe_status_t moe_preshuffled_bytes(const moe_cfg_t* cfg, int32_t which, size_t* 
   if (!w_bytes || !s_bytes) return MOE_ERR_NULL;
   const int64_t E = cfg->num_experts, Hp = cfg->pad.hidden_padded, Ip = cfg->pad.inter_padded;
   const int64_t N = which == 13 ? 2 * Ip : Hp, K = which == 13 ? Hp : Ip;
+  // whole N tiles of 16 row tiles (a half last N tile of w2 is zero-padded)
+  const int64_t NG = moe::tiled_n_groups((int)N), KB = K / 128;
   if (fp8_codes(cfg->quant_mode)) {  // UE8M0 scales are widened to fp32
-    *w_bytes = (size_t)(E * N * K);
-    *s_bytes = (size_t)(E * (N / 128) * (K / 128) * 4);
+    *w_bytes = (size_t)(E * NG * KB * 16 * 2048);
+    *s_bytes = (size_t)(E * (N / 128) * KB * 4);
   } else {
-    const int64_t KB = K / 128;
-    *w_bytes = (size_t)(E * N * K / 2);
-    *s_bytes = (size_t)(E * (N / 16) * ((KB + 3) / 4) * 64 * 4);
+    *w_bytes = (size_t)(E * NG * KB * 16 * 1024);
+    *s_bytes = (size_t)(E * NG * ((KB + 3) / 4) * 16 * 64 * 4);
   }
   return MOE_OK;
 }
@@ -405,8 +408,10 @@ moe_status_t moe_preshuffle_weights(const moe_cfg_t* cfg, int32_t which, const v
   if (!w || !s || !w_out || !s_out) return MOE_ERR_NULL;
   const int Hp = cfg->pad.hidden_padded, Ip = cfg->pad.inter_padded;
   const int N = which == 13 ? 2 * Ip : Hp, K = which == 13 ? Hp : Ip;
-  return hip_status(moe::launch_preshuffle(cfg->quant_mode, (const uint8_t*)w, s, cfg->num_experts, N, K, (uint8_t*)w_out,
-                                           s_out, as_stream(stream)));
+  const int gate_half = which == 13 ? Ip / 16 : 0;
+  return hip_status(moe::launch_preshuffle(cfg->quant_mode, (const uint8_t*)w, s, cfg->num_experts, N, K, gate_half,
+                                           moe::tile_run(cfg->quant_mode, which), (uint8_t*)w_out, s_out,
+                                           as_stream(stream)));
 }
 
 moe_status_t moe_grouped_gemm1_swiglu(const moe_cfg_t* cfg, int32_t T, const void* xq, const void* xs,

@@ -69,7 +69,8 @@ __device__ __forceinline__ void widen_fp8(const v8i& w, v8h (&h)[4]) {
 // (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16*l), through a
 // ring of S K-block slots, so S-1 K blocks are in flight per workgroup without
 // holding them in registers.  The weight tiles are copied verbatim from the
-// TILED_V1 layout, which already is MFMA fragment order; the gathered token
+// TILED_V2 layout, which already is MFMA fragment order and holds an item's
+// 16 tiles of one K block as one contiguous run; the gathered token
 // rows are placed in the same order by the per-lane source addresses.  Every
 // wave issues the same number of loads per slot, so one s_waitcnt vmcnt(N)
 // per K block plus a barrier make the slot visible to all waves.
@@ -157,18 +158,9 @@ struct RingSrc {
   const uint8_t* ts;
   const uint8_t* ws[R::DWS > 0 ? R::DWS : 1];
   const uint8_t* wsc;  // FP8, lanes 0 and 1 of the last wave: weight-scale row of K block 0
+  int wk;              // bytes between a weight tile's K blocks (tile run x tile bytes)
+  int wsk;             // MX: bytes between a scale word row's groups of 4 K blocks
 };
-
-// Weight tile t16 of local tile i (0..15) of N tile nt.
-template <bool G1>
-__device__ __forceinline__ int ring_tile(const GemmArgs& p, int nt, int i) {
-  if constexpr (G1) {
-    return (i < 8) ? nt * 8 + i : p.Ip / 16 + nt * 8 + (i - 8);
-  } else {
-    const int t = nt * 16 + i, last = p.N / 16 - 1;
-    return t < last ? t : last;  // tail tiles of a half N tile load a valid duplicate
-  }
-}
 
 // Loads of K block kb into `slot`.  Token scales: each wave fetches 16 of the
 // 64 scales of its token half (lanes 0..15 only), placed so that lane l of a
@@ -184,7 +176,7 @@ __device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const u
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(slot));
 #pragma unroll
   for (int q = 0; q < R::DW; ++q)
-    dma16<true>(src.w[q] + (int64_t)kb * R::TILE, base + R::W_OFF + (wave * R::DW + q) * 1024);
+    dma16<true>(src.w[q] + (int64_t)kb * src.wk, base + R::W_OFF + (wave * R::DW + q) * 1024);
 #pragma unroll
   for (int q = 0; q < R::DT; ++q)
     if (wave * R::DT + q < R::NTD) dma16<false>(src.t[q] + kb * R::AROW, base + R::T_OFF + (wave * R::DT + q) * 1024);
@@ -198,7 +190,7 @@ __device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const u
     if (ws != nullptr) {
       const uint32_t wbase = __builtin_amdgcn_readfirstlane(lds_addr(ws));
 #pragma unroll
-      for (int q = 0; q < R::DWS; ++q) dma4(src.ws[q] + (kb >> 2) * 256, wbase + (wave * R::DWS + q) * 256);
+      for (int q = 0; q < R::DWS; ++q) dma4(src.ws[q] + (kb >> 2) * src.wsk, wbase + (wave * R::DWS + q) * 256);
     }
   }
 }
@@ -637,7 +629,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   const int n_my = (hi - first + nw - 1) / nw;
   const int KB = p.K / 128;   // K blocks of a weight row
   const int KBI = KB >> KSL;  // K blocks of an item
-  const int NT16 = p.N / 16;
+  const int NG = tiled_n_groups(p.N);  // N tiles of the weight matrix (TILED_V2)
   const int total = n_my * KBI;
   // Items of fewer than S K blocks finish inside the prologue (which issues
   // S-1 K blocks without waiting) or within S-1 steps of the next item's
@@ -668,6 +660,8 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
 
   // ---- issue side: per-lane source addresses of the item being loaded
   RingSrc<MODE, BM> rs;
+  rs.wk = p.tile_run * R::TILE;
+  rs.wsk = p.tile_run * 256;
   int wts_step = -1, wts_item = 0;
   auto setup_issue = [&](int ii, int s) {
     const int m = item_m(ii), nt = item_nt(ii);
@@ -676,7 +670,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
 #pragma unroll
     for (int q = 0; q < R::DW; ++q) {
       const int g = wave * R::DW + q, tile = g / R::HALVES, h = g % R::HALVES;
-      rs.w[q] = p.B + (((int64_t)e * NT16 + ring_tile<G1>(p, nt, tile)) * KB + kb0) * R::TILE + h * 1024 + lane * 16;
+      rs.w[q] = p.B + tiled_index(p.tile_run, e, NG, nt, tile, KB, kb0) * R::TILE + h * 1024 + lane * 16;
     }
     const int32_t* ids = ids_lds[ii % NB];
     // rows past BM (the unused scale entries of a small block) read row 0 / the block's first row
@@ -712,7 +706,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
 #pragma unroll
       for (int q = 0; q < R::DWS; ++q)
         rs.ws[q] = (const uint8_t*)p.Bs +
-                   ((((int64_t)e * NT16 + ring_tile<G1>(p, nt, wave * R::DWS + q)) * KBq + kb0 / 4) * 64 + lane) * 4;
+                   (tiled_index(p.tile_run, e, NG, nt, wave * R::DWS + q, KBq, kb0 / 4) * 64 + lane) * 4;
     }
     // metadata of the next item: ids now; GEMM2 weights S-1 steps later,
     // once the ring's waits have covered the ids (or right away after an

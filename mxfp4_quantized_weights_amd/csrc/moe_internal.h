@@ -43,7 +43,40 @@ hipError_t launch_quant_rows(const void* in, bool in_is_bf16, int64_t rows, int 
 hipError_t launch_quant_weight_fp8(int mode, const float* w, int E, int N, int K, uint8_t* q, void* scales,
                                    hipStream_t s);
 
-hipError_t launch_preshuffle(int mode, const uint8_t* w, const void* sc, int E, int N, int K,
+// TILED_V2 weight layout: a matrix's 16-row tiles are grouped into N tiles of
+// 16 (the 256 weight rows one GEMM item multiplies), each K block of an N
+// tile in contiguous runs of tiles (below).  For w13 (gate_half = Ip/16 > 0) N tile g holds gate row
+// tiles 8g .. 8g+7 and then the matching up row tiles gate_half + 8g ..;
+// for w2 (gate_half = 0) row tiles 16g .. 16g+15, the positions past N/16
+// of a last, half N tile holding zeros.
+__host__ __device__ inline int tiled_n_groups(int N) { return (N + 255) / 256; }
+__host__ __device__ inline int tiled_row_tile(int gate_half, int N, int g, int i) {
+  if (gate_half > 0) return i < 8 ? 8 * g + i : gate_half + 8 * g + (i - 8);
+  const int t = 16 * g + i;
+  return t < N / 16 ? t : -1;
+}
+// Within an N tile, runs of R positions (the tile run) are contiguous per K
+// block: tiles are ordered [E][N tile][16 / R][K block][R], so tile position
+// i of N tile g at K block kb sits at tile index
+// (((e * NG + g) * (16 / R) + i / R) * KB + kb) * R + i % R, and stepping one
+// K block moves every position by R tiles.  MX scale word rows follow the
+// same order, groups of 4 K blocks taking the place of K blocks.
+__host__ __device__ inline int64_t tiled_index(int R, int64_t e, int NG, int g, int i, int KB, int kb) {
+  return ((((e * NG + g) * (16 / R) + i / R) * KB + kb) * R) + i % R;
+}
+// The tile run of each matrix, fixed by the quantisation mode and the matrix
+// (13: w13, 2: w2); measured on the MI355X (all layouts give bit-identical
+// results): whole 16-tile runs stream fastest for a purely streaming item
+// list (block-FP8 w13 at small batches), runs of 4 suit w2 at every batch,
+// and MXFP4 w13 at large batches is fastest with single tiles.
+inline int tile_run(int mode, int which) {
+  if (which == 2) return 4;
+  return mode == kQuantMx ? 1 : 16;
+}
+
+// CANONICAL -> TILED_V2 (gate_half as above: Ip/16 for w13, 0 for w2; tile
+// run R from tile_run).
+hipError_t launch_preshuffle(int mode, const uint8_t* w, const void* sc, int E, int N, int K, int gate_half, int R,
                              uint8_t* w_out, void* s_out, hipStream_t s);
 
 struct GemmArgs {
@@ -56,7 +89,7 @@ struct GemmArgs {
   const int32_t* npp;
   int32_t top_k;
   int32_t num_pairs;
-  const uint8_t* B;       // TILED_V1 weights
+  const uint8_t* B;       // TILED_V2 weights
   const void* Bs;         // FP8, UE8M0: f32 block scales [E, N/128, K/128]; MX: tiled scale dwords
   int32_t N;              // weight rows per expert (padded)
   int32_t K;              // reduction length (padded)
@@ -72,6 +105,7 @@ struct GemmArgs {
   int32_t ks_log2;        // K split: each item covers K / 2^ks_log2 of the reduction
   float* part;            // GEMM1 with a K split: fp32 partial sums [2^ks_log2, P, 2*Ip], then int32 [P]
   int64_t yplane;         // GEMM2 with a K split: floats between the y planes of the K pieces
+  int32_t tile_run;       // TILED_V2 tile run R of B (tile_run(mode, which))
 };
 
 // K split of the grouped GEMMs for small batches.  When few (M block, N tile)

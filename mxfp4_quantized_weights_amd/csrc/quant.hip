@@ -133,73 +133,103 @@ hipError_t launch_quant_weight_fp8(int mode, const float* w, int E, int N, int K
 }
 
 // ---------------------------------------------------------------------------
-// TILED_V1 preshuffle.  For each expert, 16-row tile nt and 128-wide K block
-// kb, the kernels' B operand is one MFMA 16x16x128 tile: lane l needs row
-// nt*16 + l%16 and K values kb*128 + 32*(l/16) .. +32.
+// TILED_V2 preshuffle.  For each expert, 16-row tile and 128-wide K block kb,
+// the kernels' B operand is one MFMA 16x16x128 tile: lane l needs the tile's
+// row l%16 and K values kb*128 + 32*(l/16) .. +32.
 //   FP8: tile = 2048 bytes, [h (2)][lane (64)][16 bytes]: half h holds the
 //        lane's K bytes 16h .. 16h+15, so each 16-byte wave load is 1 KB
 //        contiguous.  Block scales stay canonical f32 [E, N/128, K/128].
 //   UE8M0 FP8: the same tiles; the scale bytes are widened to their exact
 //        fp32 values 2^(b-127) in the canonical [E, N/128, K/128] order.
 //   MX:  tile = 1024 bytes, [lane (64)][16 bytes] (32 packed E2M1).  Scales:
-//        per (expert, nt) and group of 4 K blocks, [lane (64)][4 bytes], byte
-//        i = E8M0 of K block 4q+i for the lane's row and 32-group; missing K
-//        blocks (K/128 not a multiple of 4) hold 0.
-// Tiles are ordered [E][N/16][K/128] so a wave streams K contiguously.
+//        per (expert, N tile, group of 4 K blocks, tile position) one
+//        [lane (64)][4 bytes] word row, byte i = E8M0 of K block 4q+i for
+//        the lane's row and 32-group; missing K blocks (K/128 not a multiple
+//        of 4) hold 0.
+// Tiles are ordered [E][N tile][16 / R][K block][R] for the matrix's tile
+// run R (tiled_row_tile names the row tile at each position 0..15,
+// tiled_index the storage order), so the tiles one GEMM item needs at one K
+// block come in contiguous runs of R tiles.  MX scale word rows follow the
+// same order with groups of 4 K blocks in place of K blocks.
+// Positions without a row tile (a half last N tile of w2) hold zeros.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void preshuffle_fp8_kernel(const uint8_t* __restrict__ w, int64_t total_chunks,
-                                                             int N, int K, uint8_t* __restrict__ out) {
-  const int KB = K / 128, NT = N / 16;
+                                                             int N, int K, int gate_half, int R, uint8_t* __restrict__ out) {
+  const int KB = K / 128, NG = tiled_n_groups(N);
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total_chunks; c += (int64_t)gridDim.x * 256) {
-    int64_t tile = c >> 7;
-    int within = (int)(c & 127);
-    int h = within >> 6, l = within & 63;
-    int kb = (int)(tile % KB);
-    int64_t en = tile / KB;
-    int nt = (int)(en % NT);
-    int64_t e = en / NT;
-    int64_t row = (int64_t)nt * 16 + (l & 15);
-    int64_t col = (int64_t)kb * 128 + 32 * (l >> 4) + 16 * h;
-    uint4 v = *(const uint4*)(w + (e * N + row) * (int64_t)K + col);
+    const int within = (int)(c & 127);
+    const int h = within >> 6, l = within & 63;
+    int64_t rest = c >> 7;  // storage tile index
+    const int ir = (int)(rest % R);
+    rest /= R;
+    const int kb = (int)(rest % KB);
+    rest /= KB;
+    const int i = (int)(rest % (16 / R)) * R + ir;
+    rest /= 16 / R;
+    const int g = (int)(rest % NG);
+    const int64_t e = rest / NG;
+    const int rt = tiled_row_tile(gate_half, N, g, i);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (rt >= 0) {
+      const int64_t row = (int64_t)rt * 16 + (l & 15);
+      const int64_t col = (int64_t)kb * 128 + 32 * (l >> 4) + 16 * h;
+      v = *(const uint4*)(w + (e * N + row) * (int64_t)K + col);
+    }
     *(uint4*)(out + c * 16) = v;
   }
 }
 
 __global__ __launch_bounds__(256) void preshuffle_mx_kernel(const uint8_t* __restrict__ w, int64_t total_chunks,
-                                                            int N, int K, uint8_t* __restrict__ out) {
-  const int KB = K / 128, NT = N / 16;
+                                                            int N, int K, int gate_half, int R, uint8_t* __restrict__ out) {
+  const int KB = K / 128, NG = tiled_n_groups(N);
   const int64_t ldw = K / 2;
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total_chunks; c += (int64_t)gridDim.x * 256) {
-    int64_t tile = c >> 6;
-    int l = (int)(c & 63);
-    int kb = (int)(tile % KB);
-    int64_t en = tile / KB;
-    int nt = (int)(en % NT);
-    int64_t e = en / NT;
-    int64_t row = (int64_t)nt * 16 + (l & 15);
-    int64_t col = (int64_t)kb * 64 + 16 * (l >> 4);
-    uint4 v = *(const uint4*)(w + (e * N + row) * ldw + col);
+    const int l = (int)(c & 63);
+    int64_t rest = c >> 6;  // storage tile index
+    const int ir = (int)(rest % R);
+    rest /= R;
+    const int kb = (int)(rest % KB);
+    rest /= KB;
+    const int i = (int)(rest % (16 / R)) * R + ir;
+    rest /= 16 / R;
+    const int g = (int)(rest % NG);
+    const int64_t e = rest / NG;
+    const int rt = tiled_row_tile(gate_half, N, g, i);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (rt >= 0) {
+      const int64_t row = (int64_t)rt * 16 + (l & 15);
+      const int64_t col = (int64_t)kb * 64 + 16 * (l >> 4);
+      v = *(const uint4*)(w + (e * N + row) * ldw + col);
+    }
     *(uint4*)(out + c * 16) = v;
   }
 }
 
 __global__ __launch_bounds__(256) void preshuffle_mx_scale_kernel(const uint8_t* __restrict__ s, int64_t total_words,
-                                                                  int N, int K, uint32_t* __restrict__ out) {
-  const int KB = K / 128, KB4 = (KB + 3) / 4, NT = N / 16;
+                                                                  int N, int K, int gate_half, int R,
+                                                                  uint32_t* __restrict__ out) {
+  const int KB = K / 128, KB4 = (KB + 3) / 4, NG = tiled_n_groups(N);
   const int64_t lds = K / 32;
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < total_words; c += (int64_t)gridDim.x * 256) {
-    int l = (int)(c & 63);
-    int64_t rest = c >> 6;
-    int kq = (int)(rest % KB4);
-    int64_t en = rest / KB4;
-    int nt = (int)(en % NT);
-    int64_t e = en / NT;
-    int64_t row = (int64_t)nt * 16 + (l & 15);
+    const int l = (int)(c & 63);
+    int64_t rest = c >> 6;  // storage word-row index, ordered as the tiles with K groups of 4 blocks
+    const int ir = (int)(rest % R);
+    rest /= R;
+    const int kq = (int)(rest % KB4);
+    rest /= KB4;
+    const int i = (int)(rest % (16 / R)) * R + ir;
+    rest /= 16 / R;
+    const int g = (int)(rest % NG);
+    const int64_t e = rest / NG;
+    const int rt = tiled_row_tile(gate_half, N, g, i);
     uint32_t word = 0;
+    if (rt >= 0) {
+      const int64_t row = (int64_t)rt * 16 + (l & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int kb = kq * 4 + i;
-      if (kb < KB) word |= (uint32_t)s[(e * N + row) * lds + kb * 4 + (l >> 4)] << (8 * i);
+      for (int j = 0; j < 4; ++j) {
+        const int kb = kq * 4 + j;
+        if (kb < KB) word |= (uint32_t)s[(e * N + row) * lds + kb * 4 + (l >> 4)] << (8 * j);
+      }
     }
     out[c] = word;
   }
@@ -223,13 +253,14 @@ static unsigned grid_for(int64_t items) {
   return (unsigned)b;
 }
 
-hipError_t launch_preshuffle(int mode, const uint8_t* w, const void* sc, int E, int N, int K,
+hipError_t launch_preshuffle(int mode, const uint8_t* w, const void* sc, int E, int N, int K, int gate_half, int R,
                              uint8_t* w_out, void* s_out, hipStream_t s) {
-  const int64_t KB = K / 128, NT = N / 16;
+  const int64_t KB = K / 128, NG = tiled_n_groups(N);
   if (mode == kQuantFp8 || mode == kQuantFp8E8) {
-    int64_t chunks = (int64_t)E * NT * KB * 128;
-    hipLaunchKernelGGL(preshuffle_fp8_kernel, dim3(grid_for(chunks)), dim3(256), 0, s, w, chunks, N, K, w_out);
-    int64_t words = (int64_t)E * (N / 128) * KB;
+    const int64_t chunks = (int64_t)E * NG * KB * 16 * 128;
+    hipLaunchKernelGGL(preshuffle_fp8_kernel, dim3(grid_for(chunks)), dim3(256), 0, s, w, chunks, N, K, gate_half,
+                       R, w_out);
+    const int64_t words = (int64_t)E * (N / 128) * KB;
     if (mode == kQuantFp8E8)
       hipLaunchKernelGGL(e8m0_to_f32_kernel, dim3(grid_for(words)), dim3(256), 0, s, (const uint8_t*)sc, words,
                          (float*)s_out);
@@ -237,11 +268,12 @@ hipError_t launch_preshuffle(int mode, const uint8_t* w, const void* sc, int E, 
       hipLaunchKernelGGL(copy_words_kernel, dim3(grid_for(words)), dim3(256), 0, s, (const uint32_t*)sc, words,
                          (uint32_t*)s_out);
   } else {
-    int64_t chunks = (int64_t)E * NT * KB * 64;
-    hipLaunchKernelGGL(preshuffle_mx_kernel, dim3(grid_for(chunks)), dim3(256), 0, s, w, chunks, N, K, w_out);
-    int64_t words = (int64_t)E * NT * ((KB + 3) / 4) * 64;
+    const int64_t chunks = (int64_t)E * NG * KB * 16 * 64;
+    hipLaunchKernelGGL(preshuffle_mx_kernel, dim3(grid_for(chunks)), dim3(256), 0, s, w, chunks, N, K, gate_half,
+                       R, w_out);
+    const int64_t words = (int64_t)E * NG * ((KB + 3) / 4) * 16 * 64;
     hipLaunchKernelGGL(preshuffle_mx_scale_kernel, dim3(grid_for(words)), dim3(256), 0, s, (const uint8_t*)sc,
-                       words, N, K, (uint32_t*)s_out);
+                       words, N, K, gate_half, R, (uint32_t*)s_out);
   }
   return hipGetLastError();
 }

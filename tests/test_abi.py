@@ -197,12 +197,20 @@ def test_block_and_buffer_sizes():
     c = cfg(quant="fp8_ue8m0", block_m=128, inter=128)
     assert M.intermediate_bytes(c, 4096) == (rows * 128, rows * 4)
     assert M.e8_scale_ld(128) == 4 and M.e8_scale_ld(4096) == 32 and M.e8_scale_ld(4224) == 36
-    # TILED_V1 keeps UE8M0 block scales as fp32 values
+    # TILED_V2 keeps UE8M0 block scales as fp32 values
     assert M.preshuffled_bytes(cfg(quant="fp8_ue8m0"), 13) == M.preshuffled_bytes(cfg(), 13)
     assert M.preshuffled_bytes(cfg(), 13) == (288 * 2048 * 4096, 288 * 16 * 32 * 4)
     assert M.preshuffled_bytes(cfg(), 2) == (288 * 4096 * 1024, 288 * 32 * 8 * 4)
     assert M.preshuffled_bytes(cfg(quant="mxfp4"), 13) == (288 * 2048 * 2048, 288 * 128 * 8 * 64 * 4)
     assert M.preshuffled_bytes(cfg(quant="mxfp4"), 2) == (288 * 4096 * 512, 288 * 256 * 2 * 64 * 4)
+    # whole N tiles of 256 rows: a half last N tile of w2 (Hp = 384) is padded
+    # to 512 rows; w13's N tiles (128 gate + 128 up rows) are always whole
+    c = cfg(hidden=384, inter=640)
+    assert M.preshuffled_bytes(c, 2) == (288 * 512 * 640, 288 * 3 * 5 * 4)
+    assert M.preshuffled_bytes(c, 13) == (288 * 1280 * 384, 288 * 10 * 3 * 4)
+    c = cfg(quant="mxfp4", hidden=384, inter=640)
+    assert M.preshuffled_bytes(c, 2) == (288 * 512 * 320, 288 * 2 * 2 * 16 * 64 * 4)
+    assert M.preshuffled_bytes(c, 13) == (288 * 1280 * 192, 288 * 5 * 1 * 16 * 64 * 4)
     # workspace grows with T and covers the GEMM2 rows for gemm2_combine
     assert M.workspace_bytes(cfg(), 1) < M.workspace_bytes(cfg(), 64) < M.workspace_bytes(cfg(), 4096)
     assert M.workspace_bytes(cfg(), 64) >= 64 * 8 * 4096 * 4

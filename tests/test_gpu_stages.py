@@ -175,27 +175,66 @@ def test_permute_align_bitexact(T, E, k, BM, skew):
     assert np.array_equal(bexp.cpu().numpy(), bo)
 
 
-def _tiled_fp8_reference(q, E, N, K):
-    """The documented TILED_V1 FP8 layout, rebuilt on the host."""
-    KB, NT = K // 128, N // 16
-    out = np.zeros(E * N * K, np.uint8)
-    t = q.reshape(E, NT, 16, KB, 4, 2, 16)  # e, nt, row, kb, lane/16, h, byte
-    # out[e, nt, kb, h, lane(=g*16+row), byte]
-    out = t.transpose(0, 1, 3, 5, 4, 2, 6).reshape(-1)
-    return out
+def _row_tile(which, Ip, N, g, i):
+    """Row tile at position i of N tile g (TILED_V2): w13 = 8 gate tiles then
+    the matching 8 up tiles; w2 = 16 consecutive tiles, None past N/16."""
+    if which == 13:
+        return 8 * g + i if i < 8 else Ip // 16 + 8 * g + (i - 8)
+    t = 16 * g + i
+    return t if t < N // 16 else None
 
 
-def _tiled_mx_reference(q, s, E, N, K):
-    KB, NT = K // 128, N // 16
-    t = q.reshape(E, NT, 16, KB, 4, 16)  # e, nt, row, kb, lane/16, byte
-    w = t.transpose(0, 1, 3, 4, 2, 5).reshape(-1)
+def _tile_run(mode, which):
+    """Documented tile run R of each matrix: w2 4; w13 16, MXFP4 w13 1."""
+    if which == 2:
+        return 4
+    return 1 if mode == "mxfp4" else 16
+
+
+def _runs(a, R):
+    """[E, NG, KB', 16, ...] (position-major per K block) -> storage order
+    [E, NG, 16/R, KB', R, ...], flattened."""
+    E, NG, KB = a.shape[:3]
+    rest = a.shape[4:]
+    b = a.reshape(E, NG, KB, 16 // R, R, *rest)
+    return np.moveaxis(b, 3, 2).reshape(-1)
+
+
+def _tiled_fp8_reference(q, E, N, K, which, Ip, R):
+    """The documented TILED_V2 FP8 layout, rebuilt on the host: tile
+    [h][lane = 16*(K quarter) + row][16 bytes] at position i of N tile g and
+    K block kb, stored [e][g][i / R][kb][i % R]."""
+    KB, NG = K // 128, -(-N // 256)
+    out = np.zeros((E, NG, KB, 16, 2, 64, 16), np.uint8)
+    for g in range(NG):
+        for i in range(16):
+            rt = _row_tile(which, Ip, N, g, i)
+            if rt is None:
+                continue
+            t = q[:, rt * 16:(rt + 1) * 16, :].reshape(E, 16, KB, 4, 2, 16)  # e, row, kb, quarter, h, byte
+            out[:, g, :, i] = t.transpose(0, 2, 4, 3, 1, 5).reshape(E, KB, 2, 64, 16)
+    return _runs(out, R)
+
+
+def _tiled_mx_reference(q, s, E, N, K, which, Ip, R):
+    """TILED_V2 MX: tiles [lane][16 bytes], stored as the FP8 tiles; scale
+    word rows [lane][byte j = K block 4q + j] stored [e][g][i / R][q][i % R]."""
+    KB, NG = K // 128, -(-N // 256)
     KB4 = (KB + 3) // 4
-    sc = np.zeros((E, NT, KB4, 64, 4), np.uint8)
-    s5 = s.reshape(E, NT, 16, KB, 4)  # e, nt, row, kb, group-in-block
-    for kb in range(KB):
-        for g in range(4):
-            sc[:, :, kb // 4, g * 16:(g + 1) * 16, kb % 4] = s5[:, :, :, kb, g]
-    return w, sc.reshape(-1)
+    w = np.zeros((E, NG, KB, 16, 64, 16), np.uint8)
+    sc = np.zeros((E, NG, KB4, 16, 64, 4), np.uint8)
+    for g in range(NG):
+        for i in range(16):
+            rt = _row_tile(which, Ip, N, g, i)
+            if rt is None:
+                continue
+            t = q[:, rt * 16:(rt + 1) * 16, :].reshape(E, 16, KB, 4, 16)  # e, row, kb, quarter, byte
+            w[:, g, :, i] = t.transpose(0, 2, 3, 1, 4).reshape(E, KB, 64, 16)
+            s5 = s[:, rt * 16:(rt + 1) * 16, :].reshape(E, 16, KB, 4)  # e, row, kb, 32-group in block
+            for kb in range(KB):
+                for quarter in range(4):
+                    sc[:, g, kb // 4, i, quarter * 16:(quarter + 1) * 16, kb % 4] = s5[:, :, kb, quarter]
+    return _runs(w, R), _runs(sc, R)
 
 
 @pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
@@ -218,14 +257,14 @@ def test_preshuffle_layout(mode):
         qo, so = M.moe_preshuffle_weights(cfg, which, torch.from_numpy(q).cuda(), torch.from_numpy(s).cuda())
         torch.cuda.synchronize()
         if mode == "fp8":
-            assert np.array_equal(qo.cpu().numpy(), _tiled_fp8_reference(q, E, N, K))
+            assert np.array_equal(qo.cpu().numpy(), _tiled_fp8_reference(q, E, N, K, which, Ip, _tile_run(mode, which)))
             assert np.array_equal(so.cpu().numpy().view(np.float32), s.reshape(-1))
         elif mode == "fp8_ue8m0":
             # same tiles; the scale bytes as their exact fp32 values
-            assert np.array_equal(qo.cpu().numpy(), _tiled_fp8_reference(q, E, N, K))
+            assert np.array_equal(qo.cpu().numpy(), _tiled_fp8_reference(q, E, N, K, which, Ip, _tile_run(mode, which)))
             assert np.array_equal(so.cpu().numpy().view(np.float32), O.e8m0_to_f32(s).reshape(-1))
         else:
-            w_ref, s_ref = _tiled_mx_reference(q, s, E, N, K)
+            w_ref, s_ref = _tiled_mx_reference(q, s, E, N, K, which, Ip, _tile_run(mode, which))
             assert np.array_equal(qo.cpu().numpy(), w_ref)
             assert np.array_equal(so.cpu().numpy(), s_ref)
 
