@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--workload", default="decode_fp8")
     ap.add_argument("--T", type=int, default=0, help="override the token count")
     ap.add_argument("--block-m", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=4, help="tokens in the oracle's timed sample (0 = skip)")
+    ap.add_argument("--cpu-sample", type=int, default=64,
+                    help="tokens in the oracle's timed sample (0 = skip; the default covers the whole decode batch)")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (calibrates HBM byte counters) and exit")
@@ -83,10 +84,11 @@ def algorithmic_bytes(wl, ids, M):
                 w13_per_expert=w13, w2_per_expert=w2)
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, T: int, block_m: int):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary (calibrated against a plain
-    copy), or None when there is none or the GEMM source changed since."""
+    copy), or None when there is none, it was taken at another token count
+    or block size, or the GEMM source changed since."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
     if not os.path.exists(path):
@@ -96,7 +98,7 @@ def recorded_traffic(workload: str):
     for line in open(path):
         if line.startswith("TRAFFIC "):
             kv = dict(t.split("=", 1) for t in line.split()[1:])
-            if kv.get("gemm_src_sha256") != sha:
+            if kv.get("gemm_src_sha256") != sha or kv.get("T") != str(T) or kv.get("block_m") != str(block_m):
                 return None
             return int(kv["read_bytes"]) + int(kv["write_bytes"])
     return None
@@ -122,7 +124,8 @@ def cpu_baseline(wl, x, lg, sample_tokens: int):
     dt = time.perf_counter() - t0
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     return {"value": len(toks) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {len(toks)} of {wl.T} tokens of {wl.name} ({len(np.unique(ids))} experts), "
+            "sample": f"{'all' if len(toks) == wl.T else 'first'} {len(toks)} of {wl.T} tokens of {wl.name} "
+                      f"({len(np.unique(ids))} experts), "
                       f"{dt:.2f} s wall; weight quantisation excluded; "
                       f"host affinity {len(os.sched_getaffinity(0))} cpus"}
 
@@ -245,7 +248,7 @@ def main():
         flops1 = 4.0 * wl.T * wl.top_k * wl.I * wl.H
         peak_f = MFMA_PEAK_TFLOPS[wl.mode]
         mfma_bound = flops1 / nbytes["gemm1"] > peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
-        common = {"traffic": recorded_traffic(wl.name),
+        common = {"traffic": recorded_traffic(wl.name, wl.T, bm),
                   "kernel": ("moe_gemm_stream (GEMM1 + clamped SwiGLU + re-quantisation)" if ks1 == 1 else
                              f"moe_gemm_stream (GEMM1, K split {ks1}) + swiglu_requant"),
                   "kernel_us": round(kern[dom], 2), "algorithmic_bytes": nbytes["gemm1"],
