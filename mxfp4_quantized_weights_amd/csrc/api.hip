@@ -110,7 +110,7 @@ size_t split_bytes(const moe_cfg_t* c, int32_t T, int which, int ks) {
   const int64_t Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
   if (which == 13) return ks > 1 ? align_up((size_t)(ks * P * 2 * Ip * 4 + P * 4)) : 0;
   // unsplit: the (possibly column-chunked) y rows; split: whole planes
-  const int64_t planes = ks > 1 ? ks * P * Hp * 4 : 0, y = moe::y_reserve_bytes(P, Hp);
+  const int64_t planes = ks > 1 ? ks * moe::y_plane_bytes(P, Hp) : 0, y = moe::y_reserve_bytes(P, Hp);
   return align_up((size_t)(planes > y ? planes : y));
 }
 
@@ -122,7 +122,7 @@ size_t split_reserve(const moe_cfg_t* c, int32_t T, int which) {
   const int cap = moe::ksplit_cap(c->quant_mode, gemm_kb(c, which));
   const int64_t Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
   if (which == 13) return cap > 1 ? align_up((size_t)(cap * Ps * 2 * Ip * 4 + Ps * 4)) : 0;
-  const int64_t planes = cap > 1 ? cap * Ps * Hp * 4 : 0, y = moe::y_reserve_bytes(P, Hp);
+  const int64_t planes = cap > 1 ? cap * moe::y_plane_bytes(Ps, Hp) : 0, y = moe::y_reserve_bytes(P, Hp);
   return align_up((size_t)(planes > y ? planes : y));
 }
 
@@ -183,7 +183,7 @@ moe::GemmArgs gemm1_args(const moe_cfg_t* c, int32_t T, const void* xq, const vo
 }
 
 moe::GemmArgs gemm2_args(const moe_cfg_t* c, int32_t T, const void* aq, const void* as, const int32_t* sorted,
-                         const int32_t* bexp, const int32_t* npp, const void* w2, const void* s2, float* y,
+                         const int32_t* bexp, const int32_t* npp, const void* w2, const void* s2, uint8_t* y,
                          const float* topk_w) {
   moe::GemmArgs a{};
   const int32_t m = c->quant_mode;
@@ -252,13 +252,15 @@ hipError_t gemm2_and_combine(const moe_cfg_t* c, int32_t T, moe::GemmArgs a, int
   if (ks > 1) {
     a.ks_log2 = log2_of(ks);
     a.ldy = Hp;
-    a.yplane = P * Hp;
+    a.yplane = moe::y_plane_bytes(P, Hp);
+    a.yexp = moe::y_values_bytes(P, Hp);
     hipError_t e = moe::launch_gemm2(c->quant_mode, c->block_m, nb, a, s);
     if (e != hipSuccess) return e;
-    return moe::launch_combine(a.y, T, c->top_k, 0, H, Hp, ks, a.yplane, (uint16_t*)out_bf16, ld_out, s);
+    return moe::launch_combine(a.y, a.yexp, T, c->top_k, 0, H, Hp, ks, a.yplane, (uint16_t*)out_bf16, ld_out, s);
   }
   const int64_t W = moe::y_chunk_cols(P, Hp);
   a.ldy = W;
+  a.yexp = moe::y_values_bytes(P, W);
   for (int c0 = 0; c0 < Hp; c0 += (int)W) {
     const int wc = (int)(Hp - c0 < W ? Hp - c0 : W);
     a.nt0 = c0 / 256;
@@ -267,7 +269,7 @@ hipError_t gemm2_and_combine(const moe_cfg_t* c, int32_t T, moe::GemmArgs a, int
     if (e != hipSuccess) return e;
     const int cols = H - c0 < wc ? H - c0 : wc;
     if (cols > 0) {
-      e = moe::launch_combine(a.y, T, c->top_k, c0, cols, W, 1, 0, (uint16_t*)out_bf16, ld_out, s);
+      e = moe::launch_combine(a.y, a.yexp, T, c->top_k, c0, cols, W, 1, 0, (uint16_t*)out_bf16, ld_out, s);
       if (e != hipSuccess) return e;
     }
   }
@@ -470,7 +472,7 @@ moe_status_t moe_grouped_gemm2_combine_splitk(const moe_cfg_t* cfg, int32_t T, c
   if (ws_bytes < split_bytes(cfg, T, 2, ksplit)) return MOE_ERR_WORKSPACE;
   const int32_t nb = max_blocks(P, cfg->num_experts, cfg->block_m);
   hipStream_t s = as_stream(stream);
-  float* y = (float*)ws;
+  uint8_t* y = (uint8_t*)ws;
   moe::GemmArgs a = gemm2_args(cfg, T, aq, as, sorted_ids, block_expert, num_post_padded, w2, w2_scale, y, topk_w);
   return hip_status(gemm2_and_combine(cfg, T, a, nb, ksplit, out_bf16, ld_out, s));
 }
@@ -523,7 +525,7 @@ moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, in
   void* aq = p; p += L.aq;
   void* as = p; p += L.as;
   float* part = (float*)p; p += L.part;
-  float* y = (float*)p;
+  uint8_t* y = p;
 
   hipStream_t s = as_stream(stream);
   const int E = cfg->num_experts, k = cfg->top_k, BM = cfg->block_m;

@@ -554,25 +554,53 @@ __device__ __forceinline__ void epilogue_gemm1_part(const GemmArgs& p, const v4f
   }
 }
 
-// GEMM2 epilogue: y[pair, 4 consecutive columns] = routing weight * C per
-// lane and weight tile; routing weights from LDS.  y holds the columns of
-// this launch's N tiles (from nt0); a K piece writes its own plane.
+// GEMM2 epilogue: the weighted rows v = routing weight * C of real pairs, in
+// y's block floating point (y_plane_bytes): int16 q = rint(v * 2^-s) with one
+// exponent s = max(floor(log2 max|v|) - 14, -128) per 64 columns of a row.
+// Lane l holds, for token t = wt*64 + m*16 + l%16, columns 64*wn + 16*j +
+// 4*(l/16) + i of the N tile, so a row's 64-column group is the wave's and
+// its 4 lanes (l/16 = 0..3) share the group's largest |v| through two lane
+// exchanges.  |v| * 2^-s < 2^15, and a value that rounds to 2^15 is stored
+// as 32767, so v' = q * 2^s is within 2^s <= 2^-14 max|v| of v.  Routing
+// weights come from LDS.  y holds the columns of this launch's N tiles (from
+// nt0); a K piece writes its own plane.
 template <int MT>
 __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&acc)[MT][4], const int32_t* sid,
                                                  const float* wts, int ks, int nt, int wt, int wn) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
+  uint8_t* plane = p.y + ks * p.yplane;
+  const int col0 = (nt - p.nt0) * 256 + 64 * wn;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int t = wt * 64 + m * 16 + c16;
     const int s = sid[t];
-    if (s < p.num_pairs) {
-      const float w = wts[t];
-      float* yrow = p.y + ks * p.yplane + (int64_t)s * p.ldy + (nt - p.nt0) * 256 + 64 * wn + 4 * q;
+    const bool real = s < p.num_pairs;
+    const float w = real ? wts[t] : 0.0f;
+    float v[4][4];
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[j][i] = w * acc[m][j][i];
+        mx = fmaxf(mx, fabsf(v[j][i]));
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (real) {
+      // floor(log2 mx) from the exponent field (subnormals included)
+      const int e = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;
+      const int sx = max(e - 14, -128);
+      int16_t* yrow = (int16_t*)plane + (int64_t)s * p.ldy + col0 + 4 * q;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const v4f v = acc[m][j];
-        *(float4*)(yrow + 16 * j) = make_float4(w * v[0], w * v[1], w * v[2], w * v[3]);
+        int qv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qv[i] = min(max((int)__builtin_rintf(ldexpf(v[j][i], -sx)), -32767), 32767);
+        *(uint2*)(yrow + 16 * j) = make_uint2(((uint32_t)qv[0] & 0xFFFFu) | ((uint32_t)qv[1] << 16),
+                                              ((uint32_t)qv[2] & 0xFFFFu) | ((uint32_t)qv[3] << 16));
       }
+      if (q == 0) ((int8_t*)(plane + p.yexp))[(int64_t)s * (p.ldy / 64) + col0 / 64] = (int8_t)sx;
     }
   }
 }
@@ -1040,44 +1068,49 @@ hipError_t launch_swiglu_requant(int mode, const float* part, int ks, int P, int
   return hipGetLastError();
 }
 
-// out[t, c0 + h] = bf16(sum_j y[t*k + j, h]) with the slot sum in order
-// j = 0..k-1 (with K pieces: plane by plane, slots in order within each),
-// for h < cols (a column chunk of the output).  8 columns per
-// thread (two 16-byte non-temporal loads per slot: y is read once); the 8
-// bf16 results go out as one 16-byte store when the row stride allows it.
-// Columns h .. h+7 stay inside the y rows GEMM2 wrote (the chunk width is a
-// multiple of 256, or all Hp), only those below `cols` are stored.
-__device__ __forceinline__ float4 load_nt4(const float* p) {
-  typedef float f4 __attribute__((ext_vector_type(4)));
-  const f4 v = __builtin_nontemporal_load((const f4*)p);
-  return make_float4(v.x, v.y, v.z, v.w);
-}
-
+// out[t, c0 + h] = bf16(sum_j y[t*k + j, h]) with the slot sum in fp32 in
+// order j = 0..k-1 (with K pieces: plane by plane, slots in order within
+// each), for h < cols (a column chunk of the output).  Each y value is
+// decoded exactly, q * 2^s (int16 q, the exponent of its 64-column group).
+// 8 columns per thread (one 16-byte non-temporal load per slot: y is read
+// once); the 8 bf16 results go out as one 16-byte store when the row stride
+// allows it.  Columns h .. h+7 lie in one 64-column group and inside the y
+// rows GEMM2 wrote (the chunk width is a multiple of 256, or all Hp); only
+// those below `cols` are stored.
 template <int KMAX>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int k, int cols, int64_t ldy,
-                                                      int nplanes, int64_t plane, uint16_t* __restrict__ out,
-                                                      int64_t ld_out, int vec_store) {
+__global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict__ y, int64_t yexp, int k, int cols,
+                                                      int64_t ldy, int nplanes, int64_t plane,
+                                                      uint16_t* __restrict__ out, int64_t ld_out, int vec_store) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
   const int t = blockIdx.y;
   const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (h >= cols) return;
+  const int64_t lde = ldy / 64;
   float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   // plane by plane (K pieces of GEMM2); in a plane every slot's loads are
   // issued before the first add (k <= KMAX)
   for (int ps = 0; ps < nplanes; ++ps) {
-    const float* base = y + ps * plane + (int64_t)t * k * ldy + h;
-    float4 v0[KMAX], v1[KMAX];
+    const uint8_t* pl = y + ps * plane;
+    const int16_t* base = (const int16_t*)pl + (int64_t)t * k * ldy + h;
+    const int8_t* eb = (const int8_t*)(pl + yexp) + (int64_t)t * k * lde + h / 64;
+    u4 v[KMAX];
+    int ex[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (j < k) {
-        v0[j] = load_nt4(base + (int64_t)j * ldy);
-        v1[j] = load_nt4(base + (int64_t)j * ldy + 4);
+        v[j] = __builtin_nontemporal_load((const u4*)(base + (int64_t)j * ldy));
+        ex[j] = eb[(int64_t)j * lde];
       }
     }
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
       if (j < k) {
-        a[0] += v0[j].x; a[1] += v0[j].y; a[2] += v0[j].z; a[3] += v0[j].w;
-        a[4] += v1[j].x; a[5] += v1[j].y; a[6] += v1[j].z; a[7] += v1[j].w;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t wd = v[j][d];
+          a[2 * d] += ldexpf((float)(int)(int16_t)(wd & 0xFFFFu), ex[j]);
+          a[2 * d + 1] += ldexpf((float)((int)wd >> 16), ex[j]);
+        }
       }
     }
   }
@@ -1094,21 +1127,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_combine(const float* y, int T, int k, int c0, int cols, int64_t ldy, int nplanes, int64_t plane,
-                          uint16_t* out, int64_t ld_out, hipStream_t s) {
+hipError_t launch_combine(const uint8_t* y, int64_t yexp, int T, int k, int c0, int cols, int64_t ldy, int nplanes,
+                          int64_t plane, uint16_t* out, int64_t ld_out, hipStream_t s) {
   if (T <= 0 || cols <= 0) return hipSuccess;
   uint16_t* o = out + c0;
   // 16-byte stores need every row start 16-byte aligned
   const int vec = ((uintptr_t)o % 16 == 0) && (ld_out % 8 == 0);
   dim3 grid((unsigned)((cols + 2047) / 2048), (unsigned)T), block(256);
   if (k <= 2)
-    hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, s, y, k, cols, ldy, nplanes, plane, o, ld_out, vec);
+    hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, s, y, yexp, k, cols, ldy, nplanes, plane, o, ld_out, vec);
   else if (k <= 4)
-    hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, s, y, k, cols, ldy, nplanes, plane, o, ld_out, vec);
+    hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, s, y, yexp, k, cols, ldy, nplanes, plane, o, ld_out, vec);
   else if (k <= 8)
-    hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, y, k, cols, ldy, nplanes, plane, o, ld_out, vec);
+    hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, s, y, yexp, k, cols, ldy, nplanes, plane, o, ld_out, vec);
   else
-    hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, s, y, k, cols, ldy, nplanes, plane, o, ld_out, vec);
+    hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, s, y, yexp, k, cols, ldy, nplanes, plane, o, ld_out, vec);
   return hipGetLastError();
 }
 

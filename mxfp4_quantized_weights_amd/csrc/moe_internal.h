@@ -98,13 +98,14 @@ struct GemmArgs {
   void* as;
   int32_t Ip;
   float limit;
-  float* y;               // GEMM2 output: weighted per-pair rows [P, ldy], columns nt0*256 ..
+  uint8_t* y;             // GEMM2 output: weighted per-pair rows, columns nt0*256 .. (plane 0; see y_plane_bytes)
   const float* topk_w;    // [P]
   int32_t nt0;            // GEMM2: first 256-column N tile of this launch (items cover n_tiles tiles)
-  int64_t ldy;            // GEMM2: row stride of y in floats
+  int64_t ldy;            // GEMM2: row stride of y in values (a multiple of 256)
   int32_t ks_log2;        // K split: each item covers K / 2^ks_log2 of the reduction
   float* part;            // GEMM1 with a K split: fp32 partial sums [2^ks_log2, P, 2*Ip], then int32 [P]
-  int64_t yplane;         // GEMM2 with a K split: floats between the y planes of the K pieces
+  int64_t yplane;         // GEMM2 with a K split: bytes between the y planes of the K pieces
+  int64_t yexp;           // GEMM2: byte offset of the exponents within a plane
   int32_t tile_run;       // TILED_V2 tile run R of B (tile_run(mode, which))
 };
 
@@ -134,38 +135,52 @@ int pick_ksplit(int mode, int T, int E, int k, int block_m, int KB, int n_tiles)
 hipError_t launch_swiglu_requant(int mode, const float* part, int ks, int P, int Ip, float limit, uint8_t* aq,
                                  void* as, hipStream_t s);
 
-// Columns of the per-pair GEMM2 rows y kept at once: all Hp when P * Hp
-// fp32 values fit in kYChunkBytes, else the largest multiple of 256 that
-// does (at least 256).  GEMM2 and the combine then run once per column chunk
-// on the same y buffer, which bounds the workspace of very large batches.
-// Chunks cost time (each re-runs GEMM2's item list and its tail, and the
-// memory-side cache does not keep a 64-128 MiB chunk between GEMM2 and the
-// combine), so the cap is set high: a 4096-token, 288-expert top-8 layer
-// (512 MiB of y) runs in one piece.
+// GEMM2's weighted per-pair rows y are block floating point: one plane holds
+// int16 values [pairs, cols] (256-byte aligned) and then one int8 exponent s
+// per 64 columns [pairs, cols/64]; value v of a group is stored as
+// q = rint(v * 2^-s) with s = max(floor(log2 max|v|) - 14, -128), so
+// |q| <= 32767 and v' = q * 2^s differs from v by at most 2^(s-1), i.e.
+// 2^-15 of the group's largest |v|.  The combine decodes exactly and sums in
+// fp32.  Half the bytes of fp32 rows, for the two passes over them.
+inline int64_t y_values_bytes(int64_t pairs, int64_t cols) { return (pairs * cols * 2 + 255) / 256 * 256; }
+inline int64_t y_plane_bytes(int64_t pairs, int64_t cols) {
+  return y_values_bytes(pairs, cols) + (pairs * (cols / 64) + 255) / 256 * 256;
+}
+
+// Columns of y kept at once: all Hp when a plane of P rows fits in
+// kYChunkBytes, else the largest multiple of 256 that does (at least 256).
+// GEMM2 and the combine then run once per column chunk on the same y buffer,
+// which bounds the workspace of very large batches.  Chunks cost time (each
+// re-runs GEMM2's item list and its tail, and the memory-side cache does not
+// keep a 64-128 MiB chunk between GEMM2 and the combine), so the cap is set
+// high: a 4096-token, 288-expert top-8 layer (260 MiB of y) runs in one piece.
 #ifndef MOE_Y_CHUNK_BYTES
 #define MOE_Y_CHUNK_BYTES (1ll << 30)
 #endif
 constexpr int64_t kYChunkBytes = MOE_Y_CHUNK_BYTES;
 inline int64_t y_chunk_cols(int64_t pairs, int64_t Hp) {
-  if (pairs <= 0 || pairs * Hp * 4 <= kYChunkBytes) return Hp;
-  int64_t w = kYChunkBytes / (pairs * 4) / 256 * 256;
+  if (pairs <= 0 || y_plane_bytes(pairs, Hp) <= kYChunkBytes) return Hp;
+  // 2 bytes per value + 1 per 64 values, 512 bytes of alignment slack
+  int64_t w = (kYChunkBytes - 512) * 64 / (pairs * 129) / 256 * 256;
   return w < 256 ? 256 : (w > Hp ? Hp : w);
 }
-// Bytes reserved for y: at least pairs * y_chunk_cols * 4, and non-decreasing
-// in `pairs`, so a workspace sized for T_max tokens fits every T <= T_max.
+// Bytes reserved for y: at least one plane of pairs x y_chunk_cols, and
+// non-decreasing in `pairs`, so a workspace sized for T_max tokens fits every
+// T <= T_max.
 inline int64_t y_reserve_bytes(int64_t pairs, int64_t Hp) {
-  const int64_t full = pairs * Hp * 4;
+  const int64_t full = y_plane_bytes(pairs, Hp);
   const int64_t capped = full < kYChunkBytes ? full : kYChunkBytes;
-  const int64_t used = pairs * y_chunk_cols(pairs, Hp) * 4;
+  const int64_t used = y_plane_bytes(pairs, y_chunk_cols(pairs, Hp));
   return used > capped ? used : capped;
 }
 
 hipError_t launch_gemm1(int mode, int block_m, int nb, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm2(int mode, int block_m, int nb, const GemmArgs& a, hipStream_t s);
 
-// out[t, c0 + h] for h < cols from y rows [T*k, ldy] (pair t*k + j), summed
-// over nplanes planes `plane` floats apart.
-hipError_t launch_combine(const float* y, int T, int k, int c0, int cols, int64_t ldy, int nplanes, int64_t plane,
-                          uint16_t* out, int64_t ld_out, hipStream_t s);
+// out[t, c0 + h] for h < cols from the block-floating-point y rows (pair
+// t*k + j; values and exponents as above, exponents `yexp` bytes after the
+// values), summed over nplanes planes `plane` bytes apart.
+hipError_t launch_combine(const uint8_t* y, int64_t yexp, int T, int k, int c0, int cols, int64_t ldy, int nplanes,
+                          int64_t plane, uint16_t* out, int64_t ld_out, hipStream_t s);
 
 }  // namespace moe

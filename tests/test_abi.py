@@ -252,8 +252,10 @@ def test_ksplit_plan_and_scratch():
     P = 64 * 8
     for ks in (1, 2, 4, 8):
         assert M.splitk_bytes(c, 64, 13, ks) == (0 if ks == 1 else ks * P * 2048 * 4 + P * 4)
-    assert M.splitk_bytes(c, 64, 2, 2) == 2 * P * 4096 * 4
-    assert M.splitk_bytes(c, 64, 2, 1) == P * 4096 * 4
+    # GEMM2's y plane: int16 values [P, Hp] and one exponent byte per 64 columns
+    plane = P * 4096 * 2 + P * 4096 // 64
+    assert M.splitk_bytes(c, 64, 2, 2) == 2 * plane
+    assert M.splitk_bytes(c, 64, 2, 1) == plane
     # unusable: not a power of two up to 8, pieces under 4 K blocks, or (MX,
     # UE8M0) not whole dwords of 4 scale bytes, or too many pairs
     assert M.splitk_bytes(c, 64, 13, 3) == 0 and M.splitk_bytes(c, 64, 13, 16) == 0
@@ -273,10 +275,10 @@ def test_ksplit_plan_and_scratch():
                 need = max(M.splitk_bytes(cc, T, 2, M.plan_ksplit(cc, T, 2)),
                            M.splitk_bytes(cc, T, 13, M.plan_ksplit(cc, T, 13)))
                 assert 0 < need <= M.workspace_bytes(cc, T)
-    # unsplit GEMM2 of a batch whose y rows are column-chunked (P * Hp * 4 > 1 GiB)
-    cc = cfg(num_experts=8, hidden=2100, inter=256, block_m=64)
+    # unsplit GEMM2 of a batch whose y rows are column-chunked (P * Hp * 2 > 1 GiB)
+    cc = cfg(num_experts=8, hidden=4100, inter=256, block_m=64)
     assert 0 < M.splitk_bytes(cc, 16384, 2, 1) <= M.workspace_bytes(cc, 16384)
-    assert M.splitk_bytes(cc, 16384, 2, 1) < 16384 * 8 * 2176 * 4
+    assert M.splitk_bytes(cc, 16384, 2, 1) < 16384 * 8 * 4224 * 2
 
 
 def test_ksplit_entry_points_validate_before_launch():

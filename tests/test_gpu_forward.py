@@ -65,10 +65,10 @@ TINY = W.WORKLOADS["tiny_fp8"]
 MID = W.Workload("mid", T=200, H=512, I=384, E=16, top_k=4, mode="fp8", outlier_frac=0.01)
 STREAM = W.Workload("stream", T=2048, H=1536, I=1024, E=8, top_k=4, mode="fp8", outlier_frac=0.01)
 SHORT_K = W.Workload("short_k", T=2048, H=2048, I=128, E=8, top_k=4, mode="fp8", outlier_frac=0.01)
-# more per-pair GEMM2 rows than one y chunk holds (P * Hp * 4 > 1 GiB):
-# GEMM2 + combine run per column chunk (2048 columns, then a ragged
-# 128-column tail of which 52 are real)
-CHUNKED = W.Workload("chunked", T=16384, H=2100, I=256, E=8, top_k=8, mode="fp8", Hp=2176, outlier_frac=0.01)
+# more per-pair GEMM2 rows than one y chunk holds (P * Hp * 2 bytes > 1 GiB):
+# GEMM2 + combine run per column chunk (3840 columns, then a ragged
+# 384-column tail of which 260 are real)
+CHUNKED = W.Workload("chunked", T=16384, H=4100, I=256, E=8, top_k=8, mode="fp8", Hp=4224, outlier_frac=0.01)
 
 CASES = {
     "tiny_fp8": (TINY, None),

@@ -3,8 +3,9 @@
 Each (block, N tile) work item is cut into ksplit pieces along K.  GEMM1
 pieces store fp32 partial sums that a second kernel adds before the clamped
 SwiGLU and the re-quantisation; GEMM2 pieces store y planes that the combine
-adds.  Results differ from the unsplit launch only by fp32 summation order,
-so the checks are those of the unsplit stages: the intermediate against the
+adds.  Results differ from the unsplit launch by fp32 summation order (and,
+for GEMM2, by each plane's own block-floating-point storage of the per-pair
+rows), so the checks are those of the unsplit stages: the intermediate against the
 oracle's stage values (a code moves by at most one step at a rounding
 boundary), the layer output against the oracle rows within the mode's
 tolerance, and moe_forward bit-identical to the stage entry points called with
@@ -91,9 +92,14 @@ def test_gemm2_splitk_combine(mode):
         assert torch.all(out[:, wl.H:] == 7.0), "columns past H must not be written"
         outs[ks] = bf16_to_f32(out[:, :wl.H])
         assert_rows_close(outs[ks], ref, mode, f"gemm2 ksplit {ks}", allowance=tie)
-    # the two differ only by fp32 summation order: at most one bf16 rounding step
+    # the two differ by fp32 summation order (at most one bf16 rounding step)
+    # and by the block-floating-point storage of the per-pair rows, which each
+    # piece encodes on its own: every stored term is within 2^-14 of its
+    # 64-column group's largest |w y|, so the 2k terms of an element stay well
+    # under 2^-7 of the row RMS
     d = np.abs(outs[1] - outs[2])
-    assert np.all(d <= 2.0 ** -7 * np.maximum(np.abs(outs[1]), np.abs(outs[2])) + 1e-30)
+    rms = np.sqrt(np.mean(np.square(outs[1]), axis=1, keepdims=True))
+    assert np.all(d <= 2.0 ** -7 * (np.maximum(np.abs(outs[1]), np.abs(outs[2])) + rms) + 1e-30)
 
 
 @pytest.mark.parametrize("mode", MODES)
