@@ -477,11 +477,12 @@ __device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&
         if (wn == 0 && q == 0) ((uint8_t*)p.as)[(int64_t)(row0 + t) * ld_e8 + nt] = (uint8_t)b;
       } else {
         const float s = amax / kE4M3Max;
+        const float inv = 1.0f / s;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           uint32_t packed = 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) packed |= ((amax > 0.0f) ? fp8_quant(av[m][jj][i], s) : 0u) << (8 * i);
+          for (int i = 0; i < 4; ++i) packed |= ((amax > 0.0f) ? fp8_quant_inv(av[m][jj][i], inv) : 0u) << (8 * i);
           *(uint32_t*)(row + 16 * jj) = packed;
         }
         if (wn == 0 && q == 0) ((float*)p.as)[(int64_t)(row0 + t) * nsc + nt] = (amax > 0.0f) ? s : 0.0f;
@@ -1036,9 +1037,10 @@ __global__ __launch_bounds__(256) void swiglu_requant_kernel(const float* __rest
       if (lead) ((uint8_t*)as)[(int64_t)r * e8_scale_ld(Ip) + c / 128] = (uint8_t)b;
     } else {
       const float sc = mx / kE4M3Max;
+      const float inv = 1.0f / sc;
       uint32_t packed = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) packed |= ((mx > 0.0f) ? fp8_quant(a[i], sc) : 0u) << (8 * i);
+      for (int i = 0; i < 4; ++i) packed |= ((mx > 0.0f) ? fp8_quant_inv(a[i], inv) : 0u) << (8 * i);
       *(uint32_t*)(aq + (int64_t)r * Ip + c) = packed;
       if (lead) ((float*)as)[(int64_t)r * (Ip / 128) + c / 128] = (mx > 0.0f) ? sc : 0.0f;
     }

@@ -137,6 +137,18 @@ __device__ __forceinline__ uint32_t fp8_quant(float v, float s) {
   return e4m3_code(r);
 }
 
+// E4M3FN code of v * inv, saturated to +-448: the re-quantisation of GEMM1's
+// SwiGLU output, with inv = fl32(1/s) computed once per group.  v * inv is
+// within 1.5 ulp of the IEEE quotient v / s, so a code can differ from
+// fp8_quant's only where v / s lies that close to a rounding midpoint; the
+// intermediate's codes already differ from a host computation at such ties,
+// because GEMM1's fp32 sums run in another order.
+__device__ __forceinline__ uint32_t fp8_quant_inv(float v, float inv) {
+  float r = v * inv;
+  r = fminf(fmaxf(r, -kE4M3Max), kE4M3Max);
+  return e4m3_code(r);
+}
+
 // Quantise one value of an MX group with scale byte b (inv = 2^(127-b)).
 __device__ __forceinline__ uint32_t mx_quant(float v, float inv) {
   float r = v * inv;  // exact scaling by a power of two
@@ -144,7 +156,13 @@ __device__ __forceinline__ uint32_t mx_quant(float v, float inv) {
   return e2m1_code(r);
 }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+// silu(g) = g / (1 + e^-g), with the hardware exp2 and reciprocal (each a
+// few ulp; a relative error of ~1e-6 at |g| = 10): the value is re-quantised
+// right after, where only codes at a rounding tie can move.  Large negative g
+// gives e^-g = inf and silu = -0, as the exact formula in fp32.
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
 
 // Clamped SwiGLU (FreeToken PR #270, Summary): silu(min(g, L)) * clamp(u, -L, L).
 __device__ __forceinline__ float swiglu_clamped(float g, float u, float L) {
