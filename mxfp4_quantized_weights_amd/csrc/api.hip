@@ -210,8 +210,9 @@ moe::GemmArgs gemm2_args(const moe_cfg_t* c, int32_t T, const void* aq, const vo
   return a;
 }
 
-// Routing, permutation and quantisation of x: two launches for decode-sized
-// batches, else the three stage kernels.
+// Routing, permutation and quantisation of x in two launches: routing and
+// quantisation together, then the permutation (a one-workgroup bitmap
+// version for decode-sized batches).
 hipError_t front_end(const moe_cfg_t* c, int32_t T, const float* logits, const void* x, int64_t ld_x, int32_t* ids,
                      float* wts, int32_t* sorted, int32_t* bexp, int32_t* offs, int32_t* npp, void* xq, void* xs,
                      hipStream_t s) {
@@ -221,10 +222,9 @@ hipError_t front_end(const moe_cfg_t* c, int32_t T, const float* logits, const v
   if (moe::front_small_ok(T, E, k))
     return moe::launch_front_small(logits, T, E, k, ids, wts, BM, nb, sorted, bexp, offs, npp, x, H, ld_x, Hp, mode,
                                    xq, xs, s);
-  hipError_t e = moe::launch_route_topk(logits, T, E, k, ids, wts, s);
+  hipError_t e = moe::launch_route_and_quant(logits, T, E, k, ids, wts, x, H, ld_x, Hp, mode, xq, xs, s);
   if (e != hipSuccess) return e;
-  if ((e = moe::launch_permute_align(ids, T, k, E, BM, nb, sorted, bexp, offs, npp, s)) != hipSuccess) return e;
-  return moe::launch_quant_rows(x, true, T, H, ld_x, Hp, mode, xq, xs, s);
+  return moe::launch_permute_align(ids, T, k, E, BM, nb, sorted, bexp, offs, npp, s);
 }
 
 int log2_of(int ks) { return ks >= 8 ? 3 : ks >= 4 ? 2 : ks >= 2 ? 1 : 0; }

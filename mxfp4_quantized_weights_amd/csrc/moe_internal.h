@@ -25,6 +25,11 @@ hipError_t launch_permute_align(const int32_t* ids, int T, int k, int E, int blo
                                 int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets,
                                 int32_t* npp, hipStream_t s);
 
+// Routing (as launch_route_topk) and quantisation of bf16 x (as
+// launch_quant_rows) in one launch, for any batch with E <= 1024.
+hipError_t launch_route_and_quant(const float* logits, int T, int E, int k, int32_t* ids, float* w, const void* x_bf16,
+                                  int H, int64_t ld_x, int Hp, int mode, void* xq, void* xs, hipStream_t s);
+
 // Routing, permutation and quantisation of bf16 x in two launches, for
 // batches where front_small_ok(T, E, k) holds (same results as the three
 // stage launchers for routing output, which never repeats an expert).

@@ -382,10 +382,11 @@ hipError_t launch_permute_align(const int32_t* ids, int T, int k, int E, int blo
 }
 
 // ---------------------------------------------------------------------------
-// Small-batch front end (T <= 64 tokens): two launches instead of three.
-//   route_quant_kernel: workgroups 0 .. nr-1 route 4 tokens each (one wave
-//             per token, route_token), the others quantise the rows of x;
-//             the two parts share no data.
+// Front end in two launches instead of three.
+//   route_quant_kernel (any batch): workgroups 0 .. nr-1 route 4 tokens each
+//             (one wave per token, route_token), the others quantise the
+//             rows of x; the two parts share no data.  Larger batches then
+//             run permute_align_kernel, small ones (T <= 64):
 //   permute_small_kernel: one workgroup.  Routing never gives a token the
 //             same expert twice, so one 64-bit LDS word per expert marks the
 //             tokens that chose it (T <= 64); a pair's stable rank in its
@@ -477,10 +478,8 @@ static void launch_route_quant(int mode, dim3 grid, int nr, hipStream_t s, const
 
 bool front_small_ok(int T, int E, int k) { return T >= 1 && T <= kSmallT && E <= 1024 && k <= kMaxTopK; }
 
-hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t* ids, float* w, int block_m, int nb,
-                              int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets, int32_t* npp,
-                              const void* x_bf16, int H, int64_t ld_x, int Hp, int mode, void* xq, void* xs,
-                              hipStream_t s) {
+hipError_t launch_route_and_quant(const float* logits, int T, int E, int k, int32_t* ids, float* w, const void* x_bf16,
+                                  int H, int64_t ld_x, int Hp, int mode, void* xq, void* xs, hipStream_t s) {
   const int nr = (T + 3) / 4;
   const int64_t units = (int64_t)T * (Hp / 128);
   int64_t qwg = (units + 15) / 16;  // 16 units per workgroup
@@ -494,7 +493,14 @@ hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t*
     launch_route_quant<5>(mode, grid, nr, s, logits, T, E, k, ids, w, x_bf16, H, ld_x, Hp, xq, xs, vec);
   else
     launch_route_quant<16>(mode, grid, nr, s, logits, T, E, k, ids, w, x_bf16, H, ld_x, Hp, xq, xs, vec);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t* ids, float* w, int block_m, int nb,
+                              int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets, int32_t* npp,
+                              const void* x_bf16, int H, int64_t ld_x, int Hp, int mode, void* xq, void* xs,
+                              hipStream_t s) {
+  hipError_t e = launch_route_and_quant(logits, T, E, k, ids, w, x_bf16, H, ld_x, Hp, mode, xq, xs, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, s, ids, T, k, E, block_m, nb, sorted_ids,
                      block_expert, offsets, npp);
