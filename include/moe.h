@@ -129,11 +129,13 @@ int32_t moe_max_blocks(int32_t num_pairs, int32_t num_experts, int32_t block_m);
 
 /* Bytes of scratch that moe_forward needs for up to T_max tokens (0 if the
  * configuration is invalid; non-decreasing in T_max).  Also enough for
- * moe_grouped_gemm2_combine.  The per-pair fp32 GEMM2 rows it holds are
- * capped near 1 GiB: larger batches run GEMM2 and the combine in column
- * chunks over one reused buffer.  It also covers the K-split scratch of small
- * batches (see moe_plan_ksplit): at most 8 * min(T*k, 1024) fp32 rows of
- * 2*Ip partial sums and of Hp y columns. */
+ * moe_grouped_gemm2_combine.  The per-pair GEMM2 rows it holds (2 bytes per
+ * value plus one byte per 64) are capped near 1 GiB: larger batches run GEMM2
+ * and the combine in column chunks over one reused buffer.  It also covers
+ * the K-split scratch (see moe_plan_ksplit): at most 8 * min(T*k, 1024) fp32
+ * rows of 2*Ip partial sums and y planes of Hp columns, or for a tail split
+ * 8 * W * block_m rows of 256 fp32 partial sums (W: moe_plan_ksplit's grid,
+ * one workgroup per compute unit rounded up to a multiple of 8). */
 size_t moe_workspace_bytes(const moe_cfg_t* cfg, int32_t T_max);
 
 /* Sizes in bytes of the intermediate aq / as buffers (rows = max_blocks *
@@ -260,28 +262,37 @@ moe_status_t moe_grouped_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const vo
                                        void* out_bf16, int64_t ld_out, void* ws,
                                        size_t ws_bytes, void* stream);
 
-/* K split of the grouped GEMMs for small batches (a launch choice; the pages
- * fix none).  With few (block, N tile) work items, each is cut into ksplit
- * pieces along K so that every compute unit streams weights:
+/* K split of the grouped GEMMs (a launch choice; the pages fix none).
+ * ksplit = 2, 4 or 8: with few (block, N tile) work items, each is cut into
+ * ksplit pieces along K so that every compute unit streams weights:
  *   GEMM1: piece i stores fp32 partial sums h_i of its K range; a second
  *          kernel forms h = h_0 + h_1 + ... (in piece order), then the clamped
  *          SwiGLU and the re-quantisation as above;
- *   GEMM2: piece i stores fl32(topk_w * y_f,i) for its K range in a plane of
+ *   GEMM2: piece i stores its weighted rows for its K range in a plane of
  *          its own; the combine adds, plane by plane, the slots in order.
- * Results equal the unsplit ones up to fp32 summation order.
+ * ksplit = -2, -4 or -8 (GEMM1 only, block_m 16 or 32; a "tail split"): the
+ *   items that fill whole rounds of one workgroup per compute unit run
+ *   unsplit with the fused epilogue, and only the remaining items are cut
+ *   into -ksplit pieces and finished by the second kernel, so the last
+ *   round is spread over every workgroup.
+ * Results equal the unsplit ones up to fp32 summation order (and, for a
+ * GEMM2 split, each plane's own storage of the weighted rows).
  * moe_plan_ksplit: the split moe_forward and moe_grouped_gemm2_combine use for
  * GEMM `which` (13: gate/up, 2: down) at T tokens on the current device
- * (1, 2, 4 or 8; 1 above 1024 pairs); -1 for invalid arguments.
+ * (1, 2, 4 or 8 when items would leave compute units idle, at most 1024
+ * pairs; else for GEMM1 at block_m 16/32 the tail split with the most pieces
+ * the scale layout allows; else 1); -1 for invalid arguments.
  * moe_splitk_bytes: scratch in bytes that the explicit-split entry points need
  * for that ksplit (0 for GEMM1 without a split; 0 also if the split is not
- * usable: ksplit must be 1, 2, 4 or 8 and divide K/128 into pieces of at
- * least 4 K blocks, multiples of 4 for MXFP4 and FP8_UE8M0, at most 1024
- * pairs, and for GEMM2 the y rows must fit one chunk). */
+ * usable: |ksplit| must be 1, 2, 4 or 8 and divide K/128 into pieces of at
+ * least 4 K blocks, multiples of 4 for MXFP4 and FP8_UE8M0; a positive split
+ * at most 1024 pairs, and for GEMM2 the y rows must fit one chunk; a tail
+ * split GEMM1 at block_m 16 or 32 only). */
 int32_t moe_plan_ksplit(const moe_cfg_t* cfg, int32_t T, int32_t which);
 size_t moe_splitk_bytes(const moe_cfg_t* cfg, int32_t T, int32_t which, int32_t ksplit);
 
 /* moe_grouped_gemm1_swiglu with an explicit K split (ksplit = 1: the same
- * launch as moe_grouped_gemm1_swiglu).  ws: at least moe_splitk_bytes(cfg,
+ * launch as moe_grouped_gemm1_swiglu; negative: a tail split).  ws: at least moe_splitk_bytes(cfg,
  * T, 13, ksplit) bytes of scratch (may be NULL when that is 0).  An unusable
  * ksplit returns MOE_ERR_UNSUPPORTED before anything is enqueued. */
 moe_status_t moe_grouped_gemm1_swiglu_splitk(const moe_cfg_t* cfg, int32_t T, const void* xq,

@@ -87,9 +87,22 @@ int gemm_n_tiles(const moe_cfg_t* c, int which) {
   return which == 13 ? c->pad.inter_padded / 128 : (c->pad.hidden_padded + 255) / 256;
 }
 
+// Tail split of GEMM1 (ksplit -2, -4 or -8): only the items past the grid's
+// whole rounds are cut into -ksplit pieces; block_m 16 or 32 (the partial
+// sums of a leftover item are block_m rows of 256 floats per piece).
+bool tail_usable(const moe_cfg_t* c, int which, int ks) {
+  return which == 13 && (c->block_m == 16 || c->block_m == 32) && ks < -1 &&
+         moe::ksplit_ok(c->quant_mode, gemm_kb(c, which), -ks);
+}
+size_t tail_bytes(const moe_cfg_t* c, int ks) {
+  return align_up((size_t)((int64_t)ks * moe::gemm_grid_max() * c->block_m * 256 * 4));
+}
+
 // A K split for GEMM `which` at T tokens is usable if the pieces align with
-// the scale layout and, for GEMM2, y is not column-chunked.
+// the scale layout and, for GEMM2, y is not column-chunked; a tail split
+// (negative) as tail_usable.
 bool ksplit_usable(const moe_cfg_t* c, int32_t T, int which, int ks) {
+  if (ks < 0) return tail_usable(c, which, ks);
   if (!moe::ksplit_ok(c->quant_mode, gemm_kb(c, which), ks)) return false;
   if (ks == 1) return true;
   const int64_t P = (int64_t)T * c->top_k;
@@ -97,15 +110,24 @@ bool ksplit_usable(const moe_cfg_t* c, int32_t T, int which, int ks) {
   return which == 13 || moe::y_chunk_cols(P, c->pad.hidden_padded) == c->pad.hidden_padded;
 }
 
+// The split the library uses: a K split of every item when workgroups would
+// otherwise idle; else, for GEMM1 at block_m 16/32 where the last round of
+// items is expected to leave most workgroups idle, a tail split into the
+// most pieces the scale layout allows.
 int plan_ksplit(const moe_cfg_t* c, int32_t T, int which) {
   const int ks = moe::pick_ksplit(c->quant_mode, T, c->num_experts, c->top_k, c->block_m, gemm_kb(c, which),
                                   gemm_n_tiles(c, which));
-  return ksplit_usable(c, T, which, ks) ? ks : 1;
+  if (ks > 1 && ksplit_usable(c, T, which, ks)) return ks;
+  if (which == 13 && moe::tail_split_plan_ok(T, c->num_experts, c->top_k, c->block_m, gemm_n_tiles(c, which)))
+    for (int t = -moe::kSplitMax; t <= -2; t /= 2)
+      if (tail_usable(c, which, t)) return t;
+  return 1;
 }
 
 // Scratch of a GEMM at split ks: GEMM1 the fp32 partial sums and each pair's
 // sorted row (none without a split), GEMM2 the y planes.
 size_t split_bytes(const moe_cfg_t* c, int32_t T, int which, int ks) {
+  if (ks < 0) return tail_bytes(c, -ks);
   const int64_t P = (int64_t)T * c->top_k;
   const int64_t Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
   if (which == 13) return ks > 1 ? align_up((size_t)(ks * P * 2 * Ip * 4 + P * 4)) : 0;
@@ -121,7 +143,11 @@ size_t split_reserve(const moe_cfg_t* c, int32_t T, int which) {
   const int64_t Ps = P < moe::kSplitMaxPairs ? P : moe::kSplitMaxPairs;
   const int cap = moe::ksplit_cap(c->quant_mode, gemm_kb(c, which));
   const int64_t Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
-  if (which == 13) return cap > 1 ? align_up((size_t)(cap * Ps * 2 * Ip * 4 + Ps * 4)) : 0;
+  if (which == 13) {
+    const size_t full = cap > 1 ? align_up((size_t)(cap * Ps * 2 * Ip * 4 + Ps * 4)) : 0;
+    const size_t tail = tail_usable(c, 13, -cap) ? tail_bytes(c, cap) : 0;
+    return full > tail ? full : tail;
+  }
   const int64_t planes = cap > 1 ? cap * moe::y_plane_bytes(Ps, Hp) : 0, y = moe::y_reserve_bytes(P, Hp);
   return align_up((size_t)(planes > y ? planes : y));
 }
@@ -233,6 +259,16 @@ int log2_of(int ks) { return ks >= 8 ? 3 : ks >= 4 ? 2 : ks >= 2 ? 1 : 0; }
 // SwiGLU and re-quantisation kernel.
 hipError_t run_gemm1(const moe_cfg_t* c, int32_t T, moe::GemmArgs a, int32_t nb, int ks, float* part,
                      hipStream_t s) {
+  if (ks < -1) {
+    a.tail = 1;
+    a.ks_log2 = log2_of(-ks);
+    a.part = part;
+    hipError_t e = moe::launch_gemm1(c->quant_mode, c->block_m, nb, a, s);
+    if (e != hipSuccess) return e;
+    return moe::launch_gemm1_tail_finish(c->quant_mode, -ks, c->block_m, part, a.sorted_ids, a.npp, a.n_tiles,
+                                         moe::gemm_grid_max(), (int)((int64_t)T * c->top_k), a.Ip, a.limit, a.aq,
+                                         a.as, s);
+  }
   if (ks > 1) {
     a.ks_log2 = log2_of(ks);
     a.part = part;
@@ -446,7 +482,7 @@ moe_status_t moe_grouped_gemm1_swiglu_splitk(const moe_cfg_t* cfg, int32_t T, co
   if (T == 0) return MOE_OK;
   if (!xq || !xs || !sorted_ids || !block_expert || !num_post_padded || !w13 || !w13_scale || !aq || !as)
     return MOE_ERR_NULL;
-  if (ksplit > 1 && !ws) return MOE_ERR_NULL;
+  if (ksplit != 1 && !ws) return MOE_ERR_NULL;
   if (ws_bytes < split_bytes(cfg, T, 13, ksplit)) return MOE_ERR_WORKSPACE;
   const int32_t nb = max_blocks((int64_t)T * cfg->top_k, cfg->num_experts, cfg->block_m);
   moe::GemmArgs a = gemm1_args(cfg, T, xq, xs, sorted_ids, block_expert, num_post_padded, w13, w13_scale, aq, as);

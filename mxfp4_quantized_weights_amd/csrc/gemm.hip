@@ -87,6 +87,13 @@ __device__ __forceinline__ void widen_fp8(const v8i& w, v8h (&h)[4]) {
 // ===========================================================================
 constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 
+// A tail launch over W workgroups splits its leftover items (items mod W)
+// only when they fill at most half a round: a lightly filled last round
+// streams faster than a full one, and splitting a fuller one costs more in
+// pieces and partial sums than it saves (decode, one MI355X: T = 16, 32, 64
+// with 28-31% of a round left gain 1-5%; 69-82% left lose 2-14%).
+__host__ __device__ inline bool tail_split_on(int items, int W) { return 2 * (items % W) <= W; }
+
 // Waves of a workgroup: 4 column waves (the N tile's 16 weight tiles, 4 each)
 // times BM/64 token halves of 64 tokens; for BM < 64 one token group of BM/16
 // tiles.  A wave multiplies MT token tiles by its 4 weight tiles.
@@ -121,19 +128,22 @@ struct Ring {
 // Direct global->LDS loads, written as inline assembly so that the compiler's
 // automatic wait insertion does not see them (it would add vmcnt(0) in front
 // of every LDS read of the ring); the kernel waits for them itself.  M0 holds
-// the wave-uniform LDS base (one wait state before the load reads it).  The
+// the wave-uniform LDS base (one wait state before the load reads it); every
+// caller's base is uniform by construction, and readfirstlane states it for
+// bases the compiler cannot prove uniform (those that go through the item
+// cursors).  The
 // weight loads carry the non-temporal hint: weights are read once per launch.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the compiler does not use it in these kernels
 template <bool NT>
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
   else
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -555,6 +565,28 @@ __device__ __forceinline__ void epilogue_gemm1_part(const GemmArgs& p, const v4f
   }
 }
 
+// GEMM1 epilogue of a K piece of a tail launch's leftover item r: the fp32
+// partial sums of every row of the block (pad rows too; the finishing kernel
+// zeroes them) for the N tile's 128 gate and 128 up columns,
+// part[piece][r][row][256] (gate 0..127, up 128..255) with r < gridDim.x,
+// in the lane layout of epilogue_gemm1_s.
+template <int MT, int BM>
+__device__ __forceinline__ void epilogue_gemm1_tail(const GemmArgs& p, const v4f (&acc)[MT][4], int piece, int r,
+                                                    int wt, int wn) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int t = wt * 64 + m * 16 + c16;
+    float* row = p.part + (((int64_t)piece * gridDim.x + r) * BM + t) * 256 + 32 * wn + 4 * q;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const v4f g = acc[m][jj], u = acc[m][jj + 2];
+      *(float4*)(row + 16 * jj) = make_float4(g[0], g[1], g[2], g[3]);
+      *(float4*)(row + 128 + 16 * jj) = make_float4(u[0], u[1], u[2], u[3]);
+    }
+  }
+}
+
 // GEMM2 epilogue: the weighted rows v = routing weight * C of real pairs, in
 // y's block floating point (y_plane_bytes): int16 q = rint(v * 2^-s) with one
 // exponent s = max(floor(log2 max|v|) - 14, -128) per 64 columns of a row.
@@ -644,30 +676,56 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wt = wave >> 2, wn = wave & 3;
-  // items of XCD x: the contiguous chunk x; workgroup j of the XCD takes
-  // items j, j + nw, j + 2 nw, ... of it (nw workgroups per XCD)
+  // A workgroup's items: n_whole whole (M block, N tile) items, then n_tail
+  // K pieces.  Pieces of one list are spread as the items of the plain
+  // kernel: the list is cut into one contiguous chunk per XCD, and workgroup
+  // j of the XCD takes pieces j, j + nw, j + 2 nw, ... of it (nw workgroups
+  // per XCD; workgroups go to the XCDs round-robin).
+  //   plain and K-split launches: no whole items; the list is every item
+  //     cut into 2^KSL pieces (KSL = 0: the items themselves).
+  //   tail launches (p.tail): the items that fill whole rounds of the grid
+  //     (F per workgroup, XCD-chunked the same way), then the remaining
+  //     items cut into 2^KSL pieces, whose fp32 partial sums a second
+  //     kernel finishes (launch_gemm1_tail_finish) -- when the remaining
+  //     items fill at most half a round (tail_split_on); else the launch
+  //     runs every item whole, as the plain kernel.
   const int npp = __builtin_amdgcn_readfirstlane(*p.npp);
-  const int KSL = SPLIT ? p.ks_log2 : 0;  // K pieces per item: 2^KSL
-  const int items = ((npp / BM) * p.n_tiles) << KSL;
-  const int per = (items + kXcds - 1) / kXcds;
-  const int lo = (blockIdx.x % kXcds) * per;
-  const int hi = min(lo + per, items);
   const int nw = gridDim.x / kXcds;
-  const int first = lo + (int)(blockIdx.x / kXcds);
-  if (first >= hi) return;
-  const int n_my = (hi - first + nw - 1) / nw;
+  const int xcd = blockIdx.x % kXcds, jw = blockIdx.x / kXcds;
+  const int all_items = (npp / BM) * p.n_tiles;
+  const bool tail = SPLIT && p.tail && tail_split_on(all_items, (int)gridDim.x);
+  const int KSL = SPLIT && (tail || !p.tail) ? p.ks_log2 : 0;  // K pieces per split item: 2^KSL
+  int n_whole = 0, wbase = 0, tail_base = 0, list = all_items << KSL;
+  if (tail) {
+    const int F = all_items / (int)gridDim.x;
+    n_whole = F;
+    wbase = xcd * F * nw + jw;
+    tail_base = F * (int)gridDim.x;
+    list = (all_items - tail_base) << KSL;
+  }
+  const int per = (list + kXcds - 1) / kXcds;
+  const int lo = xcd * per;
+  const int hi = min(lo + per, list);
+  const int first = lo + jw;
+  const int n_tail = first < hi ? (hi - first + nw - 1) / nw : 0;
+  const int n_my = n_whole + n_tail;
+  if (n_my == 0) return;
   const int KB = p.K / 128;   // K blocks of a weight row
-  const int KBI = KB >> KSL;  // K blocks of an item
+  const int KBP = KB >> KSL;  // K blocks of a piece
   const int NG = tiled_n_groups(p.N);  // N tiles of the weight matrix (TILED_V2)
-  const int total = n_my * KBI;
+  const int total = n_whole * KB + n_tail * KBP;
+  // item -> (M block, N tile, K piece), K pieces innermost
+  auto item_g = [&](int ii) {
+    return ii < n_whole ? wbase + ii * nw : tail_base + ((first + (ii - n_whole) * nw) >> KSL);
+  };
+  auto item_m = [&](int ii) { return item_g(ii) / p.n_tiles; };
+  auto item_nt = [&](int ii) { return p.nt0 + item_g(ii) % p.n_tiles; };
+  auto item_ks = [&](int ii) { return ii < n_whole ? 0 : (first + (ii - n_whole) * nw) & ((1 << KSL) - 1); };
+  auto item_kbi = [&](int ii) { return ii < n_whole ? KB : KBP; };
   // Items of fewer than S K blocks finish inside the prologue (which issues
   // S-1 K blocks without waiting) or within S-1 steps of the next item's
   // metadata loads: their metadata is waited for explicitly.
-  const bool short_items = KBI < S;
-  // item -> (M block, N tile, K piece), K pieces innermost
-  auto item_m = [&](int ii) { return ((first + ii * nw) >> KSL) / p.n_tiles; };
-  auto item_nt = [&](int ii) { return p.nt0 + ((first + ii * nw) >> KSL) % p.n_tiles; };
-  auto item_ks = [&](int ii) { return (first + ii * nw) & ((1 << KSL) - 1); };
+  auto short_item = [&](int ii) { return item_kbi(ii) < S; };
 
   // sorted pair ids of item ii -> ids_lds[ii % NB] (waves 0 .. NI-1), its
   // block's expert -> exp_lds[ii % NB] (lane 0 of the last wave)
@@ -694,7 +752,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   int wts_step = -1, wts_item = 0;
   auto setup_issue = [&](int ii, int s) {
     const int m = item_m(ii), nt = item_nt(ii);
-    const int kb0 = item_ks(ii) * KBI;  // first K block of the item
+    const int kb0 = item_ks(ii) * KBP;  // first K block of the item (0 for whole items)
     const int e = __builtin_amdgcn_readfirstlane(exp_lds[ii % NB]);
 #pragma unroll
     for (int q = 0; q < R::DW; ++q) {
@@ -742,7 +800,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
     // explicit wait when items are short)
     if (ii + 1 < n_my) {
       issue_ids(ii + 1);
-      if (short_items) {
+      if (short_item(ii)) {
         vm_wait_barrier<0>();
         if constexpr (!G1) {
           issue_wts(ii + 1);
@@ -763,12 +821,14 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
 #pragma unroll
     for (int j = 0; j < 4; ++j) tiles[j] = 4 * wn + j;
   }
-  int c_nt = 0, c_row0 = 0, c_mv = MT, c_ks = 0;
+  int c_nt = 0, c_row0 = 0, c_mv = MT, c_ks = 0, c_kbi = KB, c_g = 0;
   bool active = true;
   auto setup_compute = [&](int ii) {
     c_nt = item_nt(ii);
     c_ks = item_ks(ii);
     c_row0 = item_m(ii) * BM;
+    c_kbi = item_kbi(ii);
+    c_g = item_g(ii);
     if constexpr (!G1) active = c_nt * 256 + 64 * wn < p.N;
     // real rows are a prefix of the block: count the wave's token tiles
     // that start with one
@@ -788,7 +848,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   // issue cursor (item, K block) and MX weight-scale groups: the group of up
   // to 4 K blocks that starts at K block kb (kb % 4 == 0) goes to
   // ws_buf[group count % NWS] with the loads of that K block
-  int i_ii = 0, i_kb = 0, i_grp = 0;
+  int i_ii = 0, i_kb = 0, i_grp = 0, i_kbi = item_kbi(0);
   auto issue_next = [&](auto slot_c, int s) {
     if (i_ii < n_my) {
       const uint8_t* ws = nullptr;
@@ -796,12 +856,15 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
         if ((i_kb & 3) == 0) ws = ws_buf[(i_grp++) % NWS];
       }
       ring_issue<MODE, BM>(rs, slot(slot_c), wave, i_kb, ws);
-      if (++i_kb == KBI) {
+      if (++i_kb == i_kbi) {
         i_kb = 0;
-        if (++i_ii < n_my) setup_issue(i_ii, s);
+        if (++i_ii < n_my) {
+          i_kbi = item_kbi(i_ii);
+          setup_issue(i_ii, s);
+        }
       }
     } else {
-      ring_issue<MODE, BM>(rs, slot(slot_c), wave, KBI - 1, nullptr);  // past the end: reload, never read
+      ring_issue<MODE, BM>(rs, slot(slot_c), wave, i_kbi - 1, nullptr);  // past the end: reload, never read
     }
   };
 
@@ -837,13 +900,19 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
     }
     if (active && c_mv > 0)
       ring_compute<MODE, BM, G1>(slot(std::integral_constant<int, d>{}), c_ws, tiles, wt, c_kb, sw0, sw1, c_mv, acc);
-    if (++c_kb == KBI) {
+    if (++c_kb == c_kbi) {
       const int32_t* ids = ids_lds[c_ii % NB];
       if constexpr (G1) {
-        if constexpr (SPLIT)
-          epilogue_gemm1_part<MODE, MT>(p, acc, ids, c_row0, c_ks, c_nt, wt, wn);
-        else
+        if constexpr (SPLIT) {
+          if (!p.tail)
+            epilogue_gemm1_part<MODE, MT>(p, acc, ids, c_row0, c_ks, c_nt, wt, wn);
+          else if (!tail || c_ii < n_whole)
+            epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
+          else
+            epilogue_gemm1_tail<MT, BM>(p, acc, c_ks, c_g - tail_base, wt, wn);
+        } else {
           epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
+        }
       } else {
         if (active) epilogue_gemm2_s<MT>(p, acc, ids, wts_lds[c_ii % NB], c_ks, c_nt, wt, wn);
       }
@@ -886,6 +955,8 @@ static int device_cus() {
   return cus[dev];
 }
 
+int gemm_grid_max() { return (device_cus() + kXcds - 1) / kXcds * kXcds; }
+
 // Kernels with a K split (SPLIT) are separate instances, so that the plain
 // ones carry none of its per-item state.
 template <int MODE, bool G1, bool SPLIT>
@@ -896,8 +967,9 @@ static hipError_t launch_gemm_split(int block_m, int nb, const GemmArgs& a, hipS
   // there are fewer items; a multiple of kXcds so that every XCD gets the
   // same number of workgroups.
   const int64_t items = ((int64_t)nb * a.n_tiles) << a.ks_log2;
-  const int64_t wgs = (device_cus() + kXcds - 1) / kXcds * kXcds;
-  const dim3 grid((unsigned)(items < wgs ? (items + kXcds - 1) / kXcds * kXcds : wgs));
+  const int64_t wgs = gemm_grid_max();
+  // a tail launch splits the items past the grid's whole rounds: all of it
+  const dim3 grid((unsigned)(a.tail || items >= wgs ? wgs : (items + kXcds - 1) / kXcds * kXcds));
   switch (block_m) {
     case 16:
       hipLaunchKernelGGL((moe_gemm_stream_kernel<MODE, 16, G1, SD, SPLIT>), grid, dim3(Ring<MODE, 16>::NTH), 0, s,
@@ -963,15 +1035,32 @@ bool ksplit_ok(int mode, int KB, int ks) {
   return mode == kQuantFp8 || (KB / ks) % 4 == 0;
 }
 
-int pick_ksplit(int mode, int T, int E, int k, int block_m, int KB, int n_tiles) {
+// Expected (M block, N tile) items of a GEMM under uniform routing: active
+// experts E * (1 - (1 - k/E)^T); blocks: one per active expert while an
+// expert's share of pairs fits one block.
+static double expected_items(int T, int E, int k, int block_m, int n_tiles) {
   const int64_t P = (int64_t)T * k;
-  if (P <= 0 || P > kSplitMaxPairs) return 1;
-  // expected active experts E * (1 - (1 - k/E)^T); blocks: one per active
-  // expert while an expert's share of pairs fits one block
   const double active = (double)E * (1.0 - pow(1.0 - (double)k / E, (double)T));
   const double share = (double)P / (active > 1.0 ? active : 1.0);
   const double blocks = share <= block_m ? active : (double)P / block_m + 0.5 * active;
-  const double items = blocks * n_tiles;
+  return blocks * n_tiles;
+}
+
+bool tail_split_plan_ok(int T, int E, int k, int block_m, int n_tiles) {
+  // the kernel splits the leftover items only when they fill at most half a
+  // round (tail_split_on); skip planning a tail launch (and its second,
+  // finishing kernel) where the estimate leaves clearly more, with margin
+  // for the estimate's error of a few experts
+  const double W = (double)gemm_grid_max();
+  const double items = expected_items(T, E, k, block_m, n_tiles);
+  const double left = items - W * floor(items / W);
+  return T > 0 && left <= 0.7 * W;
+}
+
+int pick_ksplit(int mode, int T, int E, int k, int block_m, int KB, int n_tiles) {
+  const int64_t P = (int64_t)T * k;
+  if (P <= 0 || P > kSplitMaxPairs) return 1;
+  const double items = expected_items(T, E, k, block_m, n_tiles);
   // a split only pays while workgroups would otherwise sit idle: once every
   // workgroup has an item, shorter pieces stream the same bytes per CU and
   // add the partial sums' round trip
@@ -1067,6 +1156,125 @@ hipError_t launch_swiglu_requant(int mode, const float* part, int ks, int P, int
     launch_requant_mode<kQuantFp8E8>(part, ks, P, Ip, limit, aq, as, s);
   else
     launch_requant_mode<kQuantMx>(part, ks, P, Ip, limit, aq, as, s);
+  return hipGetLastError();
+}
+
+// Second kernel of a tail launch: workgroup r < (leftover items) finishes
+// leftover item r (M block m, N tile nt of the items after the grid's whole
+// rounds, the numbering of the GEMM kernel): per row, the KS pieces' fp32
+// partial sums added in piece order, then the clamped SwiGLU and the
+// re-quantisation of epilogue_gemm1_s for the N tile's 128 intermediate
+// columns; pad rows get zero codes and scales.  32 threads per row (4
+// columns each), 8 rows at a time.
+template <int QMODE, int KS, int BM>
+__global__ __launch_bounds__(256) void gemm1_tail_finish_kernel(const float* __restrict__ part,
+                                                                const int32_t* __restrict__ sorted_ids,
+                                                                const int32_t* __restrict__ npp_p, int n_tiles, int W,
+                                                                int P, int Ip, float L, uint8_t* __restrict__ aq,
+                                                                void* __restrict__ as) {
+  const int items = (*npp_p / BM) * n_tiles;
+  const int F = items / W;
+  const int r = blockIdx.x;
+  if (!tail_split_on(items, W) || r >= items - F * W) return;
+  const int g = F * W + r, m = g / n_tiles, nt = g % n_tiles;
+  const int c = (threadIdx.x & 31) * 4;  // intermediate column within the N tile
+  for (int t = threadIdx.x >> 5; t < BM; t += 8) {
+    const int64_t row = (int64_t)m * BM + t;
+    const bool real = sorted_ids[row] < P;
+    float a[4];
+    {
+      // all pieces' loads first, then the sums in piece order
+      float4 gv[KS], uv[KS];
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        const float* src = part + (((int64_t)i * W + r) * BM + t) * 256 + c;
+        gv[i] = *(const float4*)src;
+        uv[i] = *(const float4*)(src + 128);
+      }
+      float4 gs = gv[0], us = uv[0];
+#pragma unroll
+      for (int i = 1; i < KS; ++i) {
+        gs.x += gv[i].x; gs.y += gv[i].y; gs.z += gv[i].z; gs.w += gv[i].w;
+        us.x += uv[i].x; us.y += uv[i].y; us.z += uv[i].z; us.w += uv[i].w;
+      }
+      a[0] = real ? swiglu_clamped(gs.x, us.x, L) : 0.0f;
+      a[1] = real ? swiglu_clamped(gs.y, us.y, L) : 0.0f;
+      a[2] = real ? swiglu_clamped(gs.z, us.z, L) : 0.0f;
+      a[3] = real ? swiglu_clamped(gs.w, us.w, L) : 0.0f;
+    }
+    float mx = fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3])));
+    constexpr int GT = QMODE == kQuantMx ? 8 : 32;  // threads of one group
+#pragma unroll
+    for (int o = 1; o < GT; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const bool lead = (threadIdx.x & (GT - 1)) == 0;
+    const int col = nt * 128 + c;
+    if constexpr (QMODE == kQuantMx) {
+      const uint32_t b = e8m0_byte(mx);
+      const float inv = e8m0_inverse(b);
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed |= mx_quant(a[i], inv) << (4 * i);
+      *(uint16_t*)(aq + row * (Ip / 2) + col / 2) = (uint16_t)packed;
+      if (lead) ((uint8_t*)as)[row * (Ip / 32) + col / 32] = (uint8_t)b;
+    } else if constexpr (QMODE == kQuantFp8E8) {
+      const uint32_t b = ue8m0_byte(mx);
+      const float inv = e8m0_inverse(b);
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed |= ((mx > 0.0f) ? fp8e8_quant(a[i], inv) : 0u) << (8 * i);
+      *(uint32_t*)(aq + row * Ip + col) = packed;
+      if (lead) ((uint8_t*)as)[row * e8_scale_ld(Ip) + nt] = (uint8_t)b;
+    } else {
+      const float sc = mx / kE4M3Max;
+      const float inv = 1.0f / sc;
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) packed |= ((mx > 0.0f) ? fp8_quant_inv(a[i], inv) : 0u) << (8 * i);
+      *(uint32_t*)(aq + row * Ip + col) = packed;
+      if (lead) ((float*)as)[row * (Ip / 128) + nt] = (mx > 0.0f) ? sc : 0.0f;
+    }
+  }
+}
+
+template <int QMODE, int BM>
+static void launch_tail_finish_bm(int ks, const float* part, const int32_t* sorted, const int32_t* npp, int n_tiles,
+                                  int W, int P, int Ip, float limit, uint8_t* aq, void* as, hipStream_t s) {
+  const dim3 grid((unsigned)W), block(256);
+  switch (ks) {
+    case 2:
+      hipLaunchKernelGGL((gemm1_tail_finish_kernel<QMODE, 2, BM>), grid, block, 0, s, part, sorted, npp, n_tiles, W,
+                         P, Ip, limit, aq, as);
+      break;
+    case 4:
+      hipLaunchKernelGGL((gemm1_tail_finish_kernel<QMODE, 4, BM>), grid, block, 0, s, part, sorted, npp, n_tiles, W,
+                         P, Ip, limit, aq, as);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm1_tail_finish_kernel<QMODE, 8, BM>), grid, block, 0, s, part, sorted, npp, n_tiles, W,
+                         P, Ip, limit, aq, as);
+      break;
+  }
+}
+
+template <int QMODE>
+static void launch_tail_finish_mode(int ks, int block_m, const float* part, const int32_t* sorted,
+                                    const int32_t* npp, int n_tiles, int W, int P, int Ip, float limit, uint8_t* aq,
+                                    void* as, hipStream_t s) {
+  if (block_m == 16)
+    launch_tail_finish_bm<QMODE, 16>(ks, part, sorted, npp, n_tiles, W, P, Ip, limit, aq, as, s);
+  else
+    launch_tail_finish_bm<QMODE, 32>(ks, part, sorted, npp, n_tiles, W, P, Ip, limit, aq, as, s);
+}
+
+hipError_t launch_gemm1_tail_finish(int mode, int ks, int block_m, const float* part, const int32_t* sorted,
+                                    const int32_t* npp, int n_tiles, int W, int P, int Ip, float limit, uint8_t* aq,
+                                    void* as, hipStream_t s) {
+  if (mode == kQuantFp8)
+    launch_tail_finish_mode<kQuantFp8>(ks, block_m, part, sorted, npp, n_tiles, W, P, Ip, limit, aq, as, s);
+  else if (mode == kQuantFp8E8)
+    launch_tail_finish_mode<kQuantFp8E8>(ks, block_m, part, sorted, npp, n_tiles, W, P, Ip, limit, aq, as, s);
+  else
+    launch_tail_finish_mode<kQuantMx>(ks, block_m, part, sorted, npp, n_tiles, W, P, Ip, limit, aq, as, s);
   return hipGetLastError();
 }
 

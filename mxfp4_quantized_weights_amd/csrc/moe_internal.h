@@ -112,6 +112,7 @@ struct GemmArgs {
   int64_t yplane;         // GEMM2 with a K split: bytes between the y planes of the K pieces
   int64_t yexp;           // GEMM2: byte offset of the exponents within a plane
   int32_t tile_run;       // TILED_V2 tile run R of B (tile_run(mode, which))
+  int32_t tail;           // GEMM1 with a K split: whole items in whole rounds, only the rest split (see below)
 };
 
 // K split of the grouped GEMMs for small batches.  When few (M block, N tile)
@@ -132,6 +133,22 @@ bool ksplit_ok(int mode, int KB, int ks);
 // workgroups (one per CU), from the expected number of active experts under
 // uniform routing.  Host-only; depends on the device's CU count.
 int pick_ksplit(int mode, int T, int E, int k, int block_m, int KB, int n_tiles);
+
+// Tail split of GEMM1 (block_m 16 or 32): a launch over gemm_grid_max()
+// workgroups runs the F = floor(items / W) whole rounds of (M block, N tile)
+// items unsplit, with the fused epilogue, and cuts only the items past them
+// into ks pieces, which store fp32 partial sums part[piece][r][block_m][256]
+// (r < W: leftover item r; 128 gate then 128 up columns of its N tile).  A
+// second kernel (one workgroup per possible r) adds the pieces in order and
+// applies the clamped SwiGLU and the re-quantisation.  This evens out the last
+// round of items without splitting the rest.
+int gemm_grid_max();
+// Whether the planner uses a tail split for a GEMM1 of n_tiles N tiles at T
+// tokens (estimated leftover items at most 0.7 of a round).
+bool tail_split_plan_ok(int T, int E, int k, int block_m, int n_tiles);
+hipError_t launch_gemm1_tail_finish(int mode, int ks, int block_m, const float* part, const int32_t* sorted,
+                                    const int32_t* npp, int n_tiles, int W, int P, int Ip, float limit, uint8_t* aq,
+                                    void* as, hipStream_t s);
 
 // GEMM1 with a K split (ks = 2, 4 or 8), second half: for each pair f < P,
 // h = sum over pieces of part[piece, f], then the clamped SwiGLU and the

@@ -242,16 +242,33 @@ def test_ksplit_plan_and_scratch():
     assert M.plan_ksplit(c, 1, 13) == 4 and M.plan_ksplit(c, 1, 2) == 2
     # two tokens: ~15.8 experts, 126 GEMM1 items -> 2 pieces; GEMM2 none
     assert M.plan_ksplit(c, 2, 13) == 2 and M.plan_ksplit(c, 2, 2) == 1
-    # 64 tokens: ~240 active experts, every workgroup has items: no split
-    assert M.plan_ksplit(c, 64, 13) == 1 and M.plan_ksplit(c, 64, 2) == 1
+    # 64 tokens: ~240 active experts, every workgroup has items: GEMM1 takes
+    # the tail split (whole rounds unsplit, the rest in 8 pieces), GEMM2 none
+    assert M.plan_ksplit(c, 64, 13) == -8 and M.plan_ksplit(c, 64, 2) == 1
     # a shared expert (E = 1, top-1): 8 GEMM1 items -> 8 pieces
     assert M.plan_ksplit(cfg(num_experts=1, top_k=1, block_m=128), 64, 13) == 8
-    # above 1024 pairs: never split
-    assert M.plan_ksplit(c, 129, 13) == 1 and M.plan_ksplit(c, 4096, 2) == 1
+    # above 1024 pairs: no split of every item; GEMM1 at block_m 16/32 keeps
+    # the tail split (it needs no per-pair scratch) where the last round is
+    # expected to be mostly idle: 100 experts at block_m 32 and 400 tokens give
+    # ~800 items, 32 past 3 rounds of 256; at 129 tokens ~2240 items leave 0.75
+    # of a round (the kernel would not split it), and 8 tokens ~470 items 0.84
+    assert M.plan_ksplit(c, 129, 13) == 1 and M.plan_ksplit(c, 4096, 2) == 1 and M.plan_ksplit(c, 8, 13) == 1
+    assert M.plan_ksplit(cfg(num_experts=100, block_m=64), 400, 13) == 1
+    assert M.plan_ksplit(cfg(num_experts=100, block_m=32), 400, 13) == -8
+    assert M.plan_ksplit(c, 16, 13) == -8 and M.plan_ksplit(c, 32, 13) == -8
+    assert M.plan_ksplit(cfg(inter=256), 64, 13) == 1   # 2 N tiles: ~480 items, 0.875 of a round left
     assert M.plan_ksplit(c, 1, 7) == -1
     P = 64 * 8
     for ks in (1, 2, 4, 8):
         assert M.splitk_bytes(c, 64, 13, ks) == (0 if ks == 1 else ks * P * 2048 * 4 + P * 4)
+    # a tail split: the pieces of at most one leftover item per workgroup (256
+    # compute units assumed here), block_m rows of 256 fp32 partial sums each
+    for ks in (2, 4, 8):
+        assert M.splitk_bytes(c, 64, 13, -ks) == ks * 256 * 16 * 256 * 4
+        assert M.splitk_bytes(cfg(block_m=32), 64, 13, -ks) == ks * 256 * 32 * 256 * 4
+        assert M.splitk_bytes(cfg(block_m=64), 64, 13, -ks) == 0   # block_m 16 or 32 only
+        assert M.splitk_bytes(c, 64, 2, -ks) == 0                  # GEMM1 only
+    assert M.splitk_bytes(c, 64, 13, -3) == 0 and M.splitk_bytes(c, 64, 13, -16) == 0
     # GEMM2's y plane: int16 values [P, Hp] and one exponent byte per 64 columns
     plane = P * 4096 * 2 + P * 4096 // 64
     assert M.splitk_bytes(c, 64, 2, 2) == 2 * plane
@@ -263,10 +280,12 @@ def test_ksplit_plan_and_scratch():
     assert M.splitk_bytes(c, 129, 13, 2) == 0        # 1032 pairs
     c24 = cfg(hidden=3072)                           # 24 K blocks
     assert M.splitk_bytes(c24, 4, 13, 4) > 0         # FP8: 6 K blocks per piece
+    assert M.splitk_bytes(c24, 4, 13, -8) == 0 and M.plan_ksplit(c24, 64, 13) == -4
     for q in ("mxfp4", "fp8_ue8m0"):
         assert M.splitk_bytes(cfg(quant=q, hidden=3072), 4, 13, 4) == 0
         assert M.splitk_bytes(cfg(quant=q, hidden=3072), 4, 13, 2) > 0
         assert M.plan_ksplit(cfg(quant=q, hidden=3072), 1, 13) == 2
+        assert M.plan_ksplit(cfg(quant=q, hidden=3072), 64, 13) == -2
     # every planned split fits the layer workspace, which stays monotone
     for q in ("fp8", "mxfp4", "fp8_ue8m0"):
         for E, k, bm in ((288, 8, 16), (1, 1, 128), (16, 4, 32)):
@@ -290,8 +309,14 @@ def test_ksplit_entry_points_validate_before_launch():
     assert lib.moe_grouped_gemm1_swiglu_splitk(*args1, 16, FAKE, big, None) == UNSUP
     assert lib.moe_grouped_gemm1_swiglu_splitk(*args1, 2, FAKE, 1024, None) == WS
     assert lib.moe_grouped_gemm1_swiglu_splitk(*args1, 2, None, big, None) == NULL
+    assert lib.moe_grouped_gemm1_swiglu_splitk(*args1, -3, FAKE, big, None) == UNSUP
+    assert lib.moe_grouped_gemm1_swiglu_splitk(*args1, -8, FAKE, 1024, None) == WS
+    assert lib.moe_grouped_gemm1_swiglu_splitk(*args1, -8, None, big, None) == NULL
+    c64 = cfg(block_m=64)
+    assert lib.moe_grouped_gemm1_swiglu_splitk(ctypes.byref(c64), 4, *([FAKE] * 9), -8, FAKE, big, None) == UNSUP
     args2 = [ctypes.byref(c), 4] + [FAKE] * 9 + [4096]
     assert lib.moe_grouped_gemm2_combine_splitk(*args2, 4, FAKE, big, None) == UNSUP
+    assert lib.moe_grouped_gemm2_combine_splitk(*args2, -2, FAKE, big, None) == UNSUP
     assert lib.moe_grouped_gemm2_combine_splitk(*args2, 2, FAKE, 1024, None) == WS
     assert lib.moe_grouped_gemm2_combine_splitk(*args2[:-1], 100, 2, FAKE, big, None) == SHAPE
     assert lib.moe_grouped_gemm2_combine(*args2, FAKE, 1024, None) == WS

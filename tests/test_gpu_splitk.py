@@ -133,3 +133,79 @@ def test_splitk_single_token_all_experts_zero():
     torch.cuda.synchronize()
     assert M.plan_ksplit(cfg, 1, 13) == 8
     assert torch.all(out.float() == 0)
+
+
+# Tail split: more (block, N tile) items than workgroups (one per compute
+# unit, 256 on the MI355X) and not a multiple of them: 40 experts x 8 N tiles
+# at block_m 16 (some experts take two blocks) give ~360 GEMM1 items, one
+# whole round and a leftover round that the tail split cuts into K pieces.
+# K = 1024 (8 K blocks): pieces of 4 K blocks (ksplit -2) in every mode.
+TAIL1 = W.Workload("tail1", T=48, H=1024, I=1024, E=40, top_k=8, mode="fp8", outlier_frac=0.02)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("bm", [16, 32])
+def test_gemm1_tail_split_stage(mode, bm):
+    """GEMM1 with the tail split (whole rounds unsplit, the leftover items in
+    K pieces finished by the second kernel) against the oracle's stages, and
+    moe_forward (which plans it) equal to the stage entry points."""
+    wl = TAIL1.with_(mode=mode)
+    log(f"gemm1 tail split {W.describe(wl)} BM={bm}")
+    cfg, ew, x, lg, (ids, wts, sid, bexp, npp, xq, xs) = _setup(wl, bm)
+    items = int(npp.item()) // bm * (wl.Ip // 128)
+    log(f"  {items} GEMM1 items")
+    assert items > 256 or bm == 32
+    ref, st, tie = _oracle_stages(wl, x, lg)
+    assert M.plan_ksplit(cfg, wl.T, 13) == -2
+    assert M.splitk_bytes(cfg, wl.T, 13, -2) > 0
+    for ks in (1, -2):
+        aq, as_ = M.moe_grouped_gemm1_swiglu(cfg, wl.T, xq, xs, sid, bexp, npp, ew.w13, ew.w13_scale, ksplit=ks)
+        torch.cuda.synchronize()
+        log(f"  ksplit {ks}")
+        check_gemm1_intermediate(wl, aq, as_, sid, npp, st)
+    xd, lgd = x.cuda(), lg.cuda()
+    out1 = M.moe_forward(cfg, xd, lgd, *ew.tiled())
+    out3 = M.moe_grouped_gemm2_combine(cfg, wl.T, aq, as_, sid, bexp, npp, ew.w2, ew.w2_scale, wts)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out3.view(torch.int16))
+    assert_rows_close(bf16_to_f32(out1), ref, mode, "tail forward", allowance=tie)
+
+
+@pytest.mark.parametrize("mode,T", [("fp8", 64), ("fp8_ue8m0", 64), ("mxfp4", 64), ("fp8", 8)])
+def test_gemm1_tail_split_full_size(mode, T):
+    """At the decode shape (T = 64, H = 4096, I = 1024, 288 experts; ~1860
+    GEMM1 items: 7 whole rounds and 72 items left, under half a round), every
+    tail split reproduces the unsplit intermediate: the same codes except at
+    rounding ties of the fp32 sums (a code then moves by one step), scales
+    equal up to that fp32 summation order.  At T = 8 (~460 items: 208 left,
+    over half a round) a tail launch runs every item whole: bit-identical."""
+    wl = W.WORKLOADS["decode_fp8"].with_(mode=mode, T=T)
+    cfg = M.make_cfg(wl.E, wl.top_k, wl.mode, wl.H, wl.I, wl.Hp, wl.Ip, block_m=16, swiglu_limit=wl.swiglu_limit)
+    log(f"gemm1 tail split, full size: {W.describe(wl)}")
+    ew = gpu_weights(M, cfg, wl)
+    x, lg = W.activations(wl, "cuda"), W.router_logits(wl, "cuda")
+    ids, wts, sid, bexp, offs, npp, xq, xs = M.moe_route_permute_quant(cfg, x, lg)
+    aq0, as0 = M.moe_grouped_gemm1_swiglu(cfg, wl.T, xq, xs, sid, bexp, npp, ew.w13, ew.w13_scale, ksplit=1)
+    torch.cuda.synchronize()
+    rows = int(npp.item())
+    rows_total = M.max_blocks(wl.T * wl.top_k, wl.E, 16) * 16
+    log(f"  {rows // 16 * 8} GEMM1 items")
+    for ks in (-2, -4, -8):
+        aq, as_ = M.moe_grouped_gemm1_swiglu(cfg, wl.T, xq, xs, sid, bexp, npp, ew.w13, ew.w13_scale, ksplit=ks)
+        torch.cuda.synchronize()
+        # rows past num_post_padded are not written by either launch
+        a0 = aq0.cpu().numpy().reshape(rows_total, -1)[:rows]
+        a1 = aq.cpu().numpy().reshape(rows_total, -1)[:rows]
+        diff = np.count_nonzero(a0 != a1)
+        log(f"  ksplit {ks}: {diff} of {a0.size} code bytes differ")
+        assert diff <= max(16, a0.size // 100000)
+        s0 = as0.cpu().numpy().reshape(rows_total, -1)[:rows]
+        s1 = as_.cpu().numpy().reshape(rows_total, -1)[:rows]
+        items = rows // 16 * 8
+        if 2 * (items % 256) > 256:
+            assert diff == 0 and np.array_equal(s0, s1)
+        if mode == "fp8":
+            s0, s1 = s0.view(np.float32), s1.view(np.float32)
+            assert np.all(np.abs(s0 - s1) <= 1e-5 * np.abs(s0))
+        else:
+            assert np.count_nonzero(s0 != s1) <= 4
