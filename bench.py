@@ -250,7 +250,8 @@ def main():
         mfma_bound = flops1 / nbytes["gemm1"] > peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
         common = {"traffic": recorded_traffic(wl.name, wl.T, bm),
                   "kernel": ("moe_gemm_stream (GEMM1 + clamped SwiGLU + re-quantisation)" if ks1 == 1 else
-                             f"moe_gemm_stream (GEMM1, K split {ks1}) + swiglu_requant"),
+                             f"moe_gemm_stream (GEMM1, leftover items in {-ks1} K pieces) + gemm1_tail_finish"
+                             if ks1 < 0 else f"moe_gemm_stream (GEMM1, K split {ks1}) + swiglu_requant"),
                   "kernel_us": round(kern[dom], 2), "algorithmic_bytes": nbytes["gemm1"],
                   "algorithmic_flops": flops1}
         if mfma_bound:
