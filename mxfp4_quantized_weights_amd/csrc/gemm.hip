@@ -664,7 +664,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   __shared__ __attribute__((aligned(256))) float wts_lds[G1 ? 1 : NB][BM];
   __shared__ float red[4][BM];
   __shared__ __attribute__((aligned(256))) uint8_t ws_buf[MODE == kGemmMx ? NWS : 1][MODE == kGemmMx ? R::WS_BYTES : 16];
-  auto slot = [&](auto ic) -> uint8_t* {
+  auto slot = [&](auto ic) __attribute__((always_inline)) -> uint8_t* {
     constexpr int i = decltype(ic)::value;
     if constexpr (i == 0) return slot0;
     else if constexpr (i == 1) return slot1;
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   const int nw = gridDim.x / kXcds;
   const int xcd = blockIdx.x % kXcds, jw = blockIdx.x / kXcds;
   const int all_items = (npp / BM) * p.n_tiles;
-  const bool tail = SPLIT && p.tail && tail_split_on(all_items, (int)gridDim.x);
+  const bool tail = SPLIT && BM <= 32 && p.tail && tail_split_on(all_items, (int)gridDim.x);
   const int KSL = SPLIT && (tail || !p.tail) ? p.ks_log2 : 0;  // K pieces per split item: 2^KSL
   int n_whole = 0, wbase = 0, tail_base = 0, list = all_items << KSL;
   if (tail) {
@@ -714,28 +714,30 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   const int KBP = KB >> KSL;  // K blocks of a piece
   const int NG = tiled_n_groups(p.N);  // N tiles of the weight matrix (TILED_V2)
   const int total = n_whole * KB + n_tail * KBP;
-  // item -> (M block, N tile, K piece), K pieces innermost
-  auto item_g = [&](int ii) {
+  // item -> (M block, N tile, K piece), K pieces innermost.  (Every lambda of
+  // this kernel is always_inline: one left as a call makes the kernel keep
+  // its arguments in scratch memory, which cost 4x at one token.)
+  auto item_g = [&](int ii) __attribute__((always_inline)) {
     return ii < n_whole ? wbase + ii * nw : tail_base + ((first + (ii - n_whole) * nw) >> KSL);
   };
-  auto item_m = [&](int ii) { return item_g(ii) / p.n_tiles; };
-  auto item_nt = [&](int ii) { return p.nt0 + item_g(ii) % p.n_tiles; };
-  auto item_ks = [&](int ii) { return ii < n_whole ? 0 : (first + (ii - n_whole) * nw) & ((1 << KSL) - 1); };
-  auto item_kbi = [&](int ii) { return ii < n_whole ? KB : KBP; };
+  auto item_m = [&](int ii) __attribute__((always_inline)) { return item_g(ii) / p.n_tiles; };
+  auto item_nt = [&](int ii) __attribute__((always_inline)) { return p.nt0 + item_g(ii) % p.n_tiles; };
+  auto item_ks = [&](int ii) __attribute__((always_inline)) { return ii < n_whole ? 0 : (first + (ii - n_whole) * nw) & ((1 << KSL) - 1); };
+  auto item_kbi = [&](int ii) __attribute__((always_inline)) { return ii < n_whole ? KB : KBP; };
   // Items of fewer than S K blocks finish inside the prologue (which issues
   // S-1 K blocks without waiting) or within S-1 steps of the next item's
   // metadata loads: their metadata is waited for explicitly.
-  auto short_item = [&](int ii) { return item_kbi(ii) < S; };
+  auto short_item = [&](int ii) __attribute__((always_inline)) { return item_kbi(ii) < S; };
 
   // sorted pair ids of item ii -> ids_lds[ii % NB] (waves 0 .. NI-1), its
   // block's expert -> exp_lds[ii % NB] (lane 0 of the last wave)
-  auto issue_ids = [&](int ii) {
+  auto issue_ids = [&](int ii) __attribute__((always_inline)) {
     if (wave < NI && id_lane)
       dma4(p.sorted_ids + item_m(ii) * BM + wave * 64 + lane, lds_addr(&ids_lds[ii % NB][wave * 64]));
     if (wave == R::NWAVE - 1 && lane == 0) dma4(p.block_expert + item_m(ii), lds_addr(&exp_lds[ii % NB]));
   };
   // GEMM2: routing weight of each row of item ii (its ids must be visible)
-  auto issue_wts = [&](int ii) {
+  auto issue_wts = [&](int ii) __attribute__((always_inline)) {
     if constexpr (!G1) {
       if (wave >= NI && wave < 2 * NI && id_lane) {
         const int r0 = (wave - NI) * 64;
@@ -750,7 +752,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   rs.wk = p.tile_run * R::TILE;
   rs.wsk = p.tile_run * 256;
   int wts_step = -1, wts_item = 0;
-  auto setup_issue = [&](int ii, int s) {
+  auto setup_issue = [&](int ii, int s) __attribute__((always_inline)) {
     const int m = item_m(ii), nt = item_nt(ii);
     const int kb0 = item_ks(ii) * KBP;  // first K block of the item (0 for whole items)
     const int e = __builtin_amdgcn_readfirstlane(exp_lds[ii % NB]);
@@ -823,7 +825,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   }
   int c_nt = 0, c_row0 = 0, c_mv = MT, c_ks = 0, c_kbi = KB, c_g = 0;
   bool active = true;
-  auto setup_compute = [&](int ii) {
+  auto setup_compute = [&](int ii) __attribute__((always_inline)) {
     c_nt = item_nt(ii);
     c_ks = item_ks(ii);
     c_row0 = item_m(ii) * BM;
@@ -849,7 +851,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   // to 4 K blocks that starts at K block kb (kb % 4 == 0) goes to
   // ws_buf[group count % NWS] with the loads of that K block
   int i_ii = 0, i_kb = 0, i_grp = 0, i_kbi = item_kbi(0);
-  auto issue_next = [&](auto slot_c, int s) {
+  auto issue_next = [&](auto slot_c, int s) __attribute__((always_inline)) {
     if (i_ii < n_my) {
       const uint8_t* ws = nullptr;
       if constexpr (MODE == kGemmMx) {
@@ -883,7 +885,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
 
   int c_ii = 0, c_kb = 0, c_grp = 0;  // compute cursor
   const uint8_t* c_ws = ws_buf[0];
-  auto step = [&](auto dc, int s) {
+  auto step = [&](auto dc, int s) __attribute__((always_inline)) {
     constexpr int d = decltype(dc)::value;
     vm_wait_barrier<(S - 2) * R::D>();
     float sw0 = 0.0f, sw1 = 0.0f;
@@ -904,12 +906,17 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
       const int32_t* ids = ids_lds[c_ii % NB];
       if constexpr (G1) {
         if constexpr (SPLIT) {
-          if (!p.tail)
+          // tail launches exist at block_m 16 / 32 only (the host refuses others)
+          if constexpr (BM <= 32) {
+            if (!p.tail)
+              epilogue_gemm1_part<MODE, MT>(p, acc, ids, c_row0, c_ks, c_nt, wt, wn);
+            else if (!tail || c_ii < n_whole)
+              epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
+            else
+              epilogue_gemm1_tail<MT, BM>(p, acc, c_ks, c_g - tail_base, wt, wn);
+          } else {
             epilogue_gemm1_part<MODE, MT>(p, acc, ids, c_row0, c_ks, c_nt, wt, wn);
-          else if (!tail || c_ii < n_whole)
-            epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
-          else
-            epilogue_gemm1_tail<MT, BM>(p, acc, c_ks, c_g - tail_base, wt, wn);
+          }
         } else {
           epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
         }
