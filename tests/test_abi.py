@@ -320,3 +320,34 @@ def test_ksplit_entry_points_validate_before_launch():
     assert lib.moe_grouped_gemm2_combine_splitk(*args2, 2, FAKE, 1024, None) == WS
     assert lib.moe_grouped_gemm2_combine_splitk(*args2[:-1], 100, 2, FAKE, big, None) == SHAPE
     assert lib.moe_grouped_gemm2_combine(*args2, FAKE, 1024, None) == WS
+
+
+def test_no_kernel_uses_scratch_memory(tmp_path):
+    """Every kernel of the built gfx950 code objects keeps its state in
+    registers and LDS: a kernel with private (scratch) memory has lost an
+    inlined helper or spilled, which once made a GEMM launch 4x slower.  Read
+    from the kernels' own metadata in a copy of libmoe.so."""
+    import shutil
+    import subprocess
+    llvm = "/opt/rocm/llvm/bin"
+    objdump, readelf = os.path.join(llvm, "llvm-objdump"), os.path.join(llvm, "llvm-readelf")
+    if not (os.path.exists(objdump) and os.path.exists(readelf)):
+        pytest.skip("LLVM tools of the ROCm install not found")
+    lib = tmp_path / "libmoe.so"
+    shutil.copy(M.LIB_PATH, lib)
+    subprocess.run([objdump, "--offloading", str(lib)], cwd=tmp_path, check=True, capture_output=True)
+    objs = sorted(p for p in tmp_path.iterdir() if "gfx950" in p.name)
+    assert objs, "no gfx950 code object in libmoe.so"
+    kernels = {}
+    for o in objs:
+        notes = subprocess.run([readelf, "--notes", str(o)], check=True, capture_output=True, text=True).stdout
+        name = None
+        for line in notes.splitlines():
+            line = line.strip()
+            if line.startswith(".name:"):
+                name = line.split(":", 1)[1].strip()
+            elif line.startswith(".private_segment_fixed_size:") and name:
+                kernels[name] = int(line.split(":", 1)[1])
+    assert len(kernels) > 50
+    assert any("moe_gemm_stream_kernel" in k for k in kernels)
+    assert {k: v for k, v in kernels.items() if v} == {}
