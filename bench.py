@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=64,
                     help="tokens in the oracle's timed sample (0 = skip; the default covers the whole decode batch)")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--weight-copies", type=int, default=1,
+                    help="rotate over this many copies of the weights, one per step, so that no "
+                         "step finds the previous step's weights in the memory-side cache")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 device-to-device copies of MIB MiB (calibrates HBM byte counters) and exit")
     return ap.parse_args()
@@ -170,18 +173,21 @@ def main():
     lg = W.router_logits(wl, "cuda")
     out = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(M.workspace_bytes(cfg, wl.T), dtype=torch.uint8, device=dev)
-    w13, s13, w2, s2 = ew.tiled()
+    copies = [tuple(ew.tiled())]
+    for _ in range(1, max(1, args.weight_copies)):
+        copies.append(tuple(t.clone() for t in copies[0]))
     stream = torch.cuda.current_stream()
 
-    def step():
+    def step(i):
+        w13, s13, w2, s2 = copies[i % len(copies)]
         M.moe_forward(cfg, x, lg, w13, s13, w2, s2, out=out, ws=ws, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = wall * 1e3 / args.steps
@@ -217,7 +223,8 @@ def main():
         part_b = M.splitk_bytes(cfg, wl.T, 13, ks1)
         part = torch.empty(max(part_b, 1), dtype=torch.uint8, device=dev)
 
-        def staged(evs):
+        def staged(evs, i):
+            w13, s13, w2, s2 = copies[i % len(copies)]
             evs[0].record(stream)
             lib.moe_route_permute_quant(cfgp, wl.T, lg.data_ptr(), x.data_ptr(), wl.H, ids.data_ptr(),
                                         wts.data_ptr(), sid.data_ptr(), bexp.data_ptr(), offs.data_ptr(),
@@ -233,13 +240,19 @@ def main():
             evs[3].record(stream)
 
         for i in range(min(args.warmup, args.steps)):
-            staged(ev[i])
+            staged(ev[i], i)
         torch.cuda.synchronize()
         for i in range(args.steps):
-            staged(ev[i])
+            staged(ev[i], i)
         torch.cuda.synchronize()
         for j, n in enumerate(names):
             kern[n] = float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)])) * 1e3  # us
+        # spread over the steps: the whole staged step and GEMM1, from the same events
+        tot = np.array([ev[i][0].elapsed_time(ev[i][len(names)]) for i in range(args.steps)]) * 1e3
+        g1 = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]) * 1e3
+        spread = {n: {"p10": round(float(np.percentile(a, 10)), 2), "median": round(float(np.median(a)), 2),
+                      "p90": round(float(np.percentile(a, 90)), 2)}
+                  for n, a in (("step", tot), ("gemm1_swiglu", g1))}
 
     tokens_per_s = wl.T / (ms * 1e-3)
     flops = wl.flops()
@@ -289,6 +302,8 @@ def main():
         "active_experts": nbytes["active_experts"],
         "layer_algorithmic_bytes": nbytes["layer"],
         "kernels_us": {k: round(v, 2) for k, v in kern.items()},
+        "events_us": spread if kern else None,
+        "weight_copies": len(copies),
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -46,7 +46,7 @@ def _weights(cfg, wl):
     return _CACHE[key]
 
 
-@pytest.mark.parametrize("name", ["decode_fp8", "prefill_fp8", "skewed_padded_fp8", "prefill_mxfp4", "tp4_decode_fp8",
+@pytest.mark.parametrize("name", ["decode_fp8", "prefill_fp8", "prefill_fp8_16k", "skewed_padded_fp8", "prefill_mxfp4", "tp4_decode_fp8",
                                   "tp8_prefill_fp8", "tp4_prefill_mxfp4", "shared_expert_fp8", "shared_expert_mxfp4",
                                   "decode_fp8_ue8m0", "prefill_fp8_ue8m0"])
 def test_fullsize_sampled(name):

@@ -78,6 +78,10 @@ WORKLOADS = {
     # prefill-shaped block-FP8 layer with activation outliers
     "prefill_fp8": Workload("prefill_fp8", T=4096, H=4096, I=1024, E=288, top_k=8, mode="fp8",
                             outlier_frac=0.01),
+    # the same layer at a long prefill (16384 tokens, ~455 per expert): enough
+    # tokens per expert weight byte that the MFMA, not HBM, is the bound
+    "prefill_fp8_16k": Workload("prefill_fp8_16k", T=16384, H=4096, I=1024, E=288, top_k=8, mode="fp8",
+                                outlier_frac=0.01),
     # MXFP4 w4a4 layer
     "prefill_mxfp4": Workload("prefill_mxfp4", T=4096, H=4096, I=1024, E=288, top_k=8,
                               mode="mxfp4"),
