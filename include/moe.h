@@ -194,9 +194,10 @@ moe_status_t moe_quant_act(const void* in, int32_t in_dtype, int32_t rows, int32
  * routing, the padded permutation and the quantisation of x, with exactly
  * the results of moe_route_topk + moe_permute_align + moe_quant_act (x bf16,
  * hidden = cfg->pad.hidden valid columns, row stride ld_x, quantised to
- * cfg->pad.hidden_padded columns in cfg->quant_mode).  Up to 64 tokens it
- * is two launches: routing and quantisation side by side, then a
- * one-workgroup permutation.  Outputs as the three entry points (sizes from
+ * cfg->pad.hidden_padded columns in cfg->quant_mode).  Up to 16 tokens it
+ * is one launch (one workgroup routes and permutes while the others
+ * quantise); larger batches take two (routing and quantisation side by side,
+ * then the permutation).  Outputs as the three entry points (sizes from
  * moe_max_blocks, moe_quant_act); all are device buffers of the caller. */
 moe_status_t moe_route_permute_quant(const moe_cfg_t* cfg, int32_t T, const float* router_logits,
                                      const void* x_bf16, int64_t ld_x, int32_t* ids, float* weights,

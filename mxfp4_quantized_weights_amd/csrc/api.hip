@@ -236,9 +236,9 @@ moe::GemmArgs gemm2_args(const moe_cfg_t* c, int32_t T, const void* aq, const vo
   return a;
 }
 
-// Routing, permutation and quantisation of x in two launches: routing and
-// quantisation together, then the permutation (a one-workgroup bitmap
-// version for decode-sized batches).
+// Routing, permutation and quantisation of x: one launch up to 16 tokens
+// (one workgroup routes and permutes, the others quantise), else two
+// (routing and quantisation together, then the permutation).
 hipError_t front_end(const moe_cfg_t* c, int32_t T, const float* logits, const void* x, int64_t ld_x, int32_t* ids,
                      float* wts, int32_t* sorted, int32_t* bexp, int32_t* offs, int32_t* npp, void* xq, void* xs,
                      hipStream_t s) {

@@ -30,8 +30,8 @@ hipError_t launch_permute_align(const int32_t* ids, int T, int k, int E, int blo
 hipError_t launch_route_and_quant(const float* logits, int T, int E, int k, int32_t* ids, float* w, const void* x_bf16,
                                   int H, int64_t ld_x, int Hp, int mode, void* xq, void* xs, hipStream_t s);
 
-// Routing, permutation and quantisation of bf16 x in two launches, for
-// batches where front_small_ok(T, E, k) holds (same results as the three
+// Routing, permutation and quantisation of bf16 x in one launch (T <= 16)
+// or two, for batches where front_small_ok(T, E, k) holds (same results as the three
 // stage launchers for routing output, which never repeats an expert).
 bool front_small_ok(int T, int E, int k);
 hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t* ids, float* w, int block_m, int nb,

@@ -382,19 +382,26 @@ hipError_t launch_permute_align(const int32_t* ids, int T, int k, int E, int blo
 }
 
 // ---------------------------------------------------------------------------
-// Front end in two launches instead of three.
+// Front end in fewer launches than three.
 //   route_quant_kernel (any batch): workgroups 0 .. nr-1 route 4 tokens each
 //             (one wave per token, route_token), the others quantise the
 //             rows of x; the two parts share no data.  Larger batches then
-//             run permute_align_kernel, small ones (T <= 64):
-//   permute_small_kernel: one workgroup.  Routing never gives a token the
-//             same expert twice, so one 64-bit LDS word per expert marks the
-//             tokens that chose it (T <= 64); a pair's stable rank in its
-//             expert's segment is the number of marked tokens below its own,
-//             and the expert's count the number of marks.  A block scan of
-//             the padded counts gives the offsets; each expert's thread
-//             writes its padding sentinels and block ids, then every pair
-//             its sorted position (the layout of permute_align_kernel).
+//             run permute_align_kernel.
+//   front_small_kernel (T <= 16, one launch): workgroup 0 (16 waves) routes
+//             every token, keeping the ids in LDS as well, then builds the
+//             permutation from them (permute_small); the other workgroups
+//             quantise the rows of x.  Routing runs on one CU here, one token
+//             per wave; with more tokens per wave it takes longer than the
+//             second launch saves, so 17 .. 64 tokens run route_quant_kernel
+//             and then permute_small_kernel.
+//   permute_small: routing never gives a token the same expert twice, so one
+//             64-bit LDS word per expert marks the tokens that chose it
+//             (T <= 64); a pair's stable rank in its expert's segment is the
+//             number of marked tokens below its own, and the expert's count
+//             the number of marks.  A block scan of the padded counts gives
+//             the offsets; each expert's thread writes its padding sentinels
+//             and block ids, then every pair its sorted position (the layout
+//             of permute_align_kernel).
 // ---------------------------------------------------------------------------
 constexpr int kSmallT = 64;
 
@@ -416,11 +423,11 @@ __global__ __launch_bounds__(256) void route_quant_kernel(const float* __restric
     quant_rows_body<true, false, MODE>(x, T, H, ld_x, Hp, xq, xs, gw, nw);
 }
 
-__global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                             int BM, int nb, int32_t* __restrict__ sorted_ids,
-                                                             int32_t* __restrict__ block_expert,
-                                                             int32_t* __restrict__ offsets,
-                                                             int32_t* __restrict__ npp) {
+// The permutation of T <= 64 tokens' pairs by one 1024-thread workgroup;
+// ids may point to LDS (visible to the whole workgroup on entry).
+__device__ __forceinline__ void permute_small(const int32_t* ids, int T, int k, int E, int BM, int nb,
+                                              int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+                                              int32_t* __restrict__ offsets, int32_t* __restrict__ npp) {
   constexpr int NW = 16;
   __shared__ uint64_t sel[1024];     // tokens that chose expert e
   __shared__ int32_t seg[1024];      // segment offset of expert e
@@ -460,6 +467,40 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __re
   }
 }
 
+__global__ __launch_bounds__(1024) void permute_small_kernel(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                             int BM, int nb, int32_t* __restrict__ sorted_ids,
+                                                             int32_t* __restrict__ block_expert,
+                                                             int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ npp) {
+  permute_small(ids, T, k, E, BM, nb, sorted_ids, block_expert, offsets, npp);
+}
+
+constexpr int kOneLaunchT = 16;
+
+template <int VPL, int MODE>
+__global__ __launch_bounds__(1024) void front_small_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                           int32_t* __restrict__ ids, float* __restrict__ w, int BM,
+                                                           int nb, int32_t* __restrict__ sorted_ids,
+                                                           int32_t* __restrict__ block_expert,
+                                                           int32_t* __restrict__ offsets, int32_t* __restrict__ npp,
+                                                           const void* __restrict__ x, int H, int64_t ld_x, int Hp,
+                                                           uint8_t* __restrict__ xq, void* __restrict__ xs, int vec) {
+  const int wave = threadIdx.x >> 6;
+  if (blockIdx.x == 0) {
+    __shared__ int32_t ids_lds[kOneLaunchT * kMaxTopK];
+    for (int t = wave; t < T; t += 16)
+      route_token<VPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, ids_lds + t * k);
+    __syncthreads();
+    permute_small(ids_lds, T, k, E, BM, nb, sorted_ids, block_expert, offsets, npp);
+    return;
+  }
+  const int64_t gw = (int64_t)(blockIdx.x - 1) * 16 + wave, nw = (int64_t)(gridDim.x - 1) * 16;
+  if (vec)
+    quant_rows_body<true, true, MODE>(x, T, H, ld_x, Hp, xq, xs, gw, nw);
+  else
+    quant_rows_body<true, false, MODE>(x, T, H, ld_x, Hp, xq, xs, gw, nw);
+}
+
 template <int VPL>
 static void launch_route_quant(int mode, dim3 grid, int nr, hipStream_t s, const float* logits, int T, int E, int k,
                                int32_t* ids, float* w, const void* x, int H, int64_t ld_x, int Hp, void* xq,
@@ -496,14 +537,49 @@ hipError_t launch_route_and_quant(const float* logits, int T, int E, int k, int3
   return hipGetLastError();
 }
 
+template <int VPL>
+static void launch_front_small_vpl(int mode, dim3 grid, hipStream_t s, const float* logits, int T, int E, int k,
+                                   int32_t* ids, float* w, int BM, int nb, int32_t* sorted_ids,
+                                   int32_t* block_expert, int32_t* offsets, int32_t* npp, const void* x, int H,
+                                   int64_t ld_x, int Hp, void* xq, void* xs, int vec) {
+  uint8_t* q = (uint8_t*)xq;
+  if (mode == kQuantFp8)
+    hipLaunchKernelGGL((front_small_kernel<VPL, kQuantFp8>), grid, dim3(1024), 0, s, logits, T, E, k, ids, w, BM, nb,
+                       sorted_ids, block_expert, offsets, npp, x, H, ld_x, Hp, q, xs, vec);
+  else if (mode == kQuantFp8E8)
+    hipLaunchKernelGGL((front_small_kernel<VPL, kQuantFp8E8>), grid, dim3(1024), 0, s, logits, T, E, k, ids, w, BM,
+                       nb, sorted_ids, block_expert, offsets, npp, x, H, ld_x, Hp, q, xs, vec);
+  else
+    hipLaunchKernelGGL((front_small_kernel<VPL, kQuantMx>), grid, dim3(1024), 0, s, logits, T, E, k, ids, w, BM, nb,
+                       sorted_ids, block_expert, offsets, npp, x, H, ld_x, Hp, q, xs, vec);
+}
+
 hipError_t launch_front_small(const float* logits, int T, int E, int k, int32_t* ids, float* w, int block_m, int nb,
                               int32_t* sorted_ids, int32_t* block_expert, int32_t* offsets, int32_t* npp,
                               const void* x_bf16, int H, int64_t ld_x, int Hp, int mode, void* xq, void* xs,
                               hipStream_t s) {
-  hipError_t e = launch_route_and_quant(logits, T, E, k, ids, w, x_bf16, H, ld_x, Hp, mode, xq, xs, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, s, ids, T, k, E, block_m, nb, sorted_ids,
-                     block_expert, offsets, npp);
+  if (T > kOneLaunchT) {
+    hipError_t e = launch_route_and_quant(logits, T, E, k, ids, w, x_bf16, H, ld_x, Hp, mode, xq, xs, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, s, ids, T, k, E, block_m, nb, sorted_ids,
+                       block_expert, offsets, npp);
+    return hipGetLastError();
+  }
+  // workgroup 0 routes and permutes; 1 + ceil(units / 64) workgroups in all
+  // (16 waves of 4 quantisation units each)
+  const int64_t units = (int64_t)T * (Hp / 128);
+  const dim3 grid((unsigned)(1 + (units + 63) / 64));
+  const int vec = ((uintptr_t)x_bf16 % 16 == 0) && ((ld_x * 2) % 16 == 0);
+  const int vpl = (E + 63) / 64;
+  if (vpl <= 1)
+    launch_front_small_vpl<1>(mode, grid, s, logits, T, E, k, ids, w, block_m, nb, sorted_ids, block_expert, offsets,
+                              npp, x_bf16, H, ld_x, Hp, xq, xs, vec);
+  else if (vpl <= 5)
+    launch_front_small_vpl<5>(mode, grid, s, logits, T, E, k, ids, w, block_m, nb, sorted_ids, block_expert, offsets,
+                              npp, x_bf16, H, ld_x, Hp, xq, xs, vec);
+  else
+    launch_front_small_vpl<16>(mode, grid, s, logits, T, E, k, ids, w, block_m, nb, sorted_ids, block_expert,
+                               offsets, npp, x_bf16, H, ld_x, Hp, xq, xs, vec);
   return hipGetLastError();
 }
 

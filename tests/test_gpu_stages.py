@@ -297,9 +297,10 @@ def test_gemm1_swiglu_stage(mode, BM):
 @pytest.mark.parametrize("T,E,k,BM,mode,ldpad", [(1, 288, 8, 16, "fp8", 0), (7, 288, 8, 16, "mxfp4", 24),
                                                  (64, 288, 8, 16, "fp8_ue8m0", 0), (64, 1024, 16, 32, "fp8", 8),
                                                  (33, 8, 2, 64, "mxfp4", 0), (64, 1, 1, 128, "fp8", 0),
-                                                 (65, 288, 8, 16, "fp8", 0), (300, 64, 4, 32, "mxfp4", 0)])
+                                                 (65, 288, 8, 16, "fp8", 0), (300, 64, 4, 32, "mxfp4", 0),
+                                                 (16, 1024, 16, 16, "fp8", 0), (17, 288, 8, 16, "fp8_ue8m0", 8)])
 def test_route_permute_quant_equals_stages(T, E, k, BM, mode, ldpad):
-    """moe_route_permute_quant (two launches up to 64 tokens) gives exactly the
+    """moe_route_permute_quant (one launch up to 16 tokens, else two) gives exactly the
     results of moe_route_topk + moe_permute_align + moe_quant_act, and those
     match the oracle."""
     log(f"route_permute_quant T={T} E={E} k={k} BM={BM} mode={mode} ldpad={ldpad}")
