@@ -158,6 +158,20 @@ __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// The same with at most min(later, R) * D loads left outstanding: the wait
+// for a ring slot after which only `later` (wave-uniform) slots were issued.
+template <int R, int D>
+__device__ __forceinline__ void vm_wait_barrier_upto(int later) {
+  if constexpr (R == 0) {
+    vm_wait_barrier<0>();
+  } else {
+    if (later >= R)
+      vm_wait_barrier<R * D>();
+    else
+      vm_wait_barrier_upto<R - 1, D>(later);
+  }
+}
+
 
 // Per-lane source addresses of one wave's loads at K block 0.
 template <int MODE, int BM>
@@ -865,9 +879,9 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
           setup_issue(i_ii, s);
         }
       }
-    } else {
-      ring_issue<MODE, BM>(rs, slot(slot_c), wave, i_kbi - 1, nullptr);  // past the end: reload, never read
     }
+    // past the end of the stream nothing is issued: the waits of the last
+    // S-2 steps count only the slots that exist
   };
 
   // prologue: metadata of item 0, then K blocks 0 .. S-2 of the stream
@@ -887,7 +901,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
   const uint8_t* c_ws = ws_buf[0];
   auto step = [&](auto dc, int s) __attribute__((always_inline)) {
     constexpr int d = decltype(dc)::value;
-    vm_wait_barrier<(S - 2) * R::D>();
+    vm_wait_barrier_upto<S - 2, R::D>(total - 1 - s);  // slots issued after this one: up to S-2
     float sw0 = 0.0f, sw1 = 0.0f;
     if constexpr (MODE != kGemmMx) {
       // GEMM1: gate and up scale; GEMM2: the scale of the wave's 128-row block
