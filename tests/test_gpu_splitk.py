@@ -171,6 +171,25 @@ def test_gemm1_tail_split_stage(mode, bm):
     assert_rows_close(bf16_to_f32(out1), ref, mode, "tail forward", allowance=tie)
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_gemm1_tail_split_few_items(mode):
+    """A tail launch with fewer items than half a round (ksplit -2 asked of
+    the stage entry point): no whole round, every item is cut into pieces,
+    and the intermediate matches the oracle's as the unsplit launch does."""
+    wl = TAIL1.with_(mode=mode, T=6, E=8, top_k=2)
+    log(f"gemm1 tail split, few items {W.describe(wl)}")
+    cfg, ew, x, lg, (ids, wts, sid, bexp, npp, xq, xs) = _setup(wl, 16)
+    items = int(npp.item()) // 16 * (wl.Ip // 128)
+    log(f"  {items} GEMM1 items")
+    assert items <= 128
+    ref, st, tie = _oracle_stages(wl, x, lg)
+    for ks in (1, -2):
+        aq, as_ = M.moe_grouped_gemm1_swiglu(cfg, wl.T, xq, xs, sid, bexp, npp, ew.w13, ew.w13_scale, ksplit=ks)
+        torch.cuda.synchronize()
+        log(f"  ksplit {ks}")
+        check_gemm1_intermediate(wl, aq, as_, sid, npp, st)
+
+
 @pytest.mark.parametrize("mode,T", [("fp8", 64), ("fp8_ue8m0", 64), ("mxfp4", 64), ("fp8", 8)])
 def test_gemm1_tail_split_full_size(mode, T):
     """At the decode shape (T = 64, H = 4096, I = 1024, 288 experts; ~1860
