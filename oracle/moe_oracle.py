@@ -575,8 +575,9 @@ def moe_forward(x: np.ndarray, logits: np.ndarray, W: QuantWeights, top_k: int,
        accumulated in fp32; first H columns.
 
     With ``return_stages`` it also returns the routing, the quantised input,
-    per (sample token, slot) pair the SwiGLU output ``a`` (fp32, before
-    re-quantisation) and its codes/scales ``aq``, and the per-pair ``y``.
+    per (sample token, slot) pair the GEMM1 output ``h`` (fp32, gate columns
+    then up columns), the SwiGLU output ``a`` (fp32, before re-quantisation)
+    and its codes/scales ``aq``, and the per-pair ``y``.
     """
     mode = W.mode
     x = np.asarray(x, F32)
@@ -591,6 +592,7 @@ def moe_forward(x: np.ndarray, logits: np.ndarray, W: QuantWeights, top_k: int,
     y = np.zeros((n, top_k, Hp), F32)
     aq_all = {}
     a_all = {}
+    h_all = {}
     for e in np.unique(ids):
         w13d, w2d = dequant_expert(W, int(e))
         rows = np.argwhere(ids == e)  # (token index in sample, slot) pairs, increasing f
@@ -604,17 +606,12 @@ def moe_forward(x: np.ndarray, logits: np.ndarray, W: QuantWeights, top_k: int,
             if return_stages:
                 aq_all[(int(t), int(j))] = (aq[i], as_[i])
                 a_all[(int(t), int(j))] = a[i]
+                h_all[(int(t), int(j))] = h[i]
     out = np.zeros((n, Hp), F32)
     for j in range(top_k):
         out = (out + (wts[:, j:j + 1] * y[:, j]).astype(F32)).astype(F32)
     out = out[:, :hidden]
     if return_stages:
-        return out, dict(ids=ids, weights=wts, xq=xq, xs=xs, y=y, aq=aq_all, a=a_all)
+        return out, dict(ids=ids, weights=wts, xq=xq, xs=xs, y=y, aq=aq_all, a=a_all, h=h_all)
     return out
 
-
-def bf16_round(v: np.ndarray) -> np.ndarray:
-    """float32 -> nearest bfloat16 (ties to even), returned as float32."""
-    u = np.asarray(v, F32).view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return r.astype(np.uint32).view(F32)

@@ -26,3 +26,16 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter):
+    # the per-output parity lines collected by parity_util (GEMM1 intermediate
+    # flips and the share of the tolerance their allowance took)
+    try:
+        from parity_util import SUMMARY
+    except Exception:  # pragma: no cover
+        return
+    if SUMMARY:
+        terminalreporter.section("parity summary")
+        for line in SUMMARY:
+            terminalreporter.write_line(line)

@@ -1,12 +1,18 @@
 """Full-size workloads on the GPU, in the launch configuration the benchmark
-uses (block_m from pick_block_m, all experts resident), checked against the
-oracle on sampled tokens (the layer is row-independent, so the oracle
-computes only those rows, with only the experts they route to).
+uses (block_m from pick_block_m, all experts resident, the splits moe_forward
+plans), checked against the oracle.
 
-Bit-exact over the whole workload: routing ids and the permutation.  Bit-exact
-on the sampled experts: the quantised weight bytes and scales.  Tolerance on
-the sampled output rows: 2e-2 (block FP8) / 6e-2 (MXFP4) times the row RMS,
-after the re-quantisation tie allowance (see parity_util).
+Bit-exact over the whole batch: routing ids, the permutation, and the
+quantised activations (codes and scales) that the front end of moe_forward
+writes.  Bit-exact on the sampled experts: the quantised weight bytes and
+scales.  moe_forward equals the stage entry points bit for bit.  On a sample
+of tokens spread over the batch (first, last, evenly strided; 64 for the
+decode, prefill, MXFP4 and skewed workloads): GEMM1's re-quantised
+intermediate passes the verified-tie check, and the output rows are within
+2e-2 (block FP8) / 6e-2 (MXFP4) of the row RMS after adding only the effect
+of the intermediate codes that differed (see parity_util).  The layer is
+row-independent, so the oracle computes only the sampled rows, with only the
+experts they route to.
 """
 import gc
 
@@ -16,13 +22,16 @@ import torch
 
 import oracle as O
 import workloads as W
-from parity_util import (assert_rows_close, bf16_to_f32, gpu_weights, log, oracle_weights_subset,
-                         requant_tie_allowance)
+from parity_util import (bf16_to_f32, check_intermediate_and_output, gpu_stage_chain, gpu_weights, log,
+                         oracle_stages, oracle_weights_subset)
 
 pytestmark = pytest.mark.gpu
 
 M = None
 _CACHE = {}
+
+# tokens sampled per workload (the rest: 16)
+SAMPLE = {"decode_fp8": 64, "prefill_fp8": 64, "prefill_mxfp4": 64, "skewed_padded_fp8": 64}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -46,9 +55,14 @@ def _weights(cfg, wl):
     return _CACHE[key]
 
 
-@pytest.mark.parametrize("name", ["decode_fp8", "prefill_fp8", "prefill_fp8_16k", "skewed_padded_fp8", "prefill_mxfp4", "tp4_decode_fp8",
-                                  "tp8_prefill_fp8", "tp4_prefill_mxfp4", "shared_expert_fp8", "shared_expert_mxfp4",
-                                  "decode_fp8_ue8m0", "prefill_fp8_ue8m0"])
+def sample_tokens(T: int, n: int):
+    """n tokens spread over [0, T): the first, the last and evenly strided."""
+    return sorted(set(np.linspace(0, T - 1, min(n, T)).round().astype(int).tolist()))
+
+
+@pytest.mark.parametrize("name", ["decode_fp8", "prefill_fp8", "prefill_fp8_16k", "skewed_padded_fp8", "prefill_mxfp4",
+                                  "tp4_decode_fp8", "tp8_prefill_fp8", "tp4_prefill_mxfp4", "shared_expert_fp8",
+                                  "shared_expert_mxfp4", "decode_fp8_ue8m0", "prefill_fp8_ue8m0"])
 def test_fullsize_sampled(name):
     wl = W.WORKLOADS[name]
     bm = M.pick_block_m(wl.T, wl.E, wl.top_k)
@@ -58,29 +72,37 @@ def test_fullsize_sampled(name):
     x = W.activations(wl, "cuda")
     lg = W.router_logits(wl, "cuda")
     out = M.moe_forward(cfg, x, lg, *ew.tiled())
-    ids, wts = M.moe_route_topk(lg, wl.top_k)
-    sid, bexp, offs, npp = M.moe_permute_align(ids, wl.E, bm)
+    ch = gpu_stage_chain(M, cfg, wl.T, x, lg, ew)
     torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ch["out"].view(torch.int16)), "moe_forward differs from the stages"
+
+    # whole batch, bit-exact: routing, permutation, quantised x
     lg_h = lg.cpu().numpy()
     ido, wo = O.route_topk(lg_h, wl.top_k)
-    assert np.array_equal(ids.cpu().numpy(), ido)
-    assert np.allclose(wts.cpu().numpy(), wo, rtol=2e-6, atol=0)
+    assert np.array_equal(ch["ids"].cpu().numpy(), ido)
+    assert np.allclose(ch["w"].cpu().numpy(), wo, rtol=2e-6, atol=0)
     so, bo, oo, no = O.permute_align(ido, wl.E, bm)
-    assert np.array_equal(sid.cpu().numpy(), so) and np.array_equal(bexp.cpu().numpy(), bo)
+    assert np.array_equal(ch["sid"].cpu().numpy(), so) and np.array_equal(ch["bexp"].cpu().numpy(), bo)
+    assert int(ch["npp"].item()) == no
+    xq_o, xs_o = O.quant_act(wl.mode, O.pad_cols(x.float().cpu().numpy(), wl.Hp))
+    assert np.array_equal(ch["xq"].cpu().numpy(), xq_o), "quantised x codes differ"
+    xs_g = ch["xs"].cpu().numpy()
+    if wl.mode == "fp8_ue8m0":
+        xs_g = xs_g[:, :wl.Hp // 128]
+    assert np.array_equal(xs_g.view(np.uint8), np.ascontiguousarray(xs_o).view(np.uint8)), "quantised x scales differ"
     active = int(np.count_nonzero(np.bincount(ido.reshape(-1), minlength=wl.E)))
-    log(f"  routing/permutation bit-exact; active experts {active}; num_post_padded {no}")
+    log(f"  routing, permutation and the {wl.T}x{wl.Hp} quantised x bit-exact; active experts {active}; "
+        f"num_post_padded {no}")
 
-    rng = np.random.default_rng(5)
-    toks = sorted({0, wl.T - 1, int(rng.integers(1, wl.T - 1))})
+    toks = sample_tokens(wl.T, SAMPLE.get(name, 16))
     experts = np.unique(ido[toks])
-    log(f"  oracle on tokens {toks} ({len(experts)} experts)")
+    log(f"  oracle on {len(toks)} tokens ({len(experts)} experts)")
     Q = oracle_weights_subset(wl, experts, "cuda")
-    for e in experts[:3]:
+    for e in experts[:: max(1, len(experts) // 4)]:
         assert np.array_equal(ew.q13[e].cpu().numpy(), Q.w13[e])
         assert np.array_equal(ew.q2[e].cpu().numpy(), Q.w2[e])
         assert np.array_equal(ew.s13[e].cpu().numpy().view(np.uint8), Q.s13[e].view(np.uint8))
         assert np.array_equal(ew.s2[e].cpu().numpy().view(np.uint8), Q.s2[e].view(np.uint8))
-    ref, st = O.moe_forward(x.float().cpu().numpy(), lg_h, Q, wl.top_k, wl.swiglu_limit, wl.H, wl.I, tokens=toks,
-                            return_stages=True)
-    tie = requant_tie_allowance(st, Q, wl.mode, wl.H)
-    assert_rows_close(bf16_to_f32(out)[toks], ref, wl.mode, name, allowance=tie)
+    ref, st = oracle_stages(wl, x, lg, Q, tokens=toks)
+    check_intermediate_and_output(wl, bf16_to_f32(out)[toks], ch["aq"], ch["as_"], ch["sid"], ch["npp"], ref, st, Q,
+                                  tokens=toks, what=name)
