@@ -6,11 +6,18 @@ re-quantisation, GEMM2 + weighted combine.  Inputs (router logits, bf16
 activations, quantised + preshuffled weights of all experts) are resident in
 HBM before the timed region starts.
 
+The default workload is the prefill layer: T = 4096 tokens, H = 4096,
+I = 1024, 288 experts, top-8, block FP8 (e4m3 weights with 128x128 scales,
+dynamic 1x128 activations), 1% of x scaled by 30 -- the largest
+configuration of the benchmark that fits one GPU.
+
 Prints one JSON line with tokens/s (whole job), effective TFLOP/s
 (6*T*k*H*I per step on the real sizes), the roofline of the dominant kernel
 (its average duration from HIP events recorded on the launch stream around
-the same kernels, called through the stage entry points) and the CPU
-oracle's throughput on a bounded sample of the same workload.
+the same kernels, called through the stage entry points) with the attainable
+ceiling min(peak, intensity x HBM bandwidth), the CPU oracle's throughput on
+a bounded sample of the same workload, and (unless --no-extras) the decode
+(T = 64) and MXFP4 (T = 4096) layers measured the same way, as extra keys.
 """
 from __future__ import annotations
 
@@ -32,11 +39,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode_fp8")
+    ap.add_argument("--workload", default="prefill_fp8")
     ap.add_argument("--T", type=int, default=0, help="override the token count")
     ap.add_argument("--block-m", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=64,
-                    help="tokens in the oracle's timed sample (0 = skip; the default covers the whole decode batch)")
+    ap.add_argument("--cpu-sample", type=int, default=-1,
+                    help="tokens in the oracle's timed sample (0 = skip; default -1: the whole batch)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the extra decode and MXFP4 measurements")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--weight-copies", type=int, default=1,
                     help="rotate over this many copies of the weights, one per step, so that no "
@@ -82,7 +91,7 @@ def algorithmic_bytes(wl, ids, M):
         aq = P * (Ip // 2 + Ip // 32)
     layer = active * (w13 + w2) + wl.T * wl.H * 2 + wl.T * wl.E * 4 + wl.T * wl.H * 2
     gemm1 = active * w13 + xq + aq
-    gemm2 = active * w2 + aq + P * Hp * 4
+    gemm2 = active * w2 + aq + wl.T * wl.H * 2 + P * 4   # + the output and the routing weights
     return dict(active_experts=active, layer=layer, gemm1=gemm1, gemm2=gemm2,
                 w13_per_expert=w13, w2_per_expert=w2)
 
@@ -109,15 +118,16 @@ def recorded_traffic(workload: str, T: int, block_m: int):
 
 def cpu_baseline(wl, x, lg, sample_tokens: int):
     """The oracle, as it stands, on the first `sample_tokens` tokens of the
-    same workload: timed from bf16 activations + quantised weights to the fp32
-    output (routing, activation quantisation, dequantisation, GEMMs, SwiGLU,
-    re-quantisation, combine).  Weight quantisation is done beforehand and
-    not timed."""
+    same workload (all of them when `sample_tokens` < 0): timed from bf16
+    activations + quantised weights to the fp32 output (routing, activation
+    quantisation, dequantisation, GEMMs, SwiGLU, re-quantisation, combine).
+    Weight quantisation is done beforehand and not timed."""
     import numpy as np
     import oracle as O
     from threadpoolctl import threadpool_info
     from oracle.from_workload import quantize_experts
-    toks = list(range(min(sample_tokens, wl.T)))
+    n = wl.T if sample_tokens < 0 else min(sample_tokens, wl.T)
+    toks = list(range(n))
     lg_h = lg.cpu().numpy()
     x_h = x.float().cpu().numpy()
     ids, _ = O.route_topk(lg_h[toks], wl.top_k)
@@ -138,72 +148,70 @@ def cpu_baseline(wl, x, lg, sample_tokens: int):
                       f"host affinity {len(os.sched_getaffinity(0))} cpus"}
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
-              "sharding is described, not built", file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
+def build_weights(M, cfg, wl, dev, copies: int):
+    """Quantised + preshuffled weights of every expert (drawn on the GPU,
+    quantised and preshuffled by the library); only the tiled copies stay."""
     import torch
     import workloads as W
-    import mxfp4_quantized_weights_amd as M
-
-    wl = W.WORKLOADS[args.workload]
-    if args.T:
-        wl = wl.with_(T=args.T)
-    bm = args.block_m or M.pick_block_m(wl.T, wl.E, wl.top_k)
-    cfg = M.make_cfg(wl.E, wl.top_k, wl.mode, wl.H, wl.I, wl.Hp, wl.Ip, block_m=bm,
-                     swiglu_limit=wl.swiglu_limit)
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-
-    # weights: drawn on the GPU, quantised and preshuffled by the library
     ew = M.ExpertWeights(cfg, dev)
     for e0 in range(0, wl.E, 16):
         ex = range(e0, min(wl.E, e0 + 16))
         ew.add_experts(e0, W.all_w13(wl, ex, "cuda"), W.all_w2(wl, ex, "cuda"))
     ew.finalize()
-    ew.q13 = ew.s13 = ew.q2 = ew.s2 = None      # only the tiled copies stay resident
+    ew.q13 = ew.s13 = ew.q2 = ew.s2 = None
     torch.cuda.empty_cache()
+    out = [tuple(ew.tiled())]
+    for _ in range(1, max(1, copies)):
+        out.append(tuple(t.clone() for t in out[0]))
+    return out
+
+
+def measure(M, wl, args, copies=None, steps=None, warmup=None, breakdown=True, block_m=None):
+    """Times `steps` moe_forward steps of workload `wl` (after `warmup`
+    untimed ones), then the same kernels through the stage entry points with
+    HIP events on the launch stream.  Returns (result dict, weight copies,
+    x, logits)."""
+    import numpy as np
+    import torch
+    import workloads as W
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    bm = (args.block_m if block_m is None else block_m) or M.pick_block_m(wl.T, wl.E, wl.top_k)
+    cfg = M.make_cfg(wl.E, wl.top_k, wl.mode, wl.H, wl.I, wl.Hp, wl.Ip, block_m=bm,
+                     swiglu_limit=wl.swiglu_limit)
+    dev = torch.device("cuda", 0)
+    if copies is None:
+        copies = build_weights(M, cfg, wl, dev, args.weight_copies)
     x = W.activations(wl, "cuda")
     lg = W.router_logits(wl, "cuda")
     out = torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(M.workspace_bytes(cfg, wl.T), dtype=torch.uint8, device=dev)
-    copies = [tuple(ew.tiled())]
-    for _ in range(1, max(1, args.weight_copies)):
-        copies.append(tuple(t.clone() for t in copies[0]))
     stream = torch.cuda.current_stream()
 
     def step(i):
         w13, s13, w2, s2 = copies[i % len(copies)]
         M.moe_forward(cfg, x, lg, w13, s13, w2, s2, out=out, ws=ws, stream=stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = wall * 1e3 / args.steps
+    ms = wall * 1e3 / steps
 
-    # per-kernel breakdown: the same kernels through the stage entry points,
-    # HIP events recorded on the launch stream between them
     ids, wts = M.moe_route_topk(lg, wl.top_k)
-    ids_h = ids.cpu().numpy()
-    nbytes = algorithmic_bytes(wl, ids_h, M)
-    kern = {}
-    if not args.no_breakdown:
+    nbytes = algorithmic_bytes(wl, ids.cpu().numpy(), M)
+    kern, spread = {}, None
+    ks1 = M.plan_ksplit(cfg, wl.T, 13)
+    if breakdown:
         # the stages moe_forward runs: the front end (routing, permutation,
         # quantisation of x; one launch for small batches), GEMM1, GEMM2 +
-        # combine
+        # combine, with HIP events recorded on the launch stream between them
         names = ["front_end", "gemm1_swiglu", "gemm2_combine"]
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
         aq_b, as_b = M.intermediate_bytes(cfg, wl.T)
         nb = M.max_blocks(wl.T * wl.top_k, wl.E, bm)
         sid = torch.empty(nb * bm, dtype=torch.int32, device=dev)
@@ -219,7 +227,6 @@ def main():
         as_ = torch.empty(as_b, dtype=torch.uint8, device=dev)
         # GEMM1 with the K split moe_forward plans (small batches: GEMM1 pieces
         # plus the SwiGLU/re-quantisation kernel)
-        ks1 = M.plan_ksplit(cfg, wl.T, 13)
         part_b = M.splitk_bytes(cfg, wl.T, 13, ks1)
         part = torch.empty(max(part_b, 1), dtype=torch.uint8, device=dev)
 
@@ -239,39 +246,49 @@ def main():
                                           wts.data_ptr(), out.data_ptr(), wl.H, ws.data_ptr(), ws.numel(), sp)
             evs[3].record(stream)
 
-        for i in range(min(args.warmup, args.steps)):
+        for i in range(min(warmup, steps)):
             staged(ev[i], i)
         torch.cuda.synchronize()
-        for i in range(args.steps):
+        for i in range(steps):
             staged(ev[i], i)
         torch.cuda.synchronize()
         for j, n in enumerate(names):
-            kern[n] = float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)])) * 1e3  # us
-        # spread over the steps: the whole staged step and GEMM1, from the same events
-        tot = np.array([ev[i][0].elapsed_time(ev[i][len(names)]) for i in range(args.steps)]) * 1e3
-        g1 = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]) * 1e3
+            kern[n] = float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)])) * 1e3  # us
+        tot = np.array([ev[i][0].elapsed_time(ev[i][len(names)]) for i in range(steps)]) * 1e3
+        g1 = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]) * 1e3
         spread = {n: {"p10": round(float(np.percentile(a, 10)), 2), "median": round(float(np.median(a)), 2),
                       "p90": round(float(np.percentile(a, 90)), 2)}
                   for n, a in (("step", tot), ("gemm1_swiglu", g1))}
 
-    tokens_per_s = wl.T / (ms * 1e-3)
+    peak_f = MFMA_PEAK_TFLOPS[wl.mode]
     flops = wl.flops()
     tflops = flops / (ms * 1e-3) / 1e12
-    dom = "gemm1_swiglu"
+    bw = HBM_PEAK_GBS * 1e9
+    # the layer's attainable step time: the larger of its MFMA time at the
+    # format's dense peak and its algorithmic bytes at the HBM peak
+    layer_floor = max(flops / (peak_f * 1e12), nbytes["layer"] / bw)
     roof = None
     if kern:
         # GEMM1 is bound by HBM or by the MFMA peak of the layer's format,
         # whichever its arithmetic intensity (real sizes) puts it under
-        dur = kern[dom] * 1e-6
+        dur = kern["gemm1_swiglu"] * 1e-6
         flops1 = 4.0 * wl.T * wl.top_k * wl.I * wl.H
-        peak_f = MFMA_PEAK_TFLOPS[wl.mode]
-        mfma_bound = flops1 / nbytes["gemm1"] > peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
+        floor1 = max(flops1 / (peak_f * 1e12), nbytes["gemm1"] / bw)
+        mfma_bound = flops1 / (peak_f * 1e12) > nbytes["gemm1"] / bw
         common = {"traffic": recorded_traffic(wl.name, wl.T, bm),
                   "kernel": ("moe_gemm_stream (GEMM1 + clamped SwiGLU + re-quantisation)" if ks1 == 1 else
                              f"moe_gemm_stream (GEMM1, leftover items in {-ks1} K pieces) + gemm1_tail_finish"
                              if ks1 < 0 else f"moe_gemm_stream (GEMM1, K split {ks1}) + swiglu_requant"),
-                  "kernel_us": round(kern[dom], 2), "algorithmic_bytes": nbytes["gemm1"],
-                  "algorithmic_flops": flops1}
+                  "kernel_us": round(kern["gemm1_swiglu"], 2), "algorithmic_bytes": nbytes["gemm1"],
+                  "algorithmic_flops": flops1,
+                  # attainable = min(peak, intensity x HBM bandwidth), and the
+                  # kernel's fraction of it
+                  "intensity_flop_per_byte": round(flops1 / nbytes["gemm1"], 2),
+                  "attainable_tflops": round(min(peak_f, flops1 / nbytes["gemm1"] * bw / 1e12), 1),
+                  "achieved_tflops": round(flops1 / dur / 1e12, 1),
+                  "attainable_frac": round(floor1 / dur, 4),
+                  "hbm_frac": round(nbytes["gemm1"] / dur / bw, 4),
+                  "mfma_frac": round(flops1 / dur / 1e12 / peak_f, 4)}
         if mfma_bound:
             tf = flops1 / dur / 1e12
             roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": peak_f, "unit": "TFLOP/s",
@@ -281,34 +298,74 @@ def main():
             roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), **common}
     res = {
+        "ms_per_step": round(ms, 4),
+        "tokens_per_s": round(wl.T / (ms * 1e-3), 1),
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "Hp": wl.Hp, "Ip": wl.Ip, "E": wl.E,
+                   "top_k": wl.top_k, "quant": wl.mode, "block_m": bm, "swiglu_limit": wl.swiglu_limit,
+                   "ksplit": [ks1, M.plan_ksplit(cfg, wl.T, 2)]},
+        "effective_tflops": round(tflops, 3),
+        "mfma_frac": round(tflops / peak_f, 5),
+        "layer_hbm_frac": round(nbytes["layer"] / (ms * 1e-3) / bw, 4),
+        "layer_attainable_us": round(layer_floor * 1e6, 1),
+        "layer_attainable_frac": round(layer_floor / (ms * 1e-3), 4),
+        "active_experts": nbytes["active_experts"],
+        "layer_algorithmic_bytes": nbytes["layer"],
+        "kernels_us": {k: round(v, 2) for k, v in kern.items()},
+        "events_us": spread,
+        "roofline": roof,
+    }
+    return res, copies, x, lg
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
+              "sharding is described, not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as W
+    import mxfp4_quantized_weights_amd as M
+
+    torch.cuda.set_device(0)
+    wl = W.WORKLOADS[args.workload]
+    if args.T:
+        wl = wl.with_(T=args.T)
+    r, copies, x, lg = measure(M, wl, args, breakdown=not args.no_breakdown)
+    res = {
         "metric": "MoE layer tokens/s + effective TFLOP/s (% of MFMA/HBM roofline), 1 MI355X",
-        "value": round(tokens_per_s, 1),
+        "value": r["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": r["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp4e2m1" if wl.mode == "mxfp4" else "fp8e4m3",
         "data": "synthetic (seeded N(0,1) activations/logits, N(0,0.02) weights, quantised by the library)",
-        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "Hp": wl.Hp, "Ip": wl.Ip, "E": wl.E,
-                   "top_k": wl.top_k, "quant": wl.mode, "block_m": bm, "swiglu_limit": wl.swiglu_limit,
-                   "ksplit": [M.plan_ksplit(cfg, wl.T, 13), M.plan_ksplit(cfg, wl.T, 2)]},
-        "effective_tflops": round(tflops, 3),
-        "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[wl.mode], 5),
-        "layer_hbm_frac": round(nbytes["layer"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "active_experts": nbytes["active_experts"],
-        "layer_algorithmic_bytes": nbytes["layer"],
-        "kernels_us": {k: round(v, 2) for k, v in kern.items()},
-        "events_us": spread if kern else None,
+        **{k: v for k, v in r.items() if k not in ("ms_per_step", "tokens_per_s")},
         "weight_copies": len(copies),
-        "roofline": roof,
         "cpu_baseline": None,
     }
-    if args.cpu_sample > 0:
+    if args.cpu_sample != 0:
         res["cpu_baseline"] = cpu_baseline(wl, x, lg, args.cpu_sample)
+    if not args.no_extras and not args.T and args.workload == "prefill_fp8":
+        # the decode layer shares the prefill layer's weights; the MXFP4 layer
+        # has its own
+        extras = {}
+        d, _, _, _ = measure(M, W.WORKLOADS["decode_fp8"], args, copies=copies, breakdown=not args.no_breakdown,
+                             block_m=0)
+        extras["decode_fp8"] = d
+        del copies
+        torch.cuda.empty_cache()
+        m, _, _, _ = measure(M, W.WORKLOADS["prefill_mxfp4"], args, breakdown=not args.no_breakdown, block_m=0)
+        extras["prefill_mxfp4"] = m
+        res["extra"] = extras
     print(json.dumps(res), flush=True)
 
 

@@ -32,7 +32,6 @@ that actually occurred: per output element, sum_j w[t,j] * |w2_e| . |deq_gpu
 """
 from __future__ import annotations
 
-import concurrent.futures
 import functools
 import os
 import sys
@@ -417,25 +416,11 @@ def oracle_weights_subset(wl: W.Workload, experts, device) -> O.QuantWeights:
     Q, done = _QCACHE[key]
     todo = sorted(set(int(e) for e in experts) - done)
     if todo:
-        quant = {"fp8": O.quant_fp8_weight, "fp8_ue8m0": O.quant_fp8e8_weight,
-                 "mxfp4": O.quant_mxfp4_rows}[wl.mode]
-
-        def one(args):
-            e, w13, w2 = args
-            Q.w13[e], Q.s13[e] = quant(w13)
-            Q.w2[e], Q.s2[e] = quant(w2)
-
-        threads = min(16, len(os.sched_getaffinity(0)))
-        with concurrent.futures.ThreadPoolExecutor(threads) as ex:
-            futs = []
-            for e in todo:   # raw weights are drawn here, on the calling thread
-                w13 = W.expert_w13(wl, e, device).cpu().numpy()
-                w2 = W.expert_w2(wl, e, device).cpu().numpy()
-                futs.append(ex.submit(one, (e, w13, w2)))
-                if len(futs) >= 2 * threads:
-                    futs.pop(0).result()
-            for f in futs:
-                f.result()
+        from oracle.from_workload import quantize_experts
+        part = quantize_experts(wl, todo, device)
+        for e in todo:
+            Q.w13[e], Q.s13[e], Q.w2[e], Q.s2[e] = part.w13[e], part.s13[e], part.w2[e], part.s2[e]
+        del part
         done.update(todo)
     return Q
 
