@@ -324,6 +324,30 @@ moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, in
                          const void* w2, const void* w2_scale, void* out_bf16, int64_t ld_out,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* Size of the scratch that moe_forward_noalloc keeps in a static device
+ * array: 128 MiB, held on every GPU the library runs on until the process
+ * ends.  It covers moe_workspace_bytes(cfg, T) for decode batches, e.g. up to
+ * 730 tokens of the 288-expert top-8 block-FP8 layer with H = 4096, I = 1024
+ * (block_m 16/32). */
+#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments and results as moe_forward (the same kernels) without ws /
+ * ws_bytes: the scratch is the library's static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES on the current device.  Returns
+ * MOE_ERR_WORKSPACE (launching nothing) when moe_workspace_bytes(cfg, T)
+ * exceeds it.  Allocates nothing (no hipMalloc, no allocating library
+ * call); the array's device address is looked up once per device, on the
+ * first call made with that device current.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (e.g. on two
+ * streams) race, so serialise them.  Nothing in the array needs to start at
+ * zero; it keeps the last call's contents. */
+moe_status_t moe_forward_noalloc(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, int64_t ld_x,
+                                 const float* router_logits, const void* w13, const void* w13_scale,
+                                 const void* w2, const void* w2_scale, void* out_bf16, int64_t ld_out,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

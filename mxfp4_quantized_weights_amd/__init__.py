@@ -29,6 +29,7 @@ MOE_LAYOUT_CANONICAL = 0
 MOE_LAYOUT_TILED_V2 = 0x4D310002
 MOE_DTYPE_BF16 = 1
 MOE_DTYPE_F32 = 2
+MOE_NOALLOC_SCRATCH_BYTES = 128 << 20
 QUANT_MODES = {"fp8": MOE_QUANT_FP8_BLOCK, "mxfp4": MOE_QUANT_MXFP4, "fp8_ue8m0": MOE_QUANT_FP8_UE8M0}
 
 
@@ -95,6 +96,7 @@ _SIGS = {
                                                        _SZ, _P]),
     "moe_grouped_gemm2_combine_splitk": (ctypes.c_int, [_CFGP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
                                                         _I32, _P, _SZ, _P]),
+    "moe_forward_noalloc": (ctypes.c_int, [_CFGP, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _I64, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -376,6 +378,24 @@ def moe_forward(cfg: MoeCfg, x: torch.Tensor, logits: torch.Tensor, w13, s13, w2
                             _dev(s13, None, "w13_scale"), _dev(w2, None, "w2"), _dev(s2, None, "w2_scale"),
                             _dev(out, torch.bfloat16, "out", contiguous=False), out.stride(0), ws.data_ptr(),
                             ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+    return out
+
+
+def moe_forward_noalloc(cfg: MoeCfg, x: torch.Tensor, logits: torch.Tensor, w13, s13, w2, s2,
+                        out: torch.Tensor | None = None, stream=None):
+    """moe_forward with the library's static scratch (no workspace argument;
+    the library allocates nothing).  Raises MoeError(MOE_ERR_WORKSPACE) when
+    the batch needs more than MOE_NOALLOC_SCRATCH_BYTES."""
+    T = x.shape[0]
+    if x.stride(1) != 1:
+        raise ValueError("x must have unit column stride")
+    if out is None:
+        out = torch.empty(T, cfg.pad.hidden, dtype=torch.bfloat16, device=x.device)
+    _check(_lib.moe_forward_noalloc(ctypes.byref(cfg), T, _dev(x, torch.bfloat16, "x", contiguous=False),
+                                    x.stride(0), _dev(logits, torch.float32, "router_logits"), _dev(w13, None, "w13"),
+                                    _dev(s13, None, "w13_scale"), _dev(w2, None, "w2"), _dev(s2, None, "w2_scale"),
+                                    _dev(out, torch.bfloat16, "out", contiguous=False), out.stride(0),
+                                    _stream(stream)), "moe_forward_noalloc")
     return out
 
 

@@ -12,6 +12,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "moe_internal.h"
 
@@ -312,6 +314,78 @@ hipError_t gemm2_and_combine(const moe_cfg_t* c, int32_t T, moe::GemmArgs a, int
   return hipSuccess;
 }
 
+// The whole layer with its scratch in ws (validated by the caller).
+moe_status_t forward_impl(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, int64_t ld_x,
+                          const float* router_logits, const void* w13, const void* w13_scale, const void* w2,
+                          const void* w2_scale, void* out_bf16, int64_t ld_out, void* ws, hipStream_t s) {
+  const Layout L = layout_for(cfg, T);
+  uint8_t* p = (uint8_t*)ws;
+  int32_t* ids = (int32_t*)p; p += L.ids;
+  float* wts = (float*)p; p += L.wts;
+  int32_t* sorted = (int32_t*)p; p += L.sorted;
+  int32_t* bexp = (int32_t*)p; p += L.bexp;
+  int32_t* offs = (int32_t*)p; p += L.offs;
+  int32_t* npp = (int32_t*)p; p += L.npp;
+  void* xq = p; p += L.xq;
+  void* xs = p; p += L.xs;
+  void* aq = p; p += L.aq;
+  void* as = p; p += L.as;
+  float* part = (float*)p; p += L.part;
+  uint8_t* y = p;
+
+  const int E = cfg->num_experts, k = cfg->top_k, BM = cfg->block_m;
+  const int64_t P = (int64_t)T * k;
+  const int32_t nb = max_blocks(P, E, BM);
+  hipError_t e;
+  if ((e = front_end(cfg, T, router_logits, x_bf16, ld_x, ids, wts, sorted, bexp, offs, npp, xq, xs, s)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  moe::GemmArgs a1 = gemm1_args(cfg, T, xq, xs, sorted, bexp, npp, w13, w13_scale, aq, as);
+  if ((e = run_gemm1(cfg, T, a1, nb, plan_ksplit(cfg, T, 13), part, s)) != hipSuccess) return MOE_ERR_HIP;
+  moe::GemmArgs a2 = gemm2_args(cfg, T, aq, as, sorted, bexp, npp, w2, w2_scale, y, wts);
+  return hip_status(gemm2_and_combine(cfg, T, a2, nb, plan_ksplit(cfg, T, 2), out_bf16, ld_out, s));
+}
+
+// Arguments of moe_forward / moe_forward_noalloc other than the scratch.
+moe_status_t check_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, int64_t ld_x,
+                           const float* router_logits, const void* w13, const void* w13_scale, const void* w2,
+                           const void* w2_scale, void* out_bf16, int64_t ld_out) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
+  if ((st = check_layout(cfg)) != MOE_OK) return st;
+  if (ld_x < cfg->pad.hidden || ld_out < cfg->pad.hidden) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!x_bf16 || !router_logits || !w13 || !w13_scale || !w2 || !w2_scale || !out_bf16) return MOE_ERR_NULL;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of moe_forward_noalloc: one static device array per GPU the
+// library runs on, held until the process ends.  Host code never uses the
+// array's name as an address (on the host it only names the symbol): the
+// device address comes from hipGetSymbolAddress, once per device with that
+// device current, and is kept per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (resolved on the device's first call).
+moe_status_t noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -539,43 +613,26 @@ size_t moe_splitk_bytes(const moe_cfg_t* cfg, int32_t T, int32_t which, int32_t 
 moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, int64_t ld_x, const float* router_logits,
                          const void* w13, const void* w13_scale, const void* w2, const void* w2_scale, void* out_bf16,
                          int64_t ld_out, void* ws, size_t ws_bytes, void* stream) {
-  moe_status_t st = check_cfg(cfg);
-  if (st != MOE_OK) return st;
-  if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
-  if ((st = check_layout(cfg)) != MOE_OK) return st;
-  if (ld_x < cfg->pad.hidden || ld_out < cfg->pad.hidden) return MOE_ERR_SHAPE;
-  if (T == 0) return MOE_OK;
-  if (!x_bf16 || !router_logits || !w13 || !w13_scale || !w2 || !w2_scale || !out_bf16 || !ws) return MOE_ERR_NULL;
-  const Layout L = layout_for(cfg, T);
-  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  moe_status_t st =
+      check_forward(cfg, T, x_bf16, ld_x, router_logits, w13, w13_scale, w2, w2_scale, out_bf16, ld_out);
+  if (st != MOE_OK || T == 0) return st;
+  if (!ws) return MOE_ERR_NULL;
+  if (ws_bytes < layout_for(cfg, T).total) return MOE_ERR_WORKSPACE;
+  return forward_impl(cfg, T, x_bf16, ld_x, router_logits, w13, w13_scale, w2, w2_scale, out_bf16, ld_out, ws,
+                      as_stream(stream));
+}
 
-  uint8_t* p = (uint8_t*)ws;
-  int32_t* ids = (int32_t*)p; p += L.ids;
-  float* wts = (float*)p; p += L.wts;
-  int32_t* sorted = (int32_t*)p; p += L.sorted;
-  int32_t* bexp = (int32_t*)p; p += L.bexp;
-  int32_t* offs = (int32_t*)p; p += L.offs;
-  int32_t* npp = (int32_t*)p; p += L.npp;
-  void* xq = p; p += L.xq;
-  void* xs = p; p += L.xs;
-  void* aq = p; p += L.aq;
-  void* as = p; p += L.as;
-  float* part = (float*)p; p += L.part;
-  uint8_t* y = p;
-
-  hipStream_t s = as_stream(stream);
-  const int E = cfg->num_experts, k = cfg->top_k, BM = cfg->block_m;
-  const int64_t P = (int64_t)T * k;
-  const int32_t nb = max_blocks(P, E, BM);
-  const int mode = cfg->quant_mode;
-  hipError_t e;
-  if ((e = front_end(cfg, T, router_logits, x_bf16, ld_x, ids, wts, sorted, bexp, offs, npp, xq, xs, s)) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
-  moe::GemmArgs a1 = gemm1_args(cfg, T, xq, xs, sorted, bexp, npp, w13, w13_scale, aq, as);
-  if ((e = run_gemm1(cfg, T, a1, nb, plan_ksplit(cfg, T, 13), part, s)) != hipSuccess) return MOE_ERR_HIP;
-  moe::GemmArgs a2 = gemm2_args(cfg, T, aq, as, sorted, bexp, npp, w2, w2_scale, y, wts);
-  return hip_status(gemm2_and_combine(cfg, T, a2, nb, plan_ksplit(cfg, T, 2), out_bf16, ld_out, s));
+moe_status_t moe_forward_noalloc(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, int64_t ld_x,
+                                 const float* router_logits, const void* w13, const void* w13_scale, const void* w2,
+                                 const void* w2_scale, void* out_bf16, int64_t ld_out, void* stream) {
+  moe_status_t st =
+      check_forward(cfg, T, x_bf16, ld_x, router_logits, w13, w13_scale, w2, w2_scale, out_bf16, ld_out);
+  if (st != MOE_OK || T == 0) return st;
+  if (layout_for(cfg, T).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws)) != MOE_OK) return st;
+  return forward_impl(cfg, T, x_bf16, ld_x, router_logits, w13, w13_scale, w2, w2_scale, out_bf16, ld_out, ws,
+                      as_stream(stream));
 }
 
 }  // extern "C"
