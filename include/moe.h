@@ -85,11 +85,11 @@ enum { MOE_GATE_SEPARATED = 0, MOE_GATE_INTERLEAVED = 1 };
 /* Weight layout tags.  CANONICAL is row-major [E, N, K] (what
  * moe_quant_weights writes).  TILED_V2 is the GEMM kernels' layout, written
  * only by moe_preshuffle_weights (the runner owns its preshuffle): 16-row x
- * 128-column MFMA tiles ordered [E][N tile][K block][16 tiles], an N tile
+ * 128-column MFMA tiles ordered [E][N tile][16/R][K block][R], an N tile
  * being the 256 weight rows one GEMM work item multiplies (w13: 128 gate
  * rows and the matching 128 up rows; w2: 256 rows, a half last N tile
- * zero-padded).  The earlier TILED_V1 tag (tiles ordered [E][N/16][K/128])
- * is no longer accepted. */
+ * zero-padded), so the tiles of one K block come in contiguous runs of R
+ * (R fixed per matrix and mode: block FP8 w13 16, w2 4; MXFP4 w13 1). */
 enum { MOE_LAYOUT_CANONICAL = 0, MOE_LAYOUT_TILED_V2 = 0x4D310002 };
 
 /* Element types accepted by moe_quant_act / moe_quant_weights. */

@@ -134,7 +134,11 @@ struct Ring {
 // cursors).  The
 // weight loads carry the non-temporal hint: weights are read once per launch.
 #pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; the compiler does not use it in these kernels
+// M0 is reserved by the compiler, which cannot see these writes; the library
+// relies on no compiler-generated code using M0 (no register-indexed moves,
+// messages, GWS or buffer-to-LDS loads), which the test suite checks on the
+// disassembly of the built code objects.
+#pragma clang diagnostic ignored "-Winline-asm"
 template <bool NT>
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   if constexpr (NT)

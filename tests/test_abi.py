@@ -351,3 +351,47 @@ def test_no_kernel_uses_scratch_memory(tmp_path):
     assert len(kernels) > 50
     assert any("moe_gemm_stream_kernel" in k for k in kernels)
     assert {k: v for k, v in kernels.items() if v} == {}
+
+
+def test_m0_written_only_by_the_direct_lds_loads(tmp_path):
+    """The GEMMs' direct global->LDS loads are inline assembly that sets M0
+    (the LDS destination base) right before each load.  The compiler keeps M0
+    for itself and cannot see those writes, so this holds only while no
+    compiler-generated code in the library uses M0.  Checked on the
+    disassembly of the built gfx950 code objects: every instruction that
+    names m0 is `s_mov_b32 m0, <sgpr>` followed by `s_nop 0` and a
+    global_load_lds_dword{,x4}; every such load comes right after one; and no
+    instruction that uses M0 implicitly (register-indexed moves, messages,
+    GWS/append/consume, buffer loads to LDS) appears."""
+    import re
+    import shutil
+    import subprocess
+    objdump = "/opt/rocm/llvm/bin/llvm-objdump"
+    if not os.path.exists(objdump):
+        pytest.skip("LLVM tools of the ROCm install not found")
+    lib = tmp_path / "libmoe.so"
+    shutil.copy(M.LIB_PATH, lib)
+    subprocess.run([objdump, "--offloading", str(lib)], cwd=tmp_path, check=True, capture_output=True)
+    objs = sorted(p for p in tmp_path.iterdir() if "gfx950" in p.name)
+    assert objs
+    insts = []
+    for o in objs:
+        dis = subprocess.run([objdump, "-d", "--mcpu=gfx950", str(o)], check=True, capture_output=True,
+                             text=True).stdout
+        for line in dis.splitlines():
+            line = line.split("//")[0].strip()
+            if line and not line.endswith(":") and not line.startswith(("Disassembly", "file format")):
+                insts.append(line)
+    writes = loads = 0
+    implicit = re.compile(r"movrel|s_sendmsg|ds_gws|ds_append|ds_consume|set_gpr_idx|buffer_load\S*\s.*\blds\b")
+    for i, ins in enumerate(insts):
+        op = ins.split()[0]
+        assert not implicit.search(ins), f"instruction with an implicit M0 use: {ins}"
+        if re.search(r"\bm0\b", ins):
+            assert re.fullmatch(r"s_mov_b32 m0, s\d+", ins), f"M0 used outside the direct loads: {ins}"
+            assert insts[i + 1] == "s_nop 0" and insts[i + 2].startswith("global_load_lds_dword"), insts[i:i + 3]
+            writes += 1
+        if op.startswith("global_load_lds"):
+            assert insts[i - 1] == "s_nop 0" and insts[i - 2].startswith("s_mov_b32 m0,"), insts[i - 2:i + 1]
+            loads += 1
+    assert writes == loads > 1000
