@@ -324,6 +324,15 @@ moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, in
                          const void* w2, const void* w2_scale, void* out_bf16, int64_t ld_out,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* Diagnostic (not part of the layer): one 16x16 output tile C = A . B^T over
+ * K = 128 from e4m3 codes, computed as one K block of the grouped GEMMs:
+ * kind 0 with one FP8 MFMA (16x16x128, unit scales; GEMM2's instruction),
+ * kind 1 with the operands widened exactly to f16 and four 16x16x32 f16 MFMAs
+ * (GEMM1's instructions).  a, b: device u8 [16, 128] row-major e4m3 codes
+ * (16-byte aligned); out: device f32 [16, 16] row-major.  Lets tests compare
+ * the two matrix-core sums with an exact one. */
+moe_status_t moe_diag_mfma_tile(int32_t kind, const void* a, const void* b, float* out, void* stream);
+
 /* Size of the scratch that moe_forward_noalloc keeps in a static device
  * array: 128 MiB, held on every GPU the library runs on until the process
  * ends.  It covers moe_workspace_bytes(cfg, T) for decode batches, e.g. up to

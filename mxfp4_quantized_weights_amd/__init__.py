@@ -97,6 +97,7 @@ _SIGS = {
     "moe_grouped_gemm2_combine_splitk": (ctypes.c_int, [_CFGP, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
                                                         _I32, _P, _SZ, _P]),
     "moe_forward_noalloc": (ctypes.c_int, [_CFGP, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _I64, _P]),
+    "moe_diag_mfma_tile": (ctypes.c_int, [_I32, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -396,6 +397,16 @@ def moe_forward_noalloc(cfg: MoeCfg, x: torch.Tensor, logits: torch.Tensor, w13,
                                     _dev(s13, None, "w13_scale"), _dev(w2, None, "w2"), _dev(s2, None, "w2_scale"),
                                     _dev(out, torch.bfloat16, "out", contiguous=False), out.stride(0),
                                     _stream(stream)), "moe_forward_noalloc")
+    return out
+
+
+def moe_diag_mfma_tile(kind: int, a: torch.Tensor, b: torch.Tensor, stream=None) -> torch.Tensor:
+    """Diagnostic: C = A . B^T (f32 [16, 16]) from e4m3 codes a, b (u8 [16, 128])
+    with one FP8 MFMA (kind 0) or four f16 MFMAs on exactly widened operands
+    (kind 1), as the grouped GEMMs compute one K block."""
+    out = torch.empty(16, 16, dtype=torch.float32, device=a.device)
+    _check(_lib.moe_diag_mfma_tile(kind, _dev(a, torch.uint8, "a"), _dev(b, torch.uint8, "b"), out.data_ptr(),
+                                   _stream(stream)), "moe_diag_mfma_tile")
     return out
 
 

@@ -95,16 +95,25 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 __host__ __device__ inline bool tail_split_on(int items, int W) { return 2 * (items % W) <= W; }
 
 // Waves of a workgroup: 4 column waves (the N tile's 16 weight tiles, 4 each)
-// times BM/64 token halves of 64 tokens; for BM < 64 one token group of BM/16
-// tiles.  A wave multiplies MT token tiles by its 4 weight tiles.
-constexpr int ring_waves(int bm) { return bm >= 64 ? bm / 16 : 4; }
+// times WT token groups: BM/64 groups of 64 tokens (4 token tiles per wave)
+// for BM >= 64, one group of BM/16 tiles below.  A wave multiplies MT token
+// tiles by its 4 weight tiles.  (One group of 8 token tiles at BM = 128 --
+// 1.5 instead of 2 FP8->f16 converts per MFMA on GEMM1's f16 path, one wave
+// per SIMD -- measured 40% slower on the 4096-token prefill layer: the
+// accumulators of 32 tiles leave too few registers, so MFMA partial sums go
+// through AGPRs and the MFMA chains serialise.)
+constexpr int ring_waves(int mode, int bm) {
+  return (void)mode, bm >= 64 ? bm / 16 : 4;
+}
 
 template <int MODE, int BM>
 struct Ring {
-  static constexpr int NWAVE = ring_waves(BM);
+  static constexpr int NWAVE = ring_waves(MODE, BM);
   static constexpr int NTH = NWAVE * 64;
-  static constexpr int MT = BM >= 64 ? 4 : BM / 16;              // token tiles per wave
   static constexpr int TT = BM / 16;                             // token tiles per slot
+  static constexpr int WT = NWAVE / 4;                           // token groups
+  static constexpr int MT = TT / WT;                             // token tiles per wave
+  static constexpr int MTH = MT >= 4 ? MT / 4 : 1;               // 64-token scale words per wave
   static constexpr int TILE = (MODE == kGemmMx) ? 1024 : 2048;  // one 16 x 128 operand tile
   static constexpr int HALVES = TILE / 1024;
   static constexpr int AROW = (MODE == kGemmMx) ? 64 : 128;     // token bytes per K block
@@ -112,6 +121,7 @@ struct Ring {
   static constexpr int T_OFF = 16 * TILE;                        // TT token tiles
   static constexpr int TS_OFF = T_OFF + TT * TILE;               // token scales, 256 B per 64 tokens
   static constexpr int NTS = BM >= 64 ? BM / 64 : 1;
+  static constexpr int TSW = 4 * NTS / NWAVE > 1 ? 4 * NTS / NWAVE : 1;  // 16-scale chunks per wave
   static constexpr int WSC_OFF = TS_OFF + NTS * 256;            // FP8: the K block's two weight scales
   static constexpr int SLOT = WSC_OFF + 16;
   static constexpr int WS_BYTES = 16 * 256;                      // MX: one group of weight scale dwords
@@ -121,7 +131,7 @@ struct Ring {
   static constexpr int DWS = (MODE == kGemmMx) ? 16 / NWAVE : 0;  // every 4th K block only
   // loads every wave issues in every K block (waits use this minimum; waves
   // that issue more only wait longer)
-  static constexpr int D = DW + NTD / NWAVE + 1;
+  static constexpr int D = DW + NTD / NWAVE + TSW;
   static_assert(16 * HALVES % NWAVE == 0 && (NTD % NWAVE == 0 || NTD < NWAVE), "load split");
 };
 
@@ -183,17 +193,17 @@ struct RingSrc {
   using R = Ring<MODE, BM>;
   const uint8_t* w[R::DW];
   const uint8_t* t[R::DT];
-  const uint8_t* ts;
+  const uint8_t* ts[R::TSW];
   const uint8_t* ws[R::DWS > 0 ? R::DWS : 1];
   const uint8_t* wsc;  // FP8, lanes 0 and 1 of the last wave: weight-scale row of K block 0
   int wk;              // bytes between a weight tile's K blocks (tile run x tile bytes)
   int wsk;             // MX: bytes between a scale word row's groups of 4 K blocks
 };
 
-// Loads of K block kb into `slot`.  Token scales: each wave fetches 16 of the
-// 64 scales of its token half (lanes 0..15 only), placed so that lane l of a
-// compute wave finds the scales of token tiles m = 0..3, row l % 16, in one
-// 16-byte word.  FP8 weight scales: the last wave fetches the K block's two
+// Loads of K block kb into `slot`.  Token scales: chunk c (16 scales, 4 per
+// 64-token group) is fetched by wave c / TSW (lanes 0..15 only), placed so
+// that lane l of a compute wave finds the scales of 4 token tiles m, row
+// l % 16, in one 16-byte word per 64 tokens.  FP8 weight scales: the last wave fetches the K block's two
 // fp32 block scales (lanes 0 and 1).  MX weight scales (one dword holds 4 K
 // blocks) are fetched only when `ws` is non-null, into that buffer.
 template <int MODE, int BM>
@@ -210,7 +220,11 @@ __device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const u
     if (wave * R::DT + q < R::NTD) dma16<false>(src.t[q] + kb * R::AROW, base + R::T_OFF + (wave * R::DT + q) * 1024);
   // token scales: fp32 per K block, or the E8M0 dword of K blocks kb & ~3 .. +3
   const int ts_off = e8_tokens(MODE) ? (kb & ~3) : kb * 4;
-  if (lane < 16) dma4(src.ts + ts_off, base + R::TS_OFF + (wave >> 2) * 256 + (wave & 3) * 64);
+#pragma unroll
+  for (int h = 0; h < R::TSW; ++h) {
+    const int c = wave * R::TSW + h;
+    if (lane < 16) dma4(src.ts[h] + ts_off, base + R::TS_OFF + (c >> 2) * 256 + (c & 3) * 64);
+  }
   if constexpr (MODE != kGemmMx) {
     if (wave == R::NWAVE - 1 && lane < 2) dma4(src.wsc + kb * 4, base + R::WSC_OFF);
   }
@@ -223,11 +237,11 @@ __device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const u
   }
 }
 
-// Per-lane row of the token-scale load (see ring_issue): entry i = 16*(wave%4)
-// + lane of token half wt holds token tile i % 4, row i / 4.
-__device__ __forceinline__ int ring_scale_row(int wave, int lane) {
-  const int i = (wave & 3) * 16 + (lane & 15);
-  return (wave >> 2) * 64 + (i & 3) * 16 + (i >> 2);
+// Per-lane row of the token-scale load of chunk c (see ring_issue): entry
+// i = 16*(c%4) + lane of 64-token group c/4 holds token tile i % 4, row i / 4.
+__device__ __forceinline__ int ring_scale_row(int c, int lane) {
+  const int i = (c & 3) * 16 + (lane & 15);
+  return (c >> 2) * 64 + (i & 3) * 16 + (i >> 2);
 }
 
 // FP8 token tile in LDS: load h of the tile holds, at lane j's 16 bytes, row
@@ -267,9 +281,9 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
   using R = Ring<MODE, BM>;
   const int lane = threadIdx.x & 63;
   const uint8_t* wl = slot + R::W_OFF + lane * 16;
-  const uint8_t* tt = slot + R::T_OFF + wt * 4 * R::TILE;  // the wave's 4 token tiles
+  const uint8_t* tt = slot + R::T_OFF + wt * R::MT * R::TILE;  // the wave's MT token tiles
   const uint8_t* tl = tt + lane * 16;
-  const uint8_t* tsl = slot + R::TS_OFF + wt * 256 + (lane & 15) * 16;
+  const uint8_t* tsl = slot + R::TS_OFF + wt * R::MTH * 256 + (lane & 15) * 16;
   constexpr int MT = R::MT;
   if constexpr (MODE == kGemmMx) {
     const uint4 tsd = *(const uint4*)tsl;
@@ -294,22 +308,27 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
       }
     }
   } else {
-    // token scales of tiles m = 0..3 (row lane % 16): fp32, or E8M0 bytes
-    // (byte kb % 4 of each dword) and their exact fp32 values
-    float tsc[4];
-    int tsb[4];
-    if constexpr (e8_tokens(MODE)) {
-      const uint4 tw = *(const uint4*)tsl;
-      const int sh = 8 * (kb & 3);
-      const uint32_t w4[4] = {tw.x, tw.y, tw.z, tw.w};
+    // token scales of tiles m (row lane % 16), one 16-byte word per 4
+    // tiles: fp32, or E8M0 bytes (byte kb % 4 of each dword) and their exact
+    // fp32 values
+    constexpr int NSC = 4 * R::MTH;
+    float tsc[NSC];
+    int tsb[NSC];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        tsb[m] = (int)((w4[m] >> sh) & 0xFFu);
-        tsc[m] = e8m0_value((uint32_t)tsb[m]);
+    for (int hh = 0; hh < R::MTH; ++hh) {
+      if constexpr (e8_tokens(MODE)) {
+        const uint4 tw = *(const uint4*)(tsl + hh * 256);
+        const int sh = 8 * (kb & 3);
+        const uint32_t w4[4] = {tw.x, tw.y, tw.z, tw.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          tsb[4 * hh + m] = (int)((w4[m] >> sh) & 0xFFu);
+          tsc[4 * hh + m] = e8m0_value((uint32_t)tsb[4 * hh + m]);
+        }
+      } else {
+        const float4 ts = *(const float4*)(tsl + hh * 256);
+        tsc[4 * hh + 0] = ts.x; tsc[4 * hh + 1] = ts.y; tsc[4 * hh + 2] = ts.z; tsc[4 * hh + 3] = ts.w;
       }
-    } else {
-      const float4 ts = *(const float4*)tsl;
-      tsc[0] = ts.x; tsc[1] = ts.y; tsc[2] = ts.z; tsc[3] = ts.w;
     }
     // GEMM1: tiles 0,1 are gate rows (scale sw0), 2,3 up rows (sw1); GEMM2: all sw0
     if constexpr (MODE == kGemmE8) {
@@ -343,7 +362,7 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
           }
         }
       }
-    } else if constexpr (MT < 4) {
+    } else if constexpr (MT != 4) {
       // plain order: every weight tile widened once, then the token tiles
       v8h wh[4][4];
 #pragma unroll
@@ -447,7 +466,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// GEMM1 epilogue: lane l holds, for token t = wt*64 + m*16 + l%16, the
+// GEMM1 epilogue: lane l holds, for token t = (wt*MT + m)*16 + l%16, the
 // intermediate columns 32*wn + 16*jj + 4*(l/16) + i of the N tile (gate in
 // acc[m][jj], up in acc[m][jj+2]).  Clamped SwiGLU, then the row's 1x128
 // amax across the 4 column waves (FP8, through LDS) or the wave's own 1x32
@@ -465,7 +484,7 @@ __device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&
   float tmax[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const bool real = sid[wt * 64 + m * 16 + c16] < p.num_pairs;
+    const bool real = sid[(wt * MT + m) * 16 + c16] < p.num_pairs;
     float mx = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
@@ -482,14 +501,14 @@ __device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&
   if constexpr (!MXQ) {
     if (q == 0) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m) red[wn][wt * 64 + m * 16 + c16] = tmax[m];
+      for (int m = 0; m < MT; ++m) red[wn][(wt * MT + m) * 16 + c16] = tmax[m];
     }
     lds_barrier();
     const int nsc = p.Ip / 128;
     const int64_t ld_e8 = (nsc + 3) / 4 * 4;  // UE8M0 scale rows: whole dwords
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int t = wt * 64 + m * 16 + c16;
+      const int t = (wt * MT + m) * 16 + c16;
       const float amax = fmaxf(fmaxf(red[0][t], red[1][t]), fmaxf(red[2][t], red[3][t]));
       uint8_t* row = p.aq + (int64_t)(row0 + t) * p.Ip + nt * 128 + 32 * wn + 4 * q;
       if constexpr (E8Q) {
@@ -520,7 +539,7 @@ __device__ __forceinline__ void epilogue_gemm1_s(const GemmArgs& p, const v4f (&
     const int nsc = p.Ip / 32;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int t = wt * 64 + m * 16 + c16;
+      const int t = (wt * MT + m) * 16 + c16;
       const uint32_t b = e8m0_byte(tmax[m]);
       const float inv = e8m0_inverse(b);
       uint8_t* row = p.aq + (int64_t)(row0 + t) * (p.Ip / 2) + nt * 64 + 16 * wn + 2 * q;
@@ -550,7 +569,7 @@ __device__ __forceinline__ void epilogue_gemm1_part(const GemmArgs& p, const v4f
   int32_t* part_row = (int32_t*)(p.part + ((int64_t)p.num_pairs << p.ks_log2) * ld);
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int t = wt * 64 + m * 16 + c16;
+    const int t = (wt * MT + m) * 16 + c16;
     const int s = sid[t];
     if (s < p.num_pairs) {
       float* row = p.part + ((int64_t)ks * p.num_pairs + s) * ld + nt * 128 + 32 * wn + 4 * q;
@@ -594,7 +613,7 @@ __device__ __forceinline__ void epilogue_gemm1_tail(const GemmArgs& p, const v4f
   const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int t = wt * 64 + m * 16 + c16;
+    const int t = (wt * MT + m) * 16 + c16;
     float* row = p.part + (((int64_t)piece * gridDim.x + r) * BM + t) * 256 + 32 * wn + 4 * q;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
@@ -608,7 +627,7 @@ __device__ __forceinline__ void epilogue_gemm1_tail(const GemmArgs& p, const v4f
 // GEMM2 epilogue: the weighted rows v = routing weight * C of real pairs, in
 // y's block floating point (y_plane_bytes): int16 q = rint(v * 2^-s) with one
 // exponent s = max(floor(log2 max|v|) - 14, -128) per 64 columns of a row.
-// Lane l holds, for token t = wt*64 + m*16 + l%16, columns 64*wn + 16*j +
+// Lane l holds, for token t = (wt*MT + m)*16 + l%16, columns 64*wn + 16*j +
 // 4*(l/16) + i of the N tile, so a row's 64-column group is the wave's and
 // its 4 lanes (l/16 = 0..3) share the group's largest |v| through two lane
 // exchanges.  |v| * 2^-s < 2^15, and a value that rounds to 2^15 is stored
@@ -623,7 +642,7 @@ __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&
   const int col0 = (nt - p.nt0) * 256 + 64 * wn;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    const int t = wt * 64 + m * 16 + c16;
+    const int t = (wt * MT + m) * 16 + c16;
     const int s = sid[t];
     const bool real = s < p.num_pairs;
     const float w = real ? wts[t] : 0.0f;
@@ -661,7 +680,7 @@ __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&
 // ring's own waits to cover it (the S-1 K blocks of the prologue are issued
 // without waits), and the kernel then waits for it explicitly.
 template <int MODE, int BM, bool G1, int S, bool SPLIT>
-__global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(GemmArgs p) {
+__global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_kernel(GemmArgs p) {
   using R = Ring<MODE, BM>;
   static_assert(S >= 3 && S <= 5, "ring depth");
   constexpr int MT = R::MT;
@@ -794,12 +813,13 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
       const int g = wave * R::DT + q, mt = g / R::HALVES, h = g % R::HALVES;
       rs.t[q] = p.A + row_of(mt * 16 + (lane & 15)) * p.lda + kb0 * R::AROW + h * 64 + (lane >> 4) * 16;
     }
-    {
+#pragma unroll
+    for (int h = 0; h < R::TSW; ++h) {
       // scale bytes before K block kb0: fp32 and MX 4 per K block, UE8M0 1
-      const int64_t row = row_of(ring_scale_row(wave, lane));
-      rs.ts = (MODE == kGemmMx) ? (const uint8_t*)p.As + row * p.ldas + kb0 * 4
-              : e8_tokens(MODE) ? (const uint8_t*)p.As + row * p.ldas + kb0
-                                : (const uint8_t*)p.As + row * p.ldas * 4 + kb0 * 4;
+      const int64_t row = row_of(ring_scale_row(wave * R::TSW + h, lane));
+      rs.ts[h] = (MODE == kGemmMx) ? (const uint8_t*)p.As + row * p.ldas + kb0 * 4
+                 : e8_tokens(MODE) ? (const uint8_t*)p.As + row * p.ldas + kb0
+                                   : (const uint8_t*)p.As + row * p.ldas * 4 + kb0 * 4;
     }
     if constexpr (MODE != kGemmMx) {
       // GEMM1: the gate and the up 128-row block of the N tile; GEMM2: the
@@ -855,7 +875,7 @@ __global__ __launch_bounds__(ring_waves(BM) * 64) void moe_gemm_stream_kernel(Ge
     const int32_t* ids = ids_lds[ii % NB];
     int mv = 0;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) mv += ids[wt * 64 + m * 16] < p.num_pairs ? 1 : 0;
+    for (int m = 0; m < MT; ++m) mv += ids[(wt * MT + m) * 16] < p.num_pairs ? 1 : 0;
     c_mv = __builtin_amdgcn_readfirstlane(mv);
   };
 

@@ -91,6 +91,9 @@ DRIVER = textwrap.dedent(r'''
         lib.moe_permute_align(FAKE, T, k, E, c.block_m, FAKE, FAKE, None, FAKE, None)
         lib.moe_quant_act(None, rng.choice([0, 1, 2, 3]), T, h, I64(hp), hp, c.quant_mode, FAKE, FAKE, None)
         lib.moe_quant_weights(c.quant_mode, None, E, i, h, FAKE, FAKE, None)
+    for kind in (-1, 0, 1, 2):
+        lib.moe_diag_mfma_tile(kind, None, FAKE, FAKE, None)
+    lib.moe_diag_mfma_tile(0, P((1 << 40) + 4), FAKE, FAKE, None)
     lib.moe_validate_cfg(None)
     lib.moe_workspace_bytes(None, 1)
     print("valid configurations seen:", ok)
@@ -102,7 +105,7 @@ def test_host_code_under_asan(tmp_path):
     flags = ["--offload-arch=gfx950", "-O1", "-std=c++20", "-fPIC", "-Xarch_host", "-g",
              "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-    objs = [str(tmp_path / f"{src}.o") for src in ("api", "route", "quant", "gemm")]
+    objs = [str(tmp_path / f"{src}.o") for src in ("api", "route", "quant", "gemm", "diag")]
     procs = [subprocess.Popen([HIPCC, *flags, "-c", os.path.join(CSRC, os.path.basename(o)[:-2] + ".hip"), "-o", o],
                               stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True) for o in objs]
     for p in procs:
