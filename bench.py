@@ -17,7 +17,8 @@ Prints one JSON line with tokens/s (whole job), effective TFLOP/s
 the same kernels, called through the stage entry points) with the attainable
 ceiling min(peak, intensity x HBM bandwidth), the CPU oracle's throughput on
 a bounded sample of the same workload, and (unless --no-extras) the decode
-(T = 64) and MXFP4 (T = 4096) layers measured the same way, as extra keys.
+(T = 64) and MXFP4 (T = 4096) layers measured the same way, plus the decode
+layer at T = 1 .. 64 replayed from a HIP graph, as extra keys.
 """
 from __future__ import annotations
 
@@ -47,6 +48,10 @@ def parse():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extra decode and MXFP4 measurements")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="only the graph-replayed decode sweep (T = 1 .. 64) of the decode layer")
+    ap.add_argument("--decode-path", default="forward", choices=["forward", "gemv"],
+                    help="decode sweep through moe_forward or through the decode (GEMV) entry points (T <= 16)")
     ap.add_argument("--weight-copies", type=int, default=1,
                     help="rotate over this many copies of the weights, one per step, so that no "
                          "step finds the previous step's weights in the memory-side cache")
@@ -317,6 +322,80 @@ def measure(M, wl, args, copies=None, steps=None, warmup=None, breakdown=True, b
     return res, copies, x, lg
 
 
+def graph_replay(M, wl, copies, sets: int = 8, reps: int = 40, block_m: int = 0, path: str = "forward"):
+    """Device-side step time of the layer with the host out of the loop: one
+    HIP graph (torch.cuda.CUDAGraph) holds `sets` moe_forward calls, each on
+    its own seeded input batch (so consecutive steps route to different
+    experts and read their weights from HBM, not from the memory-side cache),
+    and is replayed `reps` times.  This is how a serving loop runs the decode
+    layer.  Returns the mean step time and the layer's fraction of HBM
+    bandwidth over the mean algorithmic bytes of the sets.  path "gemv": the
+    same layer through the decode entry points (front end, then
+    moe_decode_gemm1_swiglu and moe_decode_gemm2_combine) instead of
+    moe_forward."""
+    import numpy as np
+    import torch
+    import workloads as W
+    bm = block_m or M.pick_block_m(wl.T, wl.E, wl.top_k)
+    cfg = M.make_cfg(wl.E, wl.top_k, wl.mode, wl.H, wl.I, wl.Hp, wl.Ip, block_m=bm,
+                     swiglu_limit=wl.swiglu_limit)
+    ins = []
+    for j in range(sets):
+        wj = wl.with_(seed=wl.seed + 1000 + j)
+        ins.append((W.activations(wj, "cuda"), W.router_logits(wj, "cuda")))
+    outs = [torch.empty(wl.T, wl.H, dtype=torch.bfloat16, device="cuda") for _ in range(sets)]
+    ws = torch.empty(M.workspace_bytes(cfg, wl.T), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+
+    if path == "gemv":
+        P = wl.T * wl.top_k
+        a32 = torch.empty(P, wl.Ip, dtype=torch.float32, device="cuda")
+        aq_b, as_b = M.decode_intermediate_bytes(cfg, wl.T)
+        aq = torch.empty(aq_b, dtype=torch.uint8, device="cuda")
+        as_ = torch.empty(as_b, dtype=torch.uint8, device="cuda")
+
+    def calls():
+        for j, (x, lg) in enumerate(ins):
+            w13, s13, w2, s2 = copies[j % len(copies)]
+            if path == "gemv":
+                ids, w, _, _, _, _, xq, xs = M.moe_route_permute_quant(cfg, x, lg)
+                M.moe_decode_gemm1_swiglu(cfg, xq, xs, ids, w13, s13, a=a32)
+                M.moe_decode_gemm2_combine(cfg, a32, ids, w, w2, s2, out=outs[j], aq=aq, as_=as_)
+            else:
+                M.moe_forward(cfg, x, lg, w13, s13, w2, s2, out=outs[j], ws=ws)
+
+    with torch.cuda.stream(stream):
+        calls()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        calls()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / (reps * sets)
+    layer, active = [], []
+    for _, lg in ins:
+        ids, _ = M.moe_route_topk(lg, wl.top_k)
+        nb = algorithmic_bytes(wl, ids.cpu().numpy(), M)
+        layer.append(nb["layer"])
+        active.append(nb["active_experts"])
+    del g
+    torch.cuda.synchronize()
+    return {"T": wl.T, "path": path, "block_m": bm, "us_per_step": round(us, 2),
+            "tokens_per_s": round(wl.T / (us * 1e-6), 1),
+            "active_experts_mean": round(float(np.mean(active)), 1),
+            "layer_hbm_frac": round(float(np.mean(layer)) / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4),
+            "ksplit": [M.plan_ksplit(cfg, wl.T, 13), M.plan_ksplit(cfg, wl.T, 2)]}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -331,6 +410,17 @@ def main():
     import mxfp4_quantized_weights_amd as M
 
     torch.cuda.set_device(0)
+    if args.decode_sweep:
+        wl = W.WORKLOADS["decode_fp8"]
+        bm = M.pick_block_m(wl.T, wl.E, wl.top_k)
+        cfg = M.make_cfg(wl.E, wl.top_k, wl.mode, wl.H, wl.I, wl.Hp, wl.Ip, block_m=bm,
+                         swiglu_limit=wl.swiglu_limit)
+        copies = build_weights(M, cfg, wl, torch.device("cuda", 0), args.weight_copies)
+        ts = (1, 2, 4, 8, 16) if args.decode_path == "gemv" else (1, 2, 4, 8, 16, 32, 64)
+        for t in ts:
+            print(json.dumps({"decode_sweep_graph": graph_replay(M, wl.with_(T=t), copies, path=args.decode_path)}),
+                  flush=True)
+        return
     wl = W.WORKLOADS[args.workload]
     if args.T:
         wl = wl.with_(T=args.T)
@@ -361,6 +451,10 @@ def main():
         d, _, _, _ = measure(M, W.WORKLOADS["decode_fp8"], args, copies=copies, breakdown=not args.no_breakdown,
                              block_m=0)
         extras["decode_fp8"] = d
+        # decode micro-batches, replayed from a HIP graph as a serving loop
+        # runs them (same weights)
+        extras["decode_sweep_graph"] = [graph_replay(M, W.WORKLOADS["decode_fp8"].with_(T=t), copies)
+                                        for t in (1, 2, 4, 8, 16, 32, 64)]
         del copies
         torch.cuda.empty_cache()
         m, _, _, _ = measure(M, W.WORKLOADS["prefill_mxfp4"], args, breakdown=not args.no_breakdown, block_m=0)

@@ -315,6 +315,55 @@ moe_status_t moe_grouped_gemm2_combine_splitk(const moe_cfg_t* cfg, int32_t T, c
                                               void* out_bf16, int64_t ld_out, int32_t ksplit,
                                               void* ws, size_t ws_bytes, void* stream);
 
+/* Decode micro-batches (FreeToken PR #270 "glm5_next: support GLM-5.3-Flash
+ * (hybrid KDA + DSA, mHC, NVFP4 expert offload)", Tuned companion: an
+ * M-tiled FP8 GEMV for decode micro-batches).  For at most 16 tokens of a
+ * block-FP8 layer (fp32 or UE8M0 scales) every active expert multiplies at
+ * most 16 rows, so two GEMV-shaped kernels can replace the grouped GEMMs:
+ * GEMM1 + clamped SwiGLU over (expert, 32 intermediate columns) items with K
+ * split across the waves of a workgroup, then the re-quantisation of the
+ * intermediate, GEMM2 over 16 output columns of every expert and the
+ * slot-ordered combine in one kernel (no permutation, no per-pair GEMM2 rows
+ * in HBM; above 4 tokens one small launch re-quantises the intermediate
+ * once, first).  moe_forward does not use them: on the MI355X the K-split
+ * grouped GEMMs, whose load ring runs through LDS, stream these layers'
+ * weights faster at every T <= 16.
+ *
+ * moe_decode_supported: 1 if the decode entry points take T tokens of this
+ * layer (quant mode FP8_BLOCK or FP8_UE8M0, TILED_V2, 1 <= T <= 16,
+ * T*k <= 128, hidden_padded 1024, 2048 or 4096, inter_padded 128, 256, 512
+ * or 1024), else 0 (also for an invalid configuration).
+ *
+ * moe_decode_gemm1_swiglu: for every pair f = t*k + j with topk_ids[f] in
+ * [0, E): a[f, c] = silu(min(g, L)) * clamp(u, -L, L) for c < Ip, with g
+ * and u the gate and up rows c and Ip + c of expert topk_ids[f] times
+ * dequantised x row t (fp32 promotion per 128-wide K block; the steps of
+ * moe_grouped_gemm1_swiglu before its re-quantisation).  xq, xs: quantised x
+ * as moe_quant_act writes it ([T, Hp] codes; fp32 [T, Hp/128] or UE8M0
+ * [T, row of whole dwords] scales); topk_ids: int32 [T, k], each token's ids
+ * distinct (as routing gives them; a repeated id counts once); a: f32
+ * [T*k, Ip] (rows of other pairs are not written).  xq and a 16-byte
+ * aligned, xs and topk_ids 4-byte aligned, else MOE_ERR_ALIGN; a shape
+ * outside moe_decode_supported: MOE_ERR_UNSUPPORTED.
+ *
+ * moe_decode_gemm2_combine: re-quantises each pair's row of a in 1x128 groups
+ * (e4m3 codes with an fp32 scale amax/448, or a UE8M0 scale: the arithmetic
+ * of moe_grouped_gemm1_swiglu's epilogue), multiplies it with w2 of the
+ * pair's expert and writes out[t, :H] = sum over slots j in order of
+ * topk_weights[t*k + j] * y[t*k + j] in bf16 (pairs with an id outside
+ * [0, E) add nothing).  The intermediate is stored in pair order: aq u8
+ * [T*k, Ip], as f32 [T*k, Ip/128] or UE8M0 bytes [T*k, row of whole dwords]
+ * (aq 8-byte and as 4-byte aligned; for more than 4 tokens it is written by
+ * a re-quantisation launch first and read back by GEMM2).  a 16-byte
+ * aligned.  Same errors as above; ld_out < hidden: MOE_ERR_SHAPE. */
+int32_t moe_decode_supported(const moe_cfg_t* cfg, int32_t T);
+moe_status_t moe_decode_gemm1_swiglu(const moe_cfg_t* cfg, int32_t T, const void* xq, const void* xs,
+                                     const int32_t* topk_ids, const void* w13, const void* w13_scale, float* a,
+                                     void* stream);
+moe_status_t moe_decode_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const float* a, const int32_t* topk_ids,
+                                      const float* topk_weights, const void* w2, const void* w2_scale,
+                                      void* out_bf16, int64_t ld_out, void* aq, void* as, void* stream);
+
 /* The whole layer: route, permute, quantise x, GEMM1+SwiGLU, GEMM2+combine,
  * all on `stream` with no host synchronisation.  x: bf16 [T, ld_x] (H valid
  * columns); router_logits f32 [T, E]; weights TILED_V2; out bf16 [T, ld_out].

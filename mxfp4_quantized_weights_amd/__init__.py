@@ -98,6 +98,9 @@ _SIGS = {
                                                         _I32, _P, _SZ, _P]),
     "moe_forward_noalloc": (ctypes.c_int, [_CFGP, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _I64, _P]),
     "moe_diag_mfma_tile": (ctypes.c_int, [_I32, _P, _P, _P, _P]),
+    "moe_decode_supported": (_I32, [_CFGP, _I32]),
+    "moe_decode_gemm1_swiglu": (ctypes.c_int, [_CFGP, _I32, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_decode_gemm2_combine": (ctypes.c_int, [_CFGP, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -361,6 +364,54 @@ def moe_grouped_gemm2_combine(cfg: MoeCfg, T: int, aq, as_, sorted_ids, block_ex
     else:
         _check(_lib.moe_grouped_gemm2_combine_splitk(*args, ksplit, ws.data_ptr(), wsb, _stream(stream)),
                "moe_grouped_gemm2_combine_splitk")
+    return out
+
+
+def decode_intermediate_bytes(cfg: MoeCfg, T: int):
+    """Sizes in bytes of the decode path's intermediate codes and scales
+    (pair order: T*k rows of Ip codes; fp32 per 128 or UE8M0 bytes in rows of
+    whole dwords)."""
+    rows, ip = T * cfg.top_k, cfg.pad.inter_padded
+    if cfg.quant_mode == MOE_QUANT_FP8_UE8M0:
+        return rows * ip, rows * ((ip // 128 + 3) // 4 * 4)
+    return rows * ip, rows * (ip // 128) * 4
+
+
+def decode_supported(cfg: MoeCfg, T: int) -> bool:
+    """Whether moe_forward runs the decode (M-tiled GEMV) kernels for T tokens."""
+    return bool(_lib.moe_decode_supported(ctypes.byref(cfg), T))
+
+
+def moe_decode_gemm1_swiglu(cfg: MoeCfg, xq, xs, topk_ids, w13, s13, a: torch.Tensor | None = None, stream=None):
+    """Decode GEMM1 + clamped SwiGLU -> a float32 [T*k, Ip] (pair order)."""
+    T = topk_ids.shape[0]
+    if a is None:
+        a = torch.zeros(T * cfg.top_k, cfg.pad.inter_padded, dtype=torch.float32, device=topk_ids.device)
+    _check(_lib.moe_decode_gemm1_swiglu(ctypes.byref(cfg), T, _dev(xq, None, "xq"), _dev(xs, None, "xs"),
+                                        _dev(topk_ids, torch.int32, "topk_ids"), _dev(w13, None, "w13"),
+                                        _dev(s13, None, "w13_scale"), _dev(a, torch.float32, "a"),
+                                        _stream(stream)), "moe_decode_gemm1_swiglu")
+    return a
+
+
+def moe_decode_gemm2_combine(cfg: MoeCfg, a, topk_ids, topk_w, w2, s2, out: torch.Tensor | None = None,
+                             aq: torch.Tensor | None = None, as_: torch.Tensor | None = None, stream=None):
+    """Decode re-quantisation + GEMM2 + combine -> out bf16 [T, H]; aq / as_
+    (pair order; allocated when not given) receive the intermediate codes
+    and scales."""
+    T = topk_ids.shape[0]
+    if out is None:
+        out = torch.empty(T, cfg.pad.hidden, dtype=torch.bfloat16, device=a.device)
+    if aq is None or as_ is None:
+        aq_b, as_b = decode_intermediate_bytes(cfg, T)
+        aq = torch.empty(aq_b, dtype=torch.uint8, device=a.device)
+        as_ = torch.empty(as_b, dtype=torch.uint8, device=a.device)
+    _check(_lib.moe_decode_gemm2_combine(ctypes.byref(cfg), T, _dev(a, torch.float32, "a"),
+                                         _dev(topk_ids, torch.int32, "topk_ids"),
+                                         _dev(topk_w, torch.float32, "topk_w"), _dev(w2, None, "w2"),
+                                         _dev(s2, None, "w2_scale"), _dev(out, torch.bfloat16, "out", contiguous=False),
+                                         out.stride(0), aq.data_ptr(), as_.data_ptr(), _stream(stream)),
+           "moe_decode_gemm2_combine")
     return out
 
 

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "quant.hip", "gemm.hip", "diag.hip"]
+SOURCES = ["api.hip", "route.hip", "quant.hip", "gemm.hip", "diag.hip", "decode.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the generated code.

@@ -314,6 +314,23 @@ hipError_t gemm2_and_combine(const moe_cfg_t* c, int32_t T, moe::GemmArgs a, int
   return hipSuccess;
 }
 
+// Whether the decode kernels (decode.hip) take T tokens of this layer.
+bool decode_takes(const moe_cfg_t* c, int32_t T) {
+  return moe::decode_ok(c->quant_mode, T, c->num_experts, c->top_k, c->pad.hidden_padded, c->pad.inter_padded);
+}
+
+moe::DecodeArgs decode_args(const moe_cfg_t* c, int32_t T) {
+  moe::DecodeArgs d{};
+  d.T = T;
+  d.E = c->num_experts;
+  d.k = c->top_k;
+  d.H = c->pad.hidden;
+  d.Hp = c->pad.hidden_padded;
+  d.Ip = c->pad.inter_padded;
+  d.limit = c->swiglu_limit;
+  return d;
+}
+
 // The whole layer with its scratch in ws (validated by the caller).
 moe_status_t forward_impl(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, int64_t ld_x,
                           const float* router_logits, const void* w13, const void* w13_scale, const void* w2,
@@ -597,6 +614,57 @@ moe_status_t moe_grouped_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const vo
   if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
   return moe_grouped_gemm2_combine_splitk(cfg, T, aq, as, sorted_ids, block_expert, num_post_padded, w2, w2_scale,
                                           topk_w, out_bf16, ld_out, plan_ksplit(cfg, T, 2), ws, ws_bytes, stream);
+}
+
+int32_t moe_decode_supported(const moe_cfg_t* cfg, int32_t T) {
+  if (check_cfg(cfg) != MOE_OK || check_tokens(cfg, T) != MOE_OK || check_layout(cfg) != MOE_OK) return 0;
+  return decode_takes(cfg, T) ? 1 : 0;
+}
+
+moe_status_t moe_decode_gemm1_swiglu(const moe_cfg_t* cfg, int32_t T, const void* xq, const void* xs,
+                                     const int32_t* topk_ids, const void* w13, const void* w13_scale, float* a,
+                                     void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
+  if ((st = check_layout(cfg)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!decode_takes(cfg, T)) return MOE_ERR_UNSUPPORTED;
+  if (!xq || !xs || !topk_ids || !w13 || !w13_scale || !a) return MOE_ERR_NULL;
+  if ((uintptr_t)xq % 16 || (uintptr_t)xs % 4 || (uintptr_t)topk_ids % 4 || (uintptr_t)a % 16) return MOE_ERR_ALIGN;
+  moe::DecodeArgs d = decode_args(cfg, T);
+  d.ids = (int32_t*)topk_ids;  // read only
+  d.xq = (const uint8_t*)xq;
+  d.xs = xs;
+  d.w13 = (const uint8_t*)w13;
+  d.s13 = (const float*)w13_scale;
+  d.a = a;
+  return hip_status(moe::launch_decode_gemm1(cfg->quant_mode, d, as_stream(stream)));
+}
+
+moe_status_t moe_decode_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const float* a, const int32_t* topk_ids,
+                                      const float* topk_weights, const void* w2, const void* w2_scale,
+                                      void* out_bf16, int64_t ld_out, void* aq, void* as, void* stream) {
+  moe_status_t st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_tokens(cfg, T)) != MOE_OK) return st;
+  if ((st = check_layout(cfg)) != MOE_OK) return st;
+  if (ld_out < cfg->pad.hidden) return MOE_ERR_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!decode_takes(cfg, T)) return MOE_ERR_UNSUPPORTED;
+  if (!a || !topk_ids || !topk_weights || !w2 || !w2_scale || !out_bf16 || !aq || !as) return MOE_ERR_NULL;
+  if ((uintptr_t)a % 16 || (uintptr_t)aq % 8 || (uintptr_t)as % 4 || (uintptr_t)out_bf16 % 2) return MOE_ERR_ALIGN;
+  moe::DecodeArgs d = decode_args(cfg, T);
+  d.ids = (int32_t*)topk_ids;  // read only
+  d.topk_w = (float*)topk_weights;
+  d.a = (float*)a;
+  d.w2 = (const uint8_t*)w2;
+  d.s2 = (const float*)w2_scale;
+  d.out = (uint16_t*)out_bf16;
+  d.ld_out = ld_out;
+  d.aq = (uint8_t*)aq;
+  d.as = as;
+  return hip_status(moe::launch_decode_gemm2(cfg->quant_mode, d, as_stream(stream)));
 }
 
 int32_t moe_plan_ksplit(const moe_cfg_t* cfg, int32_t T, int32_t which) {

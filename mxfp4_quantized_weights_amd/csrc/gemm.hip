@@ -50,18 +50,6 @@ constexpr bool e8_tokens(int mode) { return mode == kGemmE8F16 || mode == kGemmE
 // FP8 operands widened to f16 for the f16 MFMA.
 constexpr bool f16_path(int mode) { return mode == kGemmFp8F16 || mode == kGemmE8F16; }
 
-// The lane's 32 FP8 bytes as four f16 operands: step st holds bytes
-// 8st..8st+7, i.e. K = 32*(lane/16) + 8st + i for both A and B.
-__device__ __forceinline__ void widen_fp8(const v8i& w, v8h (&h)[4]) {
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const uint32_t d0 = (uint32_t)w[2 * st], d1 = (uint32_t)w[2 * st + 1];
-    const uint4 v = make_uint4(e4m3x2_to_f16x2<false>(d0), e4m3x2_to_f16x2<true>(d0),
-                               e4m3x2_to_f16x2<false>(d1), e4m3x2_to_f16x2<true>(d1));
-    h[st] = __builtin_bit_cast(v8h, v);
-  }
-}
-
 // ===========================================================================
 // The load ring and the per-K-block compute.
 //
@@ -390,7 +378,10 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
       // tiles before its first use, so the MFMA and VALU pipes overlap.
       // raw fragments are read from LDS two tiles before they are widened.
       // All 4 token tiles are computed even when some are padding: branching
-      // inside this schedule costs more than the skipped tiles save.
+      // inside this schedule costs more than the skipped tiles save, and a
+      // second, partial schedule beside it does not fit the register budget.
+      // A wave whose token tiles are all padding skips the K block.
+      if (mv == 0) return;
       v8i wraw[4], traw[4];
       wraw[0] = lds_frag32(wl + tiles[0] * R::TILE);
       wraw[1] = lds_frag32(wl + tiles[1] * R::TILE);

@@ -220,6 +220,18 @@ __device__ __forceinline__ v4f mfma_f16(const v8h& a, const v8h& b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// The lane's 32 FP8 bytes as four f16 operands: step st holds bytes
+// 8st..8st+7, i.e. K = 32*(lane/16) + 8st + i for both A and B.
+__device__ __forceinline__ void widen_fp8(const v8i& w, v8h (&h)[4]) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const uint32_t d0 = (uint32_t)w[2 * st], d1 = (uint32_t)w[2 * st + 1];
+    const uint4 v = make_uint4(e4m3x2_to_f16x2<false>(d0), e4m3x2_to_f16x2<true>(d0),
+                               e4m3x2_to_f16x2<false>(d1), e4m3x2_to_f16x2<true>(d1));
+    h[st] = __builtin_bit_cast(v8h, v);
+  }
+}
+
 // 16x16x128 FP4 (E2M1 x E2M1) MFMA with per-lane E8M0 scales: lane l's scale
 // applies to its own 32 K-values (its A row / B column, K group l/16).  The A
 // scale is byte 0 of sa; the B scale is byte OPB of sb.

@@ -205,4 +205,42 @@ hipError_t launch_gemm2(int mode, int block_m, int nb, const GemmArgs& a, hipStr
 hipError_t launch_combine(const uint8_t* y, int64_t yexp, int T, int k, int c0, int cols, int64_t ldy, int nplanes,
                           int64_t plane, uint16_t* out, int64_t ld_out, hipStream_t s);
 
+// Decode micro-batches (T <= kDecodeMaxT tokens, block FP8 with fp32 or
+// UE8M0 scales): M-tiled GEMV kernels, see decode.hip.
+//   decode_gemm1: GEMM1 and the clamped SwiGLU from the routing and the
+//     quantised x, a fp32 [T*k][Ip] in pair order f = t*k + j.
+//   decode_gemm2: re-quantisation of a (1x128), GEMM2 and the weighted
+//     combine into out; the intermediate codes and scales in pair order go
+//     to aq [T*k][Ip], as [T*k][Ip/128] fp32 or [T*k][e8_scale_ld(Ip)]
+//     UE8M0 bytes.  Up to kDecodeSmallT tokens every GEMM2 workgroup
+//     re-quantises a itself (and workgroup 0 stores aq / as); above, one
+//     launch re-quantises it once, into aq / as, before GEMM2.
+constexpr int kDecodeMaxT = 16;
+constexpr int kDecodeMaxPairs = 128;
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeSmallT = 4;
+struct DecodeArgs {
+  int32_t T, E, k, H, Hp, Ip;
+  float limit;
+  int32_t* ids;           // routing [T][k]
+  float* topk_w;          // routing weights [T][k]
+  const uint8_t* xq;      // quantised x [T][Hp] and its scales
+  const void* xs;
+  const uint8_t* w13;     // TILED_V2
+  const float* s13;
+  float* a;               // clamped SwiGLU output, fp32 [T*k][Ip]
+  const uint8_t* w2;      // TILED_V2
+  const float* s2;
+  uint16_t* out;          // bf16 [T][ld_out]
+  int64_t ld_out;
+  uint8_t* aq;            // the intermediate in pair order (see above)
+  void* as;
+};
+// Shapes the decode kernels take: quant mode block FP8, 1 <= T <= 16,
+// T*k <= 128, E <= 1024, Hp in {1024, 2048, 4096}, Ip in {128, 256, 512,
+// 1024}.
+bool decode_ok(int mode, int T, int E, int k, int Hp, int Ip);
+hipError_t launch_decode_gemm1(int mode, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_gemm2(int mode, const DecodeArgs& a, hipStream_t s);
+
 }  // namespace moe

@@ -43,12 +43,69 @@ __device__ __forceinline__ void load8(const void* in, int64_t row, int64_t ld, i
   }
 }
 
+// One 128-column unit (16 lanes, 8 elements per lane) of the row
+// quantisers, from its loaded values: FP8 (one group), UE8M0 FP8 (one
+// group) or MX (four groups of 4 lanes).  Stores when `live`.
+template <int MODE>
+__device__ __forceinline__ void quant_unit(const float (&v)[8], bool live, int64_t row, int g, int col, int units,
+                                           int cols_padded, uint8_t* __restrict__ q, void* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+  if constexpr (MODE == kQuantFp8) {
+    a = group_max<16>(a);
+    uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const float s = (a > 0.0f) ? a / kE4M3Max : 0.0f;
+    if (a > 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = fp8_quant(v[i], s);
+    }
+    if (live) {
+      *(uint2*)(q + row * (int64_t)cols_padded + col) =
+          make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+      if ((lane & 15) == 0) ((float*)scales)[row * units + g] = s;
+    }
+  } else if constexpr (MODE == kQuantFp8E8) {
+    a = group_max<16>(a);
+    const uint32_t b = ue8m0_byte(a);
+    const float inv = e8m0_inverse(b);
+    uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (a > 0.0f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[i] = fp8e8_quant(v[i], inv);
+    }
+    if (live) {
+      *(uint2*)(q + row * (int64_t)cols_padded + col) =
+          make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
+      const int64_t lds = (units + 3) / 4 * 4;
+      uint8_t* srow = (uint8_t*)scales + row * lds;
+      if ((lane & 15) == 0) srow[g] = (uint8_t)b;
+      if ((lane & 15) == 1 && g == units - 1) {
+        for (int i = units; i < lds; ++i) srow[i] = 0;
+      }
+    }
+  } else {
+    a = group_max<4>(a);
+    const uint32_t b = e8m0_byte(a);
+    const float inv = e8m0_inverse(b);
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= mx_quant(v[i], inv) << (4 * i);
+    if (live) {
+      *(uint32_t*)(q + row * (int64_t)(cols_padded / 2) + col / 2) = w;
+      if ((lane & 3) == 0) ((uint8_t*)scales)[row * (int64_t)(cols_padded / 32) + col / 32] = (uint8_t)b;
+    }
+  }
+}
+
 // A wave quantises four 128-column units (16 lanes each, 8 elements per
 // lane); a unit is one FP8 group or four MX groups of 4 lanes.  Wave `gw` of
 // `nw` quantising waves takes units 4*gw .. +3, then every 4*nw-th.
 // UE8M0 scale rows are e8_scale_ld(cols_padded) bytes long; the bytes past
-// the last group are written as zero.
-template <bool BF16, bool VEC, int MODE>
+// the last group are written as zero.  U: units per lane loaded before any
+// is quantised (U loads in flight; the results do not depend on U).
+template <bool BF16, bool VEC, int MODE, int U = 1>
 __device__ __forceinline__ void quant_rows_body(const void* __restrict__ in, int64_t rows, int cols, int64_t ld_in,
                                                 int cols_padded, uint8_t* __restrict__ q, void* __restrict__ scales,
                                                 int64_t gw, int64_t nw) {
@@ -56,64 +113,28 @@ __device__ __forceinline__ void quant_rows_body(const void* __restrict__ in, int
   const int units = cols_padded / 128;
   const int64_t total = rows * units;
   const int64_t stride = nw * 4;
-  for (int64_t u = gw * 4 + (lane >> 4); u - (lane >> 4) < total; u += stride) {
-    const bool live = u < total;
-    const int64_t row = live ? u / units : 0;
-    const int g = live ? (int)(u % units) : 0;
-    const int col = g * 128 + (lane & 15) * 8;
-    float v[8];
-    if (live) {
-      load8<BF16, VEC>(in, row, ld_in, col, cols, v);
-    } else {
+  for (int64_t u0 = gw * 4 + (lane >> 4); u0 - (lane >> 4) < total; u0 += stride * U) {
+    float v[U][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    for (int r = 0; r < U; ++r) {
+      const int64_t u = u0 + stride * r;
+      if (u < total) {
+        load8<BF16, VEC>(in, u / units, ld_in, (int)(u % units) * 128 + (lane & 15) * 8, cols, v[r]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[r][i] = 0.0f;
+      }
     }
-    float a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
-    if constexpr (MODE == kQuantFp8) {
-      a = group_max<16>(a);
-      uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      const float s = (a > 0.0f) ? a / kE4M3Max : 0.0f;
-      if (a > 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = fp8_quant(v[i], s);
-      }
-      if (live) {
-        *(uint2*)(q + row * (int64_t)cols_padded + col) =
-            make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
-        if ((lane & 15) == 0) ((float*)scales)[row * units + g] = s;
-      }
-    } else if constexpr (MODE == kQuantFp8E8) {
-      a = group_max<16>(a);
-      const uint32_t b = ue8m0_byte(a);
-      const float inv = e8m0_inverse(b);
-      uint32_t c[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (a > 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = fp8e8_quant(v[i], inv);
-      }
-      if (live) {
-        *(uint2*)(q + row * (int64_t)cols_padded + col) =
-            make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24), c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24));
-        const int64_t lds = (units + 3) / 4 * 4;
-        uint8_t* srow = (uint8_t*)scales + row * lds;
-        if ((lane & 15) == 0) srow[g] = (uint8_t)b;
-        if ((lane & 15) == 1 && g == units - 1) {
-          for (int i = units; i < lds; ++i) srow[i] = 0;
-        }
-      }
-    } else {
-      a = group_max<4>(a);
-      const uint32_t b = e8m0_byte(a);
-      const float inv = e8m0_inverse(b);
-      uint32_t w = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w |= mx_quant(v[i], inv) << (4 * i);
-      if (live) {
-        *(uint32_t*)(q + row * (int64_t)(cols_padded / 2) + col / 2) = w;
-        if ((lane & 3) == 0) ((uint8_t*)scales)[row * (int64_t)(cols_padded / 32) + col / 32] = (uint8_t)b;
-      }
+    for (int r = 0; r < U; ++r) {
+      const int64_t u = u0 + stride * r;
+      // a pass whose units all lie past the end does nothing (its lanes
+      // would only exchange zeros)
+      if (u - (lane >> 4) >= total) break;
+      const bool live = u < total;
+      const int64_t row = live ? u / units : 0;
+      const int g = live ? (int)(u % units) : 0;
+      quant_unit<MODE>(v[r], live, row, g, g * 128 + (lane & 15) * 8, units, cols_padded, q, scales);
     }
   }
 }

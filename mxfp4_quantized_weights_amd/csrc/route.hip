@@ -10,88 +10,9 @@
 #include "moe_device.h"
 #include "moe_internal.h"
 #include "moe_quant_rows.h"
+#include "moe_route.h"
 
 namespace moe {
-
-// (value, id) is better than (ov, oid): larger value, ties to the lower id.
-__device__ __forceinline__ bool better(float ov, int oid, float v, int id) {
-  return ov > v || (ov == v && oid < id);
-}
-
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void argmax_step(float& v, int& id) {
-  // lanes outside ROW_MASK keep their own value (old = src), which is a no-op
-  float ov = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
-  int oid = __builtin_amdgcn_update_dpp(id, id, CTRL, ROW_MASK, 0xF, false);
-  if (better(ov, oid, v, id)) {
-    v = ov;
-    id = oid;
-  }
-}
-
-// Wave-wide argmax with DPP row operations: quad swaps (xor 1, xor 2), half
-// and full row mirrors make every 16-lane row uniform, row broadcasts of
-// lanes 15 and 31 fold the rows into lane 63, which is read back uniformly.
-__device__ __forceinline__ void wave_argmax(float& v, int& id) {
-  argmax_step<0xB1, 0xF>(v, id);   // quad_perm [1,0,3,2]
-  argmax_step<0x4E, 0xF>(v, id);   // quad_perm [2,3,0,1]
-  argmax_step<0x141, 0xF>(v, id);  // row_half_mirror
-  argmax_step<0x140, 0xF>(v, id);  // row_mirror
-  argmax_step<0x142, 0xA>(v, id);  // row_bcast:15 into rows 1, 3
-  argmax_step<0x143, 0xC>(v, id);  // row_bcast:31 into rows 2, 3
-  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
-  id = __builtin_amdgcn_readlane(id, 63);
-}
-
-// Top-k of one token by one wave.  Each lane holds the logits of experts
-// lane + 64*i; k rounds of a wave-wide argmax pick the experts in slot order.
-// NaN logits compare as -inf.  The softmax denominator is summed in slot
-// order.  Lane j < k writes slot j to ids[j], w[j] and, if given, ids2[j].
-template <int VPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int32_t* ids, float* w,
-                                            int32_t* ids2) {
-  const int lane = threadIdx.x & 63;
-  float v[VPL];
-  uint32_t avail = 0;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    int e = lane + 64 * i;
-    float x = (e < E) ? row[e] : -INFINITY;
-    v[i] = (x != x) ? -INFINITY : x;
-    if (e < E) avail |= 1u << i;
-  }
-  float my_v = -INFINITY;
-  int my_e = 0;
-  float lmax = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      int e = lane + 64 * i;
-      if (((avail >> i) & 1u) && better(v[i], e, bv, be)) {
-        bv = v[i];
-        be = e;
-      }
-    }
-    wave_argmax(bv, be);
-    if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
-    if (j == 0) lmax = bv;
-    if (lane == j) {
-      my_v = bv;
-      my_e = be;
-    }
-  }
-  const float d = (my_v == lmax) ? 0.0f : (my_v - lmax);
-  const float ex = (lane < k) ? expf(d) : 0.0f;
-  float sum = 0.0f;
-  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
-  if (lane < k) {
-    ids[lane] = my_e;
-    w[lane] = ex / sum;
-    if (ids2) ids2[lane] = my_e;
-  }
-}
 
 // One wave per token.
 template <int VPL>

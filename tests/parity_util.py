@@ -144,10 +144,9 @@ def gpu_intermediate_rows(mode: str, Ip: int, aq, as_, sid, npp, num_pairs: int,
     ``aq``/``as_`` are GEMM1's outputs (rows by sorted position), ``sid`` the
     sorted pair ids and ``pairs`` a dict {(sample index, slot): flat pair f}.
     Pad rows (sorted ids >= P) below num_post_padded must be all zero.
+    ``sid`` None: the rows are in pair order (the decode kernels' layout).
     Returns {(sample index, slot): (element codes uint8 [Ip], scale bytes
     [groups] as stored: float32 bits or E8M0)}."""
-    sid_h = sid.cpu().numpy()
-    nrows = int(npp.item()) if torch.is_tensor(npp) else int(npp)
     row_bytes = Ip // 2 if mode == "mxfp4" else Ip
     aq_h = aq.cpu().numpy().reshape(-1)
     as_h = as_.cpu().numpy().reshape(-1)
@@ -159,11 +158,16 @@ def gpu_intermediate_rows(mode: str, Ip: int, aq, as_, sid, npp, num_pairs: int,
         as_h = as_h[:rows_total * M_e8_ld(Ip)].reshape(rows_total, M_e8_ld(Ip))[:, :Ip // 128]
     else:
         as_h = as_h[:rows_total * (Ip // 32)].reshape(rows_total, Ip // 32)
-    live = sid_h[:nrows]
-    pad = live >= num_pairs
-    assert np.all(aq_h[:nrows][pad] == 0) and np.all(as_h[:nrows][pad] == 0), "pad rows are not zero"
-    real = np.nonzero(~pad)[0]
-    row_of = dict(zip(live[real].tolist(), real.tolist()))
+    if sid is None:
+        row_of = {f: f for f in range(num_pairs)}
+    else:
+        sid_h = sid.cpu().numpy()
+        nrows = int(npp.item()) if torch.is_tensor(npp) else int(npp)
+        live = sid_h[:nrows]
+        pad = live >= num_pairs
+        assert np.all(aq_h[:nrows][pad] == 0) and np.all(as_h[:nrows][pad] == 0), "pad rows are not zero"
+        real = np.nonzero(~pad)[0]
+        row_of = dict(zip(live[real].tolist(), real.tolist()))
     out = {}
     for key, f in pairs.items():
         r = row_of[f]
@@ -359,6 +363,20 @@ def oracle_stages(wl: W.Workload, x: torch.Tensor, lg: torch.Tensor, Q: O.QuantW
     inputs, for the sample tokens (default all)."""
     return O.moe_forward(x.float().cpu().numpy(), lg.cpu().numpy(), Q, wl.top_k, wl.swiglu_limit, wl.H, wl.I,
                          tokens=tokens, return_stages=True)
+
+
+def decode_chain(M, cfg, x_dev, lg_dev, ew):
+    """The decode entry points on the front end's routing and quantised x:
+    moe_decode_gemm1_swiglu, then moe_decode_gemm2_combine.  Returns a dict
+    with the routing (ids, w), the fp32 SwiGLU rows a32, the intermediate
+    in pair order (aq, as_; sid None) and the output."""
+    ids, w, sid, bexp, offs, npp, xq, xs = M.moe_route_permute_quant(cfg, x_dev, lg_dev)
+    a32 = M.moe_decode_gemm1_swiglu(cfg, xq, xs, ids, ew.w13, ew.w13_scale)
+    aq_b, as_b = M.decode_intermediate_bytes(cfg, x_dev.shape[0])
+    aq = torch.zeros(aq_b, dtype=torch.uint8, device=a32.device)
+    as_ = torch.zeros(as_b, dtype=torch.uint8, device=a32.device)
+    out = M.moe_decode_gemm2_combine(cfg, a32, ids, w, ew.w2, ew.w2_scale, aq=aq, as_=as_)
+    return dict(ids=ids, w=w, a32=a32, sid=None, npp=None, aq=aq, as_=as_, out=out, xq=xq, xs=xs)
 
 
 def check_forward(M, wl: W.Workload, cfg, ew, x_dev, lg_dev, out, Q, tokens=None, what: str = ""):
