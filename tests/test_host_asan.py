@@ -7,7 +7,7 @@ which a child Python
 process loads under the ASan runtime and drives through every entry point's
 host-side paths: valid and invalid configurations (fuzzed fields, extreme
 sizes, NaN / infinite limits, unknown modes and layouts), NULL pointers,
-short workspaces and oversized batches.  Every such call returns before
+misaligned pointers, short workspaces and oversized batches.  Every such call returns before
 anything would be launched, so no GPU is needed.  ASan aborts the child on
 any out-of-bounds access or use of freed memory.  Host only: this test never
 runs on a GPU machine's test pass.
@@ -86,6 +86,13 @@ DRIVER = textwrap.dedent(r'''
         lib.moe_route_permute_quant(ctypes.byref(c), T, None, FAKE, I64(h), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                     FAKE, None)
         lib.moe_preshuffle_weights(ctypes.byref(c), rng.choice([13, 2, 0]), None, FAKE, FAKE, FAKE, None)
+        lib.moe_decode_supported(ctypes.byref(c), T)
+        lib.moe_decode_gemm1_swiglu(ctypes.byref(c), T, FAKE, FAKE, None, FAKE, FAKE, FAKE, None)
+        lib.moe_decode_gemm1_swiglu(ctypes.byref(c), T, P((1 << 40) + 8), FAKE, FAKE, FAKE, FAKE, FAKE, None)
+        lib.moe_decode_gemm2_combine(ctypes.byref(c), T, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, I64(h), None, FAKE,
+                                     None)
+        lib.moe_decode_gemm2_combine(ctypes.byref(c), T, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, I64(h), FAKE, FAKE,
+                                     None) if T == 0 or lib.moe_decode_supported(ctypes.byref(c), T) == 0 else None
         E, k = c.num_experts, c.top_k
         lib.moe_route_topk(None, T, E, k, FAKE, FAKE, None)
         lib.moe_permute_align(FAKE, T, k, E, c.block_m, FAKE, FAKE, None, FAKE, None)
@@ -105,7 +112,7 @@ def test_host_code_under_asan(tmp_path):
     flags = ["--offload-arch=gfx950", "-O1", "-std=c++20", "-fPIC", "-Xarch_host", "-g",
              "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-    objs = [str(tmp_path / f"{src}.o") for src in ("api", "route", "quant", "gemm", "diag")]
+    objs = [str(tmp_path / f"{src}.o") for src in ("api", "route", "quant", "gemm", "diag", "decode")]
     procs = [subprocess.Popen([HIPCC, *flags, "-c", os.path.join(CSRC, os.path.basename(o)[:-2] + ".hip"), "-o", o],
                               stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True) for o in objs]
     for p in procs:
