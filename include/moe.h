@@ -271,7 +271,7 @@ moe_status_t moe_grouped_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const vo
  *          SwiGLU and the re-quantisation as above;
  *   GEMM2: piece i stores its weighted rows for its K range in a plane of
  *          its own; the combine adds, plane by plane, the slots in order.
- * ksplit = -2, -4 or -8 (GEMM1 only, block_m 16 or 32; a "tail split"): the
+ * ksplit = -2, -4 or -8 (GEMM1 only, -8 at block_m 16 or 32 only; a "tail split"): the
  *   items that fill whole rounds of one workgroup per compute unit run
  *   unsplit with the fused epilogue, and only the remaining items are cut
  *   into -ksplit pieces and finished by the second kernel, so the last
@@ -281,14 +281,16 @@ moe_status_t moe_grouped_gemm2_combine(const moe_cfg_t* cfg, int32_t T, const vo
  * moe_plan_ksplit: the split moe_forward and moe_grouped_gemm2_combine use for
  * GEMM `which` (13: gate/up, 2: down) at T tokens on the current device
  * (1, 2, 4 or 8 when items would leave compute units idle, at most 1024
- * pairs; else for GEMM1 at block_m 16/32 the tail split with the most pieces
- * the scale layout allows; else 1); -1 for invalid arguments.
+ * pairs; else for GEMM1, when the last round of items is expected to be
+ * mostly idle, the tail split with the most pieces the scale layout allows,
+ * at most 4 at block_m 64 and 128, where MXFP4 plans none; else 1); -1 for
+ * invalid arguments.
  * moe_splitk_bytes: scratch in bytes that the explicit-split entry points need
  * for that ksplit (0 for GEMM1 without a split; 0 also if the split is not
  * usable: |ksplit| must be 1, 2, 4 or 8 and divide K/128 into pieces of at
  * least 4 K blocks, multiples of 4 for MXFP4 and FP8_UE8M0; a positive split
  * at most 1024 pairs, and for GEMM2 the y rows must fit one chunk; a tail
- * split GEMM1 at block_m 16 or 32 only). */
+ * split GEMM1 only, -8 at block_m 16 or 32 only). */
 int32_t moe_plan_ksplit(const moe_cfg_t* cfg, int32_t T, int32_t which);
 size_t moe_splitk_bytes(const moe_cfg_t* cfg, int32_t T, int32_t which, int32_t ksplit);
 

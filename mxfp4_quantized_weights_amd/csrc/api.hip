@@ -90,10 +90,12 @@ int gemm_n_tiles(const moe_cfg_t* c, int which) {
 }
 
 // Tail split of GEMM1 (ksplit -2, -4 or -8): only the items past the grid's
-// whole rounds are cut into -ksplit pieces; block_m 16 or 32 (the partial
-// sums of a leftover item are block_m rows of 256 floats per piece).
+// whole rounds are cut into -ksplit pieces (the partial sums of a leftover
+// item are block_m rows of 256 floats per piece); at block_m 64 and 128 at
+// most 4 pieces, which bounds those partial sums.
+constexpr int kTailMaxWide = 4;
 bool tail_usable(const moe_cfg_t* c, int which, int ks) {
-  return which == 13 && (c->block_m == 16 || c->block_m == 32) && ks < -1 &&
+  return which == 13 && ks < -1 && (c->block_m <= 32 || -ks <= kTailMaxWide) &&
          moe::ksplit_ok(c->quant_mode, gemm_kb(c, which), -ks);
 }
 size_t tail_bytes(const moe_cfg_t* c, int ks) {
@@ -113,13 +115,16 @@ bool ksplit_usable(const moe_cfg_t* c, int32_t T, int which, int ks) {
 }
 
 // The split the library uses: a K split of every item when workgroups would
-// otherwise idle; else, for GEMM1 at block_m 16/32 where the last round of
-// items is expected to leave most workgroups idle, a tail split into the
-// most pieces the scale layout allows.
+// otherwise idle; else, for GEMM1 where the last round of items is expected
+// to leave most workgroups idle, a tail split into the most pieces the scale
+// layout allows (at most 4 at block_m 64 and 128, and there block FP8 only:
+// on one MI355X the tensor-parallel share of the prefill layer, I = 128,
+// gained 9% in GEMM1 from it, the MXFP4 share with I = 256 lost 20%).
 int plan_ksplit(const moe_cfg_t* c, int32_t T, int which) {
   const int ks = moe::pick_ksplit(c->quant_mode, T, c->num_experts, c->top_k, c->block_m, gemm_kb(c, which),
                                   gemm_n_tiles(c, which));
   if (ks > 1 && ksplit_usable(c, T, which, ks)) return ks;
+  if (c->block_m >= 64 && c->quant_mode == MOE_QUANT_MXFP4) return 1;
   if (which == 13 && moe::tail_split_plan_ok(T, c->num_experts, c->top_k, c->block_m, gemm_n_tiles(c, which)))
     for (int t = -moe::kSplitMax; t <= -2; t /= 2)
       if (tail_usable(c, which, t)) return t;
@@ -147,7 +152,8 @@ size_t split_reserve(const moe_cfg_t* c, int32_t T, int which) {
   const int64_t Hp = c->pad.hidden_padded, Ip = c->pad.inter_padded;
   if (which == 13) {
     const size_t full = cap > 1 ? align_up((size_t)(cap * Ps * 2 * Ip * 4 + Ps * 4)) : 0;
-    const size_t tail = tail_usable(c, 13, -cap) ? tail_bytes(c, cap) : 0;
+    const int tcap = c->block_m <= 32 || cap < kTailMaxWide ? cap : kTailMaxWide;
+    const size_t tail = tail_usable(c, 13, -tcap) ? tail_bytes(c, tcap) : 0;
     return full > tail ? full : tail;
   }
   const int64_t planes = cap > 1 ? cap * moe::y_plane_bytes(Ps, Hp) : 0, y = moe::y_reserve_bytes(P, Hp);

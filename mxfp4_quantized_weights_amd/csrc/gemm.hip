@@ -82,6 +82,11 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 // with 28-31% of a round left gain 1-5%; 69-82% left lose 2-14%).
 __host__ __device__ inline bool tail_split_on(int items, int W) { return 2 * (items % W) <= W; }
 
+// Kernel instances by split (template argument SPLIT): none; a K split of
+// every item; a tail launch (GEMM1).  Each carries only its own epilogues,
+// which keeps the plain and K-split kernels' register use as it is.
+constexpr int kNoSplit = 0, kKSplit = 1, kTailSplit = 2;
+
 // Waves of a workgroup: 4 column waves (the N tile's 16 weight tiles, 4 each)
 // times WT token groups: BM/64 groups of 64 tokens (4 token tiles per wave)
 // for BM >= 64, one group of BM/16 tiles below.  A wave multiplies MT token
@@ -601,11 +606,16 @@ __device__ __forceinline__ void epilogue_gemm1_part(const GemmArgs& p, const v4f
 template <int MT, int BM>
 __device__ __forceinline__ void epilogue_gemm1_tail(const GemmArgs& p, const v4f (&acc)[MT][4], int piece, int r,
                                                     int wt, int wn) {
-  const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
+  // the lane's offset is formed here, not hoisted out of the ring loop, where
+  // it would hold registers for the whole launch
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, q = lane >> 4, c16 = lane & 15;
+  float* item = p.part + ((int64_t)piece * gridDim.x + r) * BM * 256;
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int t = (wt * MT + m) * 16 + c16;
-    float* row = p.part + (((int64_t)piece * gridDim.x + r) * BM + t) * 256 + 32 * wn + 4 * q;
+    float* row = item + t * 256 + 32 * wn + 4 * q;
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) {
       const v4f g = acc[m][jj], u = acc[m][jj + 2];
@@ -670,7 +680,7 @@ __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&
 // start; when an item has fewer than S K blocks that is too late for the
 // ring's own waits to cover it (the S-1 K blocks of the prologue are issued
 // without waits), and the kernel then waits for it explicitly.
-template <int MODE, int BM, bool G1, int S, bool SPLIT>
+template <int MODE, int BM, bool G1, int S, int SPLIT>
 __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_kernel(GemmArgs p) {
   using R = Ring<MODE, BM>;
   static_assert(S >= 3 && S <= 5, "ring depth");
@@ -717,12 +727,18 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
   //     kernel finishes (launch_gemm1_tail_finish) -- when the remaining
   //     items fill at most half a round (tail_split_on); else the launch
   //     runs every item whole, as the plain kernel.
+  // A plain launch may group NTG N tiles of one M block into an item (when
+  // K has fewer than S K blocks, so that every item streams at least S):
+  // the item's K blocks run N tile by N tile, each with its own epilogue,
+  // and the block's metadata serves them all.
+  const int NTG = SPLIT == kNoSplit ? p.ntg : 1;
+  const int n_grp = p.n_tiles / NTG;  // items per M block
   const int npp = __builtin_amdgcn_readfirstlane(*p.npp);
   const int nw = gridDim.x / kXcds;
   const int xcd = blockIdx.x % kXcds, jw = blockIdx.x / kXcds;
-  const int all_items = (npp / BM) * p.n_tiles;
-  const bool tail = SPLIT && BM <= 32 && p.tail && tail_split_on(all_items, (int)gridDim.x);
-  const int KSL = SPLIT && (tail || !p.tail) ? p.ks_log2 : 0;  // K pieces per split item: 2^KSL
+  const int all_items = (npp / BM) * n_grp;
+  const bool tail = SPLIT == kTailSplit && tail_split_on(all_items, (int)gridDim.x);
+  const int KSL = SPLIT == kKSplit || tail ? p.ks_log2 : 0;  // K pieces per split item: 2^KSL
   int n_whole = 0, wbase = 0, tail_base = 0, list = all_items << KSL;
   if (tail) {
     const int F = all_items / (int)gridDim.x;
@@ -741,17 +757,18 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
   const int KB = p.K / 128;   // K blocks of a weight row
   const int KBP = KB >> KSL;  // K blocks of a piece
   const int NG = tiled_n_groups(p.N);  // N tiles of the weight matrix (TILED_V2)
-  const int total = n_whole * KB + n_tail * KBP;
+  const int total = n_whole * KB + n_tail * KBP * NTG;
   // item -> (M block, N tile, K piece), K pieces innermost.  (Every lambda of
   // this kernel is always_inline: one left as a call makes the kernel keep
   // its arguments in scratch memory, which cost 4x at one token.)
   auto item_g = [&](int ii) __attribute__((always_inline)) {
     return ii < n_whole ? wbase + ii * nw : tail_base + ((first + (ii - n_whole) * nw) >> KSL);
   };
-  auto item_m = [&](int ii) __attribute__((always_inline)) { return item_g(ii) / p.n_tiles; };
-  auto item_nt = [&](int ii) __attribute__((always_inline)) { return p.nt0 + item_g(ii) % p.n_tiles; };
+  auto item_m = [&](int ii) __attribute__((always_inline)) { return item_g(ii) / n_grp; };
+  auto item_nt = [&](int ii) __attribute__((always_inline)) { return p.nt0 + item_g(ii) % n_grp * NTG; };  // first N tile
   auto item_ks = [&](int ii) __attribute__((always_inline)) { return ii < n_whole ? 0 : (first + (ii - n_whole) * nw) & ((1 << KSL) - 1); };
-  auto item_kbi = [&](int ii) __attribute__((always_inline)) { return ii < n_whole ? KB : KBP; };
+  auto item_kbs = [&](int ii) __attribute__((always_inline)) { return ii < n_whole ? KB : KBP; };  // per N tile
+  auto item_kbi = [&](int ii) __attribute__((always_inline)) { return item_kbs(ii) * NTG; };
   // Items of fewer than S K blocks finish inside the prologue (which issues
   // S-1 K blocks without waiting) or within S-1 steps of the next item's
   // metadata loads: their metadata is waited for explicitly.
@@ -780,15 +797,36 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
   rs.wk = p.tile_run * R::TILE;
   rs.wsk = p.tile_run * 256;
   int wts_step = -1, wts_item = 0;
-  auto setup_issue = [&](int ii, int s) __attribute__((always_inline)) {
-    const int m = item_m(ii), nt = item_nt(ii);
-    const int kb0 = item_ks(ii) * KBP;  // first K block of the item (0 for whole items)
-    const int e = __builtin_amdgcn_readfirstlane(exp_lds[ii % NB]);
+  int i_e = 0, i_nt = 0;  // expert and N tile being loaded
+  // weight-side sources of N tile nt of expert e from K block kb0
+  auto setup_weights = [&](int e, int nt, int kb0) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < R::DW; ++q) {
       const int g = wave * R::DW + q, tile = g / R::HALVES, h = g % R::HALVES;
       rs.w[q] = p.B + tiled_index(p.tile_run, e, NG, nt, tile, KB, kb0) * R::TILE + h * 1024 + lane * 16;
     }
+    if constexpr (MODE != kGemmMx) {
+      // GEMM1: the gate and the up 128-row block of the N tile; GEMM2: the
+      // N tile's two 128-row blocks (the second clamped to the last block)
+      const int NB128 = p.N / 128;
+      const int b0 = G1 ? nt : nt * 2, b1 = G1 ? p.Ip / 128 + nt : min(nt * 2 + 1, NB128 - 1);
+      rs.wsc = (const uint8_t*)((const float*)p.Bs + ((int64_t)e * NB128 + ((lane & 1) ? b1 : b0)) * KB + kb0);
+    }
+    if constexpr (R::DWS > 0) {
+      const int KBq = (KB + 3) / 4;
+#pragma unroll
+      for (int q = 0; q < R::DWS; ++q)
+        rs.ws[q] = (const uint8_t*)p.Bs +
+                   (tiled_index(p.tile_run, e, NG, nt, wave * R::DWS + q, KBq, kb0 / 4) * 64 + lane) * 4;
+    }
+  };
+  auto setup_issue = [&](int ii, int s) __attribute__((always_inline)) {
+    const int m = item_m(ii), nt = item_nt(ii);
+    const int kb0 = item_ks(ii) * KBP;  // first K block of the item (0 for whole items)
+    const int e = __builtin_amdgcn_readfirstlane(exp_lds[ii % NB]);
+    i_e = e;
+    i_nt = nt;
+    setup_weights(e, nt, kb0);
     const int32_t* ids = ids_lds[ii % NB];
     // rows past BM (the unused scale entries of a small block) read row 0 / the block's first row
     auto row_of = [&](int r) -> int64_t {
@@ -811,20 +849,6 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
       rs.ts[h] = (MODE == kGemmMx) ? (const uint8_t*)p.As + row * p.ldas + kb0 * 4
                  : e8_tokens(MODE) ? (const uint8_t*)p.As + row * p.ldas + kb0
                                    : (const uint8_t*)p.As + row * p.ldas * 4 + kb0 * 4;
-    }
-    if constexpr (MODE != kGemmMx) {
-      // GEMM1: the gate and the up 128-row block of the N tile; GEMM2: the
-      // N tile's two 128-row blocks (the second clamped to the last block)
-      const int NB128 = p.N / 128;
-      const int b0 = G1 ? nt : nt * 2, b1 = G1 ? p.Ip / 128 + nt : min(nt * 2 + 1, NB128 - 1);
-      rs.wsc = (const uint8_t*)((const float*)p.Bs + ((int64_t)e * NB128 + ((lane & 1) ? b1 : b0)) * KB + kb0);
-    }
-    if constexpr (R::DWS > 0) {
-      const int KBq = (KB + 3) / 4;
-#pragma unroll
-      for (int q = 0; q < R::DWS; ++q)
-        rs.ws[q] = (const uint8_t*)p.Bs +
-                   (tiled_index(p.tile_run, e, NG, nt, wave * R::DWS + q, KBq, kb0 / 4) * 64 + lane) * 4;
     }
     // metadata of the next item: ids now; GEMM2 weights S-1 steps later,
     // once the ring's waits have covered the ids (or right away after an
@@ -852,14 +876,15 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
 #pragma unroll
     for (int j = 0; j < 4; ++j) tiles[j] = 4 * wn + j;
   }
-  int c_nt = 0, c_row0 = 0, c_mv = MT, c_ks = 0, c_kbi = KB, c_g = 0;
+  int c_nt = 0, c_row0 = 0, c_mv = MT, c_ks = 0, c_kbi = KB, c_g = 0, c_sub = 0;
   bool active = true;
   auto setup_compute = [&](int ii) __attribute__((always_inline)) {
     c_nt = item_nt(ii);
     c_ks = item_ks(ii);
     c_row0 = item_m(ii) * BM;
-    c_kbi = item_kbi(ii);
+    c_kbi = item_kbs(ii);  // K blocks per N tile
     c_g = item_g(ii);
+    c_sub = 0;
     if constexpr (!G1) active = c_nt * 256 + 64 * wn < p.N;
     // real rows are a prefix of the block: count the wave's token tiles
     // that start with one
@@ -879,7 +904,7 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
   // issue cursor (item, K block) and MX weight-scale groups: the group of up
   // to 4 K blocks that starts at K block kb (kb % 4 == 0) goes to
   // ws_buf[group count % NWS] with the loads of that K block
-  int i_ii = 0, i_kb = 0, i_grp = 0, i_kbi = item_kbi(0);
+  int i_ii = 0, i_kb = 0, i_grp = 0, i_kbi = item_kbs(0), i_sub = 0;
   auto issue_next = [&](auto slot_c, int s) __attribute__((always_inline)) {
     if (i_ii < n_my) {
       const uint8_t* ws = nullptr;
@@ -889,8 +914,12 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
       ring_issue<MODE, BM>(rs, slot(slot_c), wave, i_kb, ws);
       if (++i_kb == i_kbi) {
         i_kb = 0;
-        if (++i_ii < n_my) {
-          i_kbi = item_kbi(i_ii);
+        if (++i_sub < NTG) {
+          // the item's next N tile (grouped items are whole: from K block 0)
+          setup_weights(i_e, ++i_nt, 0);
+        } else if (++i_ii < n_my) {
+          i_sub = 0;
+          i_kbi = item_kbs(i_ii);
           setup_issue(i_ii, s);
         }
       }
@@ -934,18 +963,13 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
     if (++c_kb == c_kbi) {
       const int32_t* ids = ids_lds[c_ii % NB];
       if constexpr (G1) {
-        if constexpr (SPLIT) {
-          // tail launches exist at block_m 16 / 32 only (the host refuses others)
-          if constexpr (BM <= 32) {
-            if (!p.tail)
-              epilogue_gemm1_part<MODE, MT>(p, acc, ids, c_row0, c_ks, c_nt, wt, wn);
-            else if (!tail || c_ii < n_whole)
-              epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
-            else
-              epilogue_gemm1_tail<MT, BM>(p, acc, c_ks, c_g - tail_base, wt, wn);
-          } else {
-            epilogue_gemm1_part<MODE, MT>(p, acc, ids, c_row0, c_ks, c_nt, wt, wn);
-          }
+        if constexpr (SPLIT == kKSplit) {
+          epilogue_gemm1_part<MODE, MT>(p, acc, ids, c_row0, c_ks, c_nt, wt, wn);
+        } else if constexpr (SPLIT == kTailSplit) {
+          if (!tail || c_ii < n_whole)
+            epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
+          else
+            epilogue_gemm1_tail<MT, BM>(p, acc, c_ks, c_g - tail_base, wt, wn);
         } else {
           epilogue_gemm1_s<MODE, BM>(p, acc, red, ids, c_row0, c_nt, wt, wn);
         }
@@ -957,7 +981,12 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[m][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
       c_kb = 0;
-      if (++c_ii < n_my) setup_compute(c_ii);
+      if (++c_sub < NTG) {
+        ++c_nt;
+        if constexpr (!G1) active = c_nt * 256 + 64 * wn < p.N;
+      } else if (++c_ii < n_my) {
+        setup_compute(c_ii);
+      }
     }
   };
   for (int s0 = 0; s0 < total; s0 += S) {
@@ -995,14 +1024,14 @@ int gemm_grid_max() { return (device_cus() + kXcds - 1) / kXcds * kXcds; }
 
 // Kernels with a K split (SPLIT) are separate instances, so that the plain
 // ones carry none of its per-item state.
-template <int MODE, bool G1, bool SPLIT>
+template <int MODE, bool G1, int SPLIT>
 static hipError_t launch_gemm_split(int block_m, int nb, const GemmArgs& a, hipStream_t s) {
   constexpr int SR = (MODE == kGemmMx) ? MOE_RING_S_MX : MOE_RING_S_FP8;    // block_m 64 / 128
   constexpr int SD = (MODE == kGemmMx) ? MOE_RING_S_MX : MOE_RING_S_SMALL;  // block_m 16 / 32
   // One workgroup per CU (the ring's LDS use allows no more), fewer when
   // there are fewer items; a multiple of kXcds so that every XCD gets the
   // same number of workgroups.
-  const int64_t items = ((int64_t)nb * a.n_tiles) << a.ks_log2;
+  const int64_t items = ((int64_t)nb * (a.n_tiles / a.ntg)) << a.ks_log2;
   const int64_t wgs = gemm_grid_max();
   // a tail launch splits the items past the grid's whole rounds: all of it
   const dim3 grid((unsigned)(a.tail || items >= wgs ? wgs : (items + kXcds - 1) / kXcds * kXcds));
@@ -1029,15 +1058,37 @@ static hipError_t launch_gemm_split(int block_m, int nb, const GemmArgs& a, hipS
 
 template <int MODE, bool G1>
 static hipError_t launch_gemm_mode(int block_m, int nb, const GemmArgs& a, hipStream_t s) {
-  return a.ks_log2 > 0 ? launch_gemm_split<MODE, G1, true>(block_m, nb, a, s)
-                       : launch_gemm_split<MODE, G1, false>(block_m, nb, a, s);
+  if constexpr (G1) {
+    if (a.tail) return launch_gemm_split<MODE, G1, kTailSplit>(block_m, nb, a, s);
+  }
+  return a.ks_log2 > 0 ? launch_gemm_split<MODE, G1, kKSplit>(block_m, nb, a, s)
+                       : launch_gemm_split<MODE, G1, kNoSplit>(block_m, nb, a, s);
+}
+
+// Ring depth of a launch.
+static int ring_depth(int gmode, int block_m) {
+  if (gmode == kGemmMx) return MOE_RING_S_MX;
+  return block_m >= 64 ? MOE_RING_S_FP8 : MOE_RING_S_SMALL;
+}
+
+// N tiles per item of a plain launch: 1, or when K has fewer K blocks than
+// the ring's depth the smallest power of two (dividing the launch's N tiles)
+// whose items stream at least that many, so that no item waits for its
+// metadata (items of fewer K blocks than the depth must).
+static int n_tile_group(int gmode, int block_m, const GemmArgs& a) {
+  const int KB = a.K / 128, S = ring_depth(gmode, block_m);
+  int g = 1;
+  while (g * KB < S && a.n_tiles % (2 * g) == 0) g *= 2;
+  return g;
 }
 
 // GEMM1's output is re-quantised, so its sum must be fp32-exact: block FP8
 // (either scale format) runs on the f16 MFMA (FP8 storage, exact widening in
 // registers).
-hipError_t launch_gemm1(int mode, int block_m, int nb, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm1(int mode, int block_m, int nb, const GemmArgs& a0, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
+  GemmArgs a = a0;
+  a.ntg = 1;
   switch (mode) {
     case kQuantFp8: return launch_gemm_mode<kGemmFp8F16, true>(block_m, nb, a, s);
     case kQuantFp8E8: return launch_gemm_mode<kGemmE8F16, true>(block_m, nb, a, s);
@@ -1045,8 +1096,11 @@ hipError_t launch_gemm1(int mode, int block_m, int nb, const GemmArgs& a, hipStr
   }
 }
 
-hipError_t launch_gemm2(int mode, int block_m, int nb, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm2(int mode, int block_m, int nb, const GemmArgs& a0, hipStream_t s) {
   if (nb <= 0) return hipSuccess;
+  GemmArgs a = a0;
+  const int gm = mode == kQuantFp8 ? kGemmFp8 : mode == kQuantFp8E8 ? kGemmE8 : kGemmMx;
+  a.ntg = a.ks_log2 > 0 ? 1 : n_tile_group(gm, block_m, a);
   switch (mode) {
     case kQuantFp8: return launch_gemm_mode<kGemmFp8, false>(block_m, nb, a, s);
     case kQuantFp8E8: return launch_gemm_mode<kGemmE8, false>(block_m, nb, a, s);
@@ -1090,6 +1144,11 @@ bool tail_split_plan_ok(int T, int E, int k, int block_m, int n_tiles) {
   const double W = (double)gemm_grid_max();
   const double items = expected_items(T, E, k, block_m, n_tiles);
   const double left = items - W * floor(items / W);
+  // at block_m 64 / 128 only for a few rounds of items (one GPU's share of
+  // a tensor-parallel layer, small batches), where the last round is a large
+  // part of the launch: the estimate ignores experts with a second block,
+  // which many-round prefill batches have
+  if (block_m >= 64 && items >= 4 * W) return false;
   return T > 0 && left <= 0.7 * W;
 }
 
@@ -1298,8 +1357,12 @@ static void launch_tail_finish_mode(int ks, int block_m, const float* part, cons
                                     void* as, hipStream_t s) {
   if (block_m == 16)
     launch_tail_finish_bm<QMODE, 16>(ks, part, sorted, npp, n_tiles, W, P, Ip, limit, aq, as, s);
-  else
+  else if (block_m == 32)
     launch_tail_finish_bm<QMODE, 32>(ks, part, sorted, npp, n_tiles, W, P, Ip, limit, aq, as, s);
+  else if (block_m == 64)
+    launch_tail_finish_bm<QMODE, 64>(ks, part, sorted, npp, n_tiles, W, P, Ip, limit, aq, as, s);
+  else
+    launch_tail_finish_bm<QMODE, 128>(ks, part, sorted, npp, n_tiles, W, P, Ip, limit, aq, as, s);
 }
 
 hipError_t launch_gemm1_tail_finish(int mode, int ks, int block_m, const float* part, const int32_t* sorted,

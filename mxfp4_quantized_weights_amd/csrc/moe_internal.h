@@ -113,6 +113,7 @@ struct GemmArgs {
   int64_t yexp;           // GEMM2: byte offset of the exponents within a plane
   int32_t tile_run;       // TILED_V2 tile run R of B (tile_run(mode, which))
   int32_t tail;           // GEMM1 with a K split: whole items in whole rounds, only the rest split (see below)
+  int32_t ntg;            // N tiles per item (set by launch_gemm1 / launch_gemm2)
 };
 
 // K split of the grouped GEMMs for small batches.  When few (M block, N tile)
@@ -134,7 +135,7 @@ bool ksplit_ok(int mode, int KB, int ks);
 // uniform routing.  Host-only; depends on the device's CU count.
 int pick_ksplit(int mode, int T, int E, int k, int block_m, int KB, int n_tiles);
 
-// Tail split of GEMM1 (block_m 16 or 32): a launch over gemm_grid_max()
+// Tail split of GEMM1 (every block_m): a launch over gemm_grid_max()
 // workgroups runs the F = floor(items / W) whole rounds of (M block, N tile)
 // items unsplit, with the fused epilogue, and cuts only the items past them
 // into ks pieces, which store fp32 partial sums part[piece][r][block_m][256]

@@ -247,14 +247,20 @@ def test_ksplit_plan_and_scratch():
     assert M.plan_ksplit(c, 64, 13) == -8 and M.plan_ksplit(c, 64, 2) == 1
     # a shared expert (E = 1, top-1): 8 GEMM1 items -> 8 pieces
     assert M.plan_ksplit(cfg(num_experts=1, top_k=1, block_m=128), 64, 13) == 8
-    # above 1024 pairs: no split of every item; GEMM1 at block_m 16/32 keeps
-    # the tail split (it needs no per-pair scratch) where the last round is
-    # expected to be mostly idle: 100 experts at block_m 32 and 400 tokens give
-    # ~800 items, 32 past 3 rounds of 256; at 129 tokens ~2240 items leave 0.75
-    # of a round (the kernel would not split it), and 8 tokens ~470 items 0.84
+    # above 1024 pairs: no split of every item; GEMM1 keeps the tail split (it
+    # needs no per-pair scratch) where the last round is expected to be mostly
+    # idle: 100 experts at block_m 32 or 64 and 400 tokens give ~800 items, 32
+    # past 3 rounds of 256 (at most 4 pieces at block_m 64 and 128); at 129
+    # tokens ~2240 items leave 0.75 of a round (the kernel would not split
+    # it), and 8 tokens ~470 items 0.84
     assert M.plan_ksplit(c, 129, 13) == 1 and M.plan_ksplit(c, 4096, 2) == 1 and M.plan_ksplit(c, 8, 13) == 1
-    assert M.plan_ksplit(cfg(num_experts=100, block_m=64), 400, 13) == 1
+    assert M.plan_ksplit(cfg(num_experts=100, block_m=64), 400, 13) == -4
     assert M.plan_ksplit(cfg(num_experts=100, block_m=32), 400, 13) == -8
+    # one GPU's share of the prefill layer under 8-way tensor parallelism
+    # (I = 128: one N tile per block): ~290 items, one round and a few left
+    assert M.plan_ksplit(cfg(inter=128, block_m=128), 4096, 13) == -4
+    # the prefill layer itself: ~2300-2500 items, most of a round left
+    assert M.plan_ksplit(cfg(block_m=128), 4096, 13) == 1
     assert M.plan_ksplit(c, 16, 13) == -8 and M.plan_ksplit(c, 32, 13) == -8
     assert M.plan_ksplit(cfg(inter=256), 64, 13) == 1   # 2 N tiles: ~480 items, 0.875 of a round left
     assert M.plan_ksplit(c, 1, 7) == -1
@@ -266,7 +272,7 @@ def test_ksplit_plan_and_scratch():
     for ks in (2, 4, 8):
         assert M.splitk_bytes(c, 64, 13, -ks) == ks * 256 * 16 * 256 * 4
         assert M.splitk_bytes(cfg(block_m=32), 64, 13, -ks) == ks * 256 * 32 * 256 * 4
-        assert M.splitk_bytes(cfg(block_m=64), 64, 13, -ks) == 0   # block_m 16 or 32 only
+        assert M.splitk_bytes(cfg(block_m=64), 64, 13, -ks) == (ks * 256 * 64 * 256 * 4 if ks <= 4 else 0)
         assert M.splitk_bytes(c, 64, 2, -ks) == 0                  # GEMM1 only
     assert M.splitk_bytes(c, 64, 13, -3) == 0 and M.splitk_bytes(c, 64, 13, -16) == 0
     # GEMM2's y plane: int16 values [P, Hp] and one exponent byte per 64 columns

@@ -151,13 +151,14 @@ def test_splitk_single_token_all_experts_zero():
 # Tail split: more (block, N tile) items than workgroups (one per compute
 # unit, 256 on the MI355X) and not a multiple of them: 40 experts x 8 N tiles
 # at block_m 16 (some experts take two blocks) give ~360 GEMM1 items, one
-# whole round and a leftover round that the tail split cuts into K pieces.
+# whole round and a leftover round that the tail split cuts into K pieces;
+# at block_m 64 and 128 (one block per expert) 320 items.
 # K = 1024 (8 K blocks): pieces of 4 K blocks (ksplit -2) in every mode.
 TAIL1 = W.Workload("tail1", T=48, H=1024, I=1024, E=40, top_k=8, mode="fp8", outlier_frac=0.02)
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("bm", [16, 32])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
 def test_gemm1_tail_split_stage(mode, bm):
     """GEMM1 with the tail split (whole rounds unsplit, the leftover items in
     K pieces finished by the second kernel) against the oracle's stages, and
@@ -169,13 +170,18 @@ def test_gemm1_tail_split_stage(mode, bm):
     log(f"  {items} GEMM1 items")
     assert items > 256 or bm == 32
     ref, st, Q = _oracle_stages(wl, x, lg)
-    assert M.plan_ksplit(cfg, wl.T, 13) == -2
+    # planned at every block_m for block FP8, at block_m 16 / 32 for MXFP4
+    # (which still takes it when asked)
+    planned = -2 if bm <= 32 or mode != "mxfp4" else 1
+    assert M.plan_ksplit(cfg, wl.T, 13) == planned
     assert M.splitk_bytes(cfg, wl.T, 13, -2) > 0
+    res = {}
     for ks in (1, -2):
         aq, as_ = M.moe_grouped_gemm1_swiglu(cfg, wl.T, xq, xs, sid, bexp, npp, ew.w13, ew.w13_scale, ksplit=ks)
         torch.cuda.synchronize()
         log(f"  ksplit {ks}")
-        tie = _verify(wl, aq, as_, sid, npp, st, Q)
+        res[ks] = (aq, as_, _verify(wl, aq, as_, sid, npp, st, Q))
+    aq, as_, tie = res[planned]
     xd, lgd = x.cuda(), lg.cuda()
     out1 = M.moe_forward(cfg, xd, lgd, *ew.tiled())
     out3 = M.moe_grouped_gemm2_combine(cfg, wl.T, aq, as_, sid, bexp, npp, ew.w2, ew.w2_scale, wts)
