@@ -101,7 +101,9 @@ __device__ __forceinline__ void quant_unit(const float (&v)[8], bool live, int64
 
 // A wave quantises four 128-column units (16 lanes each, 8 elements per
 // lane); a unit is one FP8 group or four MX groups of 4 lanes.  Wave `gw` of
-// `nw` quantising waves takes units 4*gw .. +3, then every 4*nw-th.
+// `nw` quantising waves takes units 4*gw .. +3, then every 4*nw-th.  A lane
+// keeps its unit's (row, group) and steps both by the stride (one division
+// at the start, none per unit).
 // UE8M0 scale rows are e8_scale_ld(cols_padded) bytes long; the bytes past
 // the last group are written as zero.  U: units per lane loaded before any
 // is quantised (U loads in flight; the results do not depend on U).
@@ -113,28 +115,43 @@ __device__ __forceinline__ void quant_rows_body(const void* __restrict__ in, int
   const int units = cols_padded / 128;
   const int64_t total = rows * units;
   const int64_t stride = nw * 4;
-  for (int64_t u0 = gw * 4 + (lane >> 4); u0 - (lane >> 4) < total; u0 += stride * U) {
+  const int64_t drow = stride / units;
+  const int dg = (int)(stride - drow * units);
+  int64_t u = gw * 4 + (lane >> 4);
+  int64_t row = u / units;
+  int g = (int)(u - row * units);
+  while (u - (lane >> 4) < total) {
     float v[U][8];
+    int64_t ur[U], rr[U];
+    int gr[U];
 #pragma unroll
     for (int r = 0; r < U; ++r) {
-      const int64_t u = u0 + stride * r;
+      ur[r] = u;
+      rr[r] = row;
+      gr[r] = g;
       if (u < total) {
-        load8<BF16, VEC>(in, u / units, ld_in, (int)(u % units) * 128 + (lane & 15) * 8, cols, v[r]);
+        load8<BF16, VEC>(in, row, ld_in, g * 128 + (lane & 15) * 8, cols, v[r]);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[r][i] = 0.0f;
       }
+      u += stride;
+      row += drow;
+      g += dg;
+      if (g >= units) {
+        g -= units;
+        ++row;
+      }
     }
 #pragma unroll
     for (int r = 0; r < U; ++r) {
-      const int64_t u = u0 + stride * r;
       // a pass whose units all lie past the end does nothing (its lanes
       // would only exchange zeros)
-      if (u - (lane >> 4) >= total) break;
-      const bool live = u < total;
-      const int64_t row = live ? u / units : 0;
-      const int g = live ? (int)(u % units) : 0;
-      quant_unit<MODE>(v[r], live, row, g, g * 128 + (lane & 15) * 8, units, cols_padded, q, scales);
+      if (ur[r] - (lane >> 4) >= total) break;
+      const bool live = ur[r] < total;
+      const int64_t row_r = live ? rr[r] : 0;
+      const int g_r = live ? gr[r] : 0;
+      quant_unit<MODE>(v[r], live, row_r, g_r, g_r * 128 + (lane & 15) * 8, units, cols_padded, q, scales);
     }
   }
 }

@@ -338,8 +338,10 @@ __global__ __launch_bounds__(256) void route_quant_kernel(const float* __restric
     return;
   }
   const int64_t gw = (int64_t)(blockIdx.x - nr) * 4 + wave, nw = (int64_t)(gridDim.x - nr) * 4;
+  // two units' loads in flight per lane: large batches take two or more
+  // passes of the grid
   if (vec)
-    quant_rows_body<true, true, MODE>(x, T, H, ld_x, Hp, xq, xs, gw, nw);
+    quant_rows_body<true, true, MODE, 2>(x, T, H, ld_x, Hp, xq, xs, gw, nw);
   else
     quant_rows_body<true, false, MODE>(x, T, H, ld_x, Hp, xq, xs, gw, nw);
 }

@@ -40,6 +40,56 @@ def _spread_values(rng, rows, cols):
     return v
 
 
+def _fp8_decision_rows():
+    """Groups of 128 values whose quotients v / s lie on, or one or two fp32
+    steps beside, every positive E4M3 value and every midpoint between
+    neighbouring values (both signs), for several group scales s = amax / 448
+    (amax = the group's first value: 448, so that s = 1, and scales that are
+    not powers of two).  These are the quotients whose E4M3 code is decided
+    closest, so a quantiser that does not form the IEEE quotient, or rounds
+    it otherwise, shows here."""
+    tab = O.e4m3_value_table()[:0x7F].astype(np.float64)  # codes 0x00 .. 0x7E
+    targets = np.concatenate([tab, (tab[:-1] + tab[1:]) / 2])
+    groups = []
+    for amax in (448.0, 3.7, 1.37e-3, 77.7, 2.9e5):
+        a32 = np.float32(amax)
+        sc = a32 / np.float32(448.0)
+        vals = []
+        for t in targets:
+            v0 = np.float32(t) * sc
+            for v in (np.nextafter(np.nextafter(v0, np.float32(-np.inf)), np.float32(-np.inf)),
+                      np.nextafter(v0, np.float32(-np.inf)), v0, np.nextafter(v0, np.float32(np.inf)),
+                      np.nextafter(np.nextafter(v0, np.float32(np.inf)), np.float32(np.inf))):
+                if 0 < v <= a32:
+                    vals += [v, -v]
+        vals = np.array(vals, np.float32)
+        for i in range(0, len(vals), 127):
+            g = np.zeros(128, np.float32)
+            g[0] = a32 if (i // 127) % 2 == 0 else -a32
+            chunk = vals[i:i + 127]
+            g[1:1 + len(chunk)] = chunk
+            groups.append(g)
+    while len(groups) % 8:
+        groups.append(np.zeros(128, np.float32))
+    return np.stack(groups).reshape(-1, 8 * 128)
+
+
+def test_quant_act_fp8_every_code_and_midpoint():
+    """Block-FP8 activation codes at every decision point (_fp8_decision_rows),
+    bit-exact against the oracle: the code is the RNE E4M3 code of the IEEE
+    quotient fl32(v / s) (reading r4)."""
+    v = _fp8_decision_rows()
+    rows, cols = v.shape
+    log(f"quant_act fp8 decision rows: {rows} x {cols}")
+    q, s = M.moe_quant_act(torch.from_numpy(v).cuda(), cols, "fp8")
+    torch.cuda.synchronize()
+    qo, so = O.quant_act("fp8", v)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    qg = q.cpu().numpy()
+    bad = np.argwhere(qg != qo)
+    assert len(bad) == 0, f"{len(bad)} codes differ, e.g. v={v[tuple(bad[0])]!r}: {qg[tuple(bad[0])]:#x} vs {qo[tuple(bad[0])]:#x}"
+
+
 @pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_quant_act_bitexact(mode, dtype):
