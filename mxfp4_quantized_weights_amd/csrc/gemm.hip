@@ -626,15 +626,17 @@ __device__ __forceinline__ void epilogue_gemm1_tail(const GemmArgs& p, const v4f
 }
 
 // GEMM2 epilogue: the weighted rows v = routing weight * C of real pairs, in
-// y's block floating point (y_plane_bytes): int16 q = rint(v * 2^-s) with one
-// exponent s = max(floor(log2 max|v|) - 14, -128) per 64 columns of a row.
-// Lane l holds, for token t = (wt*MT + m)*16 + l%16, columns 64*wn + 16*j +
-// 4*(l/16) + i of the N tile, so a row's 64-column group is the wave's and
-// its 4 lanes (l/16 = 0..3) share the group's largest |v| through two lane
-// exchanges.  |v| * 2^-s < 2^15, and a value that rounds to 2^15 is stored
-// as 32767, so v' = q * 2^s is within 2^s <= 2^-14 max|v| of v.  Routing
-// weights come from LDS.  y holds the columns of this launch's N tiles (from
-// nt0); a K piece writes its own plane.
+// y's block floating point (y_plane_bytes): int16 q = rint(v * 2^-s),
+// saturated to the int16 range, with one exponent s = max(floor(log2
+// max|v|) - 14, -128) per 64 columns of a row.  Lane l holds, for token t =
+// (wt*MT + m)*16 + l%16, columns 64*wn + 16*j + 4*(l/16) + i of the N tile,
+// so a row's 64-column group is the wave's and its 4 lanes (l/16 = 0..3)
+// share the group's largest |v| through two lane exchanges; that maximum is
+// |w| * max|C| (rounding is monotonic).  |v| * 2^-s < 2^15, so only a
+// value that rounds to 2^15 saturates (to 32767), and v' = q * 2^s is within
+// 2^s <= 2^-14 max|v| of v.  Routing weights come from LDS.  y holds the
+// columns of this launch's N tiles (from nt0); a K piece writes its own
+// plane.
 template <int MT>
 __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&acc)[MT][4], const int32_t* sid,
                                                  const float* wts, int ks, int nt, int wt, int wn) {
@@ -647,17 +649,14 @@ __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&
     const int s = sid[t];
     const bool real = s < p.num_pairs;
     const float w = real ? wts[t] : 0.0f;
-    float v[4][4];
-    float mx = 0.0f;
+    float mc = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[j][i] = w * acc[m][j][i];
-        mx = fmaxf(mx, fabsf(v[j][i]));
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int i = 0; i < 4; ++i) mc = fmaxf(mc, fabsf(acc[m][j][i]));
+    mc = fmaxf(mc, __shfl_xor(mc, 16));
+    mc = fmaxf(mc, __shfl_xor(mc, 32));
+    const float mx = fabsf(w) * mc;
     if (real) {
       // floor(log2 mx) from the exponent field (subnormals included)
       const int e = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;
@@ -667,9 +666,9 @@ __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&
       for (int j = 0; j < 4; ++j) {
         int qv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qv[i] = min(max((int)__builtin_rintf(ldexpf(v[j][i], -sx)), -32767), 32767);
-        *(uint2*)(yrow + 16 * j) = make_uint2(((uint32_t)qv[0] & 0xFFFFu) | ((uint32_t)qv[1] << 16),
-                                              ((uint32_t)qv[2] & 0xFFFFu) | ((uint32_t)qv[3] << 16));
+        for (int i = 0; i < 4; ++i) qv[i] = (int)__builtin_rintf(ldexpf(w * acc[m][j][i], -sx));
+        *(uint2*)(yrow + 16 * j) = make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(qv[0], qv[1])),
+                                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(qv[2], qv[3])));
       }
       if (q == 0) ((int8_t*)(plane + p.yexp))[(int64_t)s * (p.ldy / 64) + col0 / 64] = (int8_t)sx;
     }

@@ -23,38 +23,26 @@ constexpr float kE4M3Max = 448.0f;
 constexpr float kE2M1Max = 6.0f;
 
 // E4M3FN code of a finite fp32 value with |v| <= 448, rounded to nearest,
-// ties to even; the sign bit is kept (also for zero).
+// ties to even; the sign bit is kept (also for zero and for values that round
+// to zero).  This is the hardware conversion: on gfx950 it rounds exactly so
+// (compared with the rounding written out -- RNE at the 20th fraction bit for
+// normal codes, multiples of 2^-9 below 2^-6 -- on every E4M3 value, every
+// midpoint and their fp32 neighbours, fp32 subnormals and 2^20 random values;
+// the quantiser tests hold its codes to the oracle's), in one instruction
+// instead of a branch per value.
 __device__ __forceinline__ uint32_t e4m3_code(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t ua = u & 0x7FFFFFFFu;
-  float a = __uint_as_float(ua);
-  uint32_t code;
-  if (a < 0.015625f) {
-    // below the smallest normal 2^-6: multiples of 2^-9; a * 2^9 is exact
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    // keep 3 mantissa bits with round-half-even at bit 20, then rebias 127 -> 7
-    ua += 0x7FFFFu + ((ua >> 20) & 1u);
-    code = (ua >> 20) - (120u << 3);
-  }
-  return sign | code;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
 }
 
 // E2M1 code of a finite fp32 value with |v| <= 6 (grid 0, .5, 1, 1.5, 2, 3,
-// 4, 6), rounded to nearest, ties to the even code; sign in bit 3.
+// 4, 6), rounded to nearest, ties to the even code; sign in bit 3 (kept for
+// zero).  The hardware conversion with scale 1: on gfx950 it rounds exactly
+// so (compared with the rounding written out -- rint of 2a below 2, of a
+// between 2 and 4, of a/2 above -- on every grid value and midpoint, their
+// fp32 neighbours, fp32 subnormals and 2^20 random values; the quantiser
+// tests hold its codes to the oracle's), without the branches.
 __device__ __forceinline__ uint32_t e2m1_code(float v) {
-  uint32_t sign = (__float_as_uint(v) >> 28) & 8u;
-  float a = fabsf(v);
-  uint32_t c;
-  if (a < 2.0f) {
-    c = (uint32_t)__builtin_rintf(a * 2.0f);          // codes 0..4, spacing 0.5
-  } else if (a < 4.0f) {
-    c = (uint32_t)__builtin_rintf(a) + 2u;            // 2 -> 4, 3 -> 5, 4 -> 6
-  } else {
-    c = (uint32_t)__builtin_rintf(a * 0.5f) + 4u;     // 4 -> 6, 6 -> 7
-  }
-  return sign | c;
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, 0.0f, 1.0f, 0) & 0xFu;
 }
 
 // E8M0 byte of an MX block: 2^(floor(log2 amax) - 2) biased by 127, clamped to

@@ -161,10 +161,12 @@ hipError_t launch_swiglu_requant(int mode, const float* part, int ks, int P, int
 // GEMM2's weighted per-pair rows y are block floating point: one plane holds
 // int16 values [pairs, cols] (256-byte aligned) and then one int8 exponent s
 // per 64 columns [pairs, cols/64]; value v of a group is stored as
-// q = rint(v * 2^-s) with s = max(floor(log2 max|v|) - 14, -128), so
-// |q| <= 32767 and v' = q * 2^s differs from v by at most 2^(s-1), i.e.
-// 2^-15 of the group's largest |v|.  The combine decodes exactly and sums in
-// fp32.  Half the bytes of fp32 rows, for the two passes over them.
+// q = rint(v * 2^-s), saturated to the int16 range, with s =
+// max(floor(log2 max|v|) - 14, -128): |v| * 2^-s < 2^15, so v' = q * 2^s
+// differs from v by at most 2^(s-1) (2^-15 of the group's largest |v|), or
+// 2^s where the largest value rounds to 2^15 and saturates.  The combine
+// decodes exactly and sums in fp32.  Half the bytes of fp32 rows, for the
+// two passes over them.
 inline int64_t y_values_bytes(int64_t pairs, int64_t cols) { return (pairs * cols * 2 + 255) / 256 * 256; }
 inline int64_t y_plane_bytes(int64_t pairs, int64_t cols) {
   return y_values_bytes(pairs, cols) + (pairs * (cols / 64) + 255) / 256 * 256;
