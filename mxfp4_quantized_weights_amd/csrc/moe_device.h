@@ -24,23 +24,20 @@ constexpr float kE2M1Max = 6.0f;
 
 // E4M3FN code of a finite fp32 value with |v| <= 448, rounded to nearest,
 // ties to even; the sign bit is kept (also for zero and for values that round
-// to zero).  This is the hardware conversion: on gfx950 it rounds exactly so
-// (compared with the rounding written out -- RNE at the 20th fraction bit for
-// normal codes, multiples of 2^-9 below 2^-6 -- on every E4M3 value, every
-// midpoint and their fp32 neighbours, fp32 subnormals and 2^20 random values;
-// the quantiser tests hold its codes to the oracle's), in one instruction
-// instead of a branch per value.
+// to zero).  This is the hardware conversion, which rounds exactly so on
+// gfx950: the GPU quantiser tests hold its codes to the oracle's on every
+// E4M3 value and midpoint and their fp32 neighbours, at several group scales,
+// and on rows spanning fp32's range, subnormals and signed zeros included.
+// One instruction instead of a branch per value.
 __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
 }
 
 // E2M1 code of a finite fp32 value with |v| <= 6 (grid 0, .5, 1, 1.5, 2, 3,
 // 4, 6), rounded to nearest, ties to the even code; sign in bit 3 (kept for
-// zero).  The hardware conversion with scale 1: on gfx950 it rounds exactly
-// so (compared with the rounding written out -- rint of 2a below 2, of a
-// between 2 and 4, of a/2 above -- on every grid value and midpoint, their
-// fp32 neighbours, fp32 subnormals and 2^20 random values; the quantiser
-// tests hold its codes to the oracle's), without the branches.
+// zero).  The hardware conversion with scale 1, which rounds exactly so on
+// gfx950: the GPU quantiser tests hold its codes to the oracle's on every
+// grid value and midpoint and their fp32 neighbours, at several E8M0 scales.
 __device__ __forceinline__ uint32_t e2m1_code(float v) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, 0.0f, 1.0f, 0) & 0xFu;
 }

@@ -90,6 +90,43 @@ def test_quant_act_fp8_every_code_and_midpoint():
     assert len(bad) == 0, f"{len(bad)} codes differ, e.g. v={v[tuple(bad[0])]!r}: {qg[tuple(bad[0])]:#x} vs {qo[tuple(bad[0])]:#x}"
 
 
+def test_quant_act_mxfp4_every_code_and_midpoint():
+    """MXFP4 activation codes at every decision point: groups of 32 whose
+    largest value fixes the E8M0 scale (6 * 2^k: scale 2^k) and whose other
+    values, scaled by 2^-k, lie on or one or two fp32 steps beside every E2M1
+    value and every midpoint between neighbours, both signs.  Bit-exact
+    against the oracle (RNE on the code grid, reading r7/r8)."""
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    targets = np.concatenate([grid, (grid[:-1] + grid[1:]) / 2]).astype(np.float32)
+    groups = []
+    for k in (0, -3, 5, -20):
+        sc = np.float32(2.0 ** k)
+        vals = []
+        for t in targets:
+            v0 = t * sc
+            lo1 = np.nextafter(v0, np.float32(-np.inf))
+            hi1 = np.nextafter(v0, np.float32(np.inf))
+            for v in (np.nextafter(lo1, np.float32(-np.inf)), lo1, v0, hi1, np.nextafter(hi1, np.float32(np.inf))):
+                if 0 < v <= 6 * sc:
+                    vals += [v, -v]
+        vals = np.array(vals, np.float32)
+        for i in range(0, len(vals), 31):
+            g = np.zeros(32, np.float32)
+            g[0] = 6 * sc
+            chunk = vals[i:i + 31]
+            g[1:1 + len(chunk)] = chunk
+            groups.append(g)
+    while len(groups) % 32:
+        groups.append(np.zeros(32, np.float32))
+    v = np.stack(groups).reshape(-1, 1024)
+    log(f"quant_act mxfp4 decision rows: {v.shape[0]} x {v.shape[1]}")
+    q, s = M.moe_quant_act(torch.from_numpy(v).cuda(), v.shape[1], "mxfp4")
+    torch.cuda.synchronize()
+    qo, so = O.quant_act("mxfp4", v)
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
 @pytest.mark.parametrize("mode", ["fp8", "fp8_ue8m0", "mxfp4"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_quant_act_bitexact(mode, dtype):
