@@ -199,25 +199,38 @@ struct RingSrc {
 // l % 16, in one 16-byte word per 64 tokens.  FP8 weight scales: the last wave fetches the K block's two
 // fp32 block scales (lanes 0 and 1).  MX weight scales (one dword holds 4 K
 // blocks) are fetched only when `ws` is non-null, into that buffer.
+// `part` (0..3) issues one of four groups of the loads: the first and second
+// half of the weight loads, the token loads and token scales, and the weight
+// scales; -1 issues all.  The compute interleaves the parts with its own
+// work (ring_compute), so the loads of one K block do not queue up in front
+// of the vector memory unit all at once.
 template <int MODE, int BM>
 __device__ __forceinline__ void ring_issue(const RingSrc<MODE, BM>& src, const uint8_t* slot, int wave, int kb,
-                                           const uint8_t* ws) {
+                                           const uint8_t* ws, int part = -1) {
   using R = Ring<MODE, BM>;
   const int lane = threadIdx.x & 63;
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(slot));
+  constexpr int DWH = (R::DW + 1) / 2;
+  if (part < 0 || part <= 1) {
 #pragma unroll
-  for (int q = 0; q < R::DW; ++q)
-    dma16<true>(src.w[q] + (int64_t)kb * src.wk, base + R::W_OFF + (wave * R::DW + q) * 1024);
-#pragma unroll
-  for (int q = 0; q < R::DT; ++q)
-    if (wave * R::DT + q < R::NTD) dma16<false>(src.t[q] + kb * R::AROW, base + R::T_OFF + (wave * R::DT + q) * 1024);
-  // token scales: fp32 per K block, or the E8M0 dword of K blocks kb & ~3 .. +3
-  const int ts_off = e8_tokens(MODE) ? (kb & ~3) : kb * 4;
-#pragma unroll
-  for (int h = 0; h < R::TSW; ++h) {
-    const int c = wave * R::TSW + h;
-    if (lane < 16) dma4(src.ts[h] + ts_off, base + R::TS_OFF + (c >> 2) * 256 + (c & 3) * 64);
+    for (int q = 0; q < R::DW; ++q)
+      if (part < 0 || (q < DWH) == (part == 0))
+        dma16<true>(src.w[q] + (int64_t)kb * src.wk, base + R::W_OFF + (wave * R::DW + q) * 1024);
   }
+  if (part < 0 || part == 2) {
+#pragma unroll
+    for (int q = 0; q < R::DT; ++q)
+      if (wave * R::DT + q < R::NTD)
+        dma16<false>(src.t[q] + kb * R::AROW, base + R::T_OFF + (wave * R::DT + q) * 1024);
+    // token scales: fp32 per K block, or the E8M0 dword of K blocks kb & ~3 .. +3
+    const int ts_off = e8_tokens(MODE) ? (kb & ~3) : kb * 4;
+#pragma unroll
+    for (int h = 0; h < R::TSW; ++h) {
+      const int c = wave * R::TSW + h;
+      if (lane < 16) dma4(src.ts[h] + ts_off, base + R::TS_OFF + (c >> 2) * 256 + (c & 3) * 64);
+    }
+  }
+  if (part >= 0 && part != 3) return;
   if constexpr (MODE != kGemmMx) {
     if (wave == R::NWAVE - 1 && lane < 2) dma4(src.wsc + kb * 4, base + R::WSC_OFF);
   }
@@ -267,11 +280,21 @@ __device__ __forceinline__ v4f mfma_fp4_scaled_t(const v8i& w, const v8i& t, v4f
 // Only the first `mv` token tiles hold real rows (an expert's last block is
 // padded); the others are skipped (mv is wave-uniform, 1..MT), except in the
 // scheduled f16 path of 4 token tiles.
-template <int MODE, int BM, bool G1>
+// iss(part) issues load group `part` of the next K block (ring_issue).  The
+// scheduled f16 path (GEMM1, block FP8, 4 token tiles per wave) issues the
+// weight loads before its tiles and the token and scale loads two tile steps
+// in, so the K block's loads reach the vector memory unit in two bursts while
+// its long compute runs; every other path issues all of them first.  (Same
+// MI355X, alternating runs: FP8 GEMM1 at prefill 750 -> 733 us, on the skewed
+// batch 362 -> 348 us; the same split in GEMM2 and the MX GEMM1, whose
+// compute is short, cost them 1-4%.)
+template <int MODE, int BM, bool G1, typename ISS>
 __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t* ws, const int (&tiles)[4], int wt,
                                              int kb, float sw0, float sw1, int mv,
-                                             v4f (&acc)[Ring<MODE, BM>::MT][4]) {
+                                             v4f (&acc)[Ring<MODE, BM>::MT][4], ISS&& iss) {
   using R = Ring<MODE, BM>;
+  constexpr bool SPREAD = f16_path(MODE) && Ring<MODE, BM>::MT == 4;
+  if constexpr (!SPREAD) iss(-1);  // (a no-op: the caller issued them)
   const int lane = threadIdx.x & 63;
   const uint8_t* wl = slot + R::W_OFF + lane * 16;
   const uint8_t* tt = slot + R::T_OFF + wt * R::MT * R::TILE;  // the wave's MT token tiles
@@ -386,7 +409,14 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
       // inside this schedule costs more than the skipped tiles save, and a
       // second, partial schedule beside it does not fit the register budget.
       // A wave whose token tiles are all padding skips the K block.
-      if (mv == 0) return;
+      if (mv == 0) {
+        iss(-1);
+        return;
+      }
+      // weights before the tiles, tokens and scales two tile steps in (the
+      // addresses then leave the registers before the schedule's peak)
+      iss(0);
+      iss(1);
       v8i wraw[4], traw[4];
       wraw[0] = lds_frag32(wl + tiles[0] * R::TILE);
       wraw[1] = lds_frag32(wl + tiles[1] * R::TILE);
@@ -408,6 +438,10 @@ __device__ __forceinline__ void ring_compute(const uint8_t* slot, const uint8_t*
 #pragma unroll
       for (int g = 0; g < 16; ++g) {
         const int j = kW[g], m = kT[g];
+        if (g == 2) {
+          iss(2);
+          iss(3);
+        }
         v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < 4; ++k) c = mfma_f16(wh[j][k], th[m][k], c);
@@ -904,13 +938,21 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
   // to 4 K blocks that starts at K block kb (kb % 4 == 0) goes to
   // ws_buf[group count % NWS] with the loads of that K block
   int i_ii = 0, i_kb = 0, i_grp = 0, i_kbi = item_kbs(0), i_sub = 0;
-  auto issue_next = [&](auto slot_c, int s) __attribute__((always_inline)) {
+  // the issue cursor's K block: issue_prep picks its MX weight-scale group
+  // buffer, issue_part issues load group `part` (-1: all) into slot_c,
+  // issue_step moves the cursor on
+  const uint8_t* i_ws = nullptr;
+  auto issue_prep = [&]() __attribute__((always_inline)) {
+    i_ws = nullptr;
+    if constexpr (MODE == kGemmMx) {
+      if (i_ii < n_my && (i_kb & 3) == 0) i_ws = ws_buf[(i_grp++) % NWS];
+    }
+  };
+  auto issue_part = [&](auto slot_c, int part) __attribute__((always_inline)) {
+    if (i_ii < n_my) ring_issue<MODE, BM>(rs, slot(slot_c), wave, i_kb, i_ws, part);
+  };
+  auto issue_step = [&](int s) __attribute__((always_inline)) {
     if (i_ii < n_my) {
-      const uint8_t* ws = nullptr;
-      if constexpr (MODE == kGemmMx) {
-        if ((i_kb & 3) == 0) ws = ws_buf[(i_grp++) % NWS];
-      }
-      ring_issue<MODE, BM>(rs, slot(slot_c), wave, i_kb, ws);
       if (++i_kb == i_kbi) {
         i_kb = 0;
         if (++i_sub < NTG) {
@@ -925,6 +967,11 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
     }
     // past the end of the stream nothing is issued: the waits of the last
     // S-2 steps count only the slots that exist
+  };
+  auto issue_next = [&](auto slot_c, int s) __attribute__((always_inline)) {
+    issue_prep();
+    issue_part(slot_c, -1);
+    issue_step(s);
   };
 
   // prologue: metadata of item 0, then K blocks 0 .. S-2 of the stream
@@ -953,12 +1000,25 @@ __global__ __launch_bounds__(ring_waves(MODE, BM) * 64) void moe_gemm_stream_ker
       sw1 = sc.y;
     }
     if (s == wts_step) issue_wts(wts_item);
-    issue_next(std::integral_constant<int, (d + S - 1) % S>{}, s);
+    // the loads of K block s + S - 1: in two groups during the compute of the
+    // scheduled f16 path (ring_compute), else all of them first
+    constexpr bool split = f16_path(MODE) && MT == 4;
+    auto iss = [&](int part) __attribute__((always_inline)) {
+      if constexpr (split) issue_part(std::integral_constant<int, (d + S - 1) % S>{}, part);
+    };
+    if constexpr (split)
+      issue_prep();
+    else
+      issue_next(std::integral_constant<int, (d + S - 1) % S>{}, s);
     if constexpr (MODE == kGemmMx) {
       if ((c_kb & 3) == 0) c_ws = ws_buf[(c_grp++) % NWS];
     }
     if (active && c_mv > 0)
-      ring_compute<MODE, BM, G1>(slot(std::integral_constant<int, d>{}), c_ws, tiles, wt, c_kb, sw0, sw1, c_mv, acc);
+      ring_compute<MODE, BM, G1>(slot(std::integral_constant<int, d>{}), c_ws, tiles, wt, c_kb, sw0, sw1, c_mv, acc,
+                                 iss);
+    else
+      iss(-1);
+    if constexpr (split) issue_step(s);
     if (++c_kb == c_kbi) {
       const int32_t* ids = ids_lds[c_ii % NB];
       if constexpr (G1) {
