@@ -666,7 +666,9 @@ __device__ __forceinline__ void epilogue_gemm1_tail(const GemmArgs& p, const v4f
 // (wt*MT + m)*16 + l%16, columns 64*wn + 16*j + 4*(l/16) + i of the N tile,
 // so a row's 64-column group is the wave's and its 4 lanes (l/16 = 0..3)
 // share the group's largest |v| through two lane exchanges; that maximum is
-// |w| * max|C| (rounding is monotonic).  |v| * 2^-s < 2^15, so only a
+// |w| * max|C| (rounding is monotonic).  Within a group the values are stored
+// in lane order (y_group_col): lane l's 16 values, (j, i) in order, fill
+// positions 16*(l/16) .. +16, two 16-byte stores per token tile.  |v| * 2^-s < 2^15, so only a
 // value that rounds to 2^15 saturates (to 32767), and v' = q * 2^s is within
 // 2^s <= 2^-14 max|v| of v.  Routing weights come from LDS.  y holds the
 // columns of this launch's N tiles (from nt0); a K piece writes its own
@@ -695,15 +697,18 @@ __device__ __forceinline__ void epilogue_gemm2_s(const GemmArgs& p, const v4f (&
       // floor(log2 mx) from the exponent field (subnormals included)
       const int e = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) - 1 : 0;
       const int sx = max(e - 14, -128);
-      int16_t* yrow = (int16_t*)plane + (int64_t)s * p.ldy + col0 + 4 * q;
+      int16_t* ygrp = (int16_t*)plane + (int64_t)s * p.ldy + col0 + 16 * q;
+      uint32_t pk[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         int qv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) qv[i] = (int)__builtin_rintf(ldexpf(w * acc[m][j][i], -sx));
-        *(uint2*)(yrow + 16 * j) = make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(qv[0], qv[1])),
-                                              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(qv[2], qv[3])));
+        pk[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(qv[0], qv[1]));
+        pk[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pk_i16(qv[2], qv[3]));
       }
+      *(uint4*)ygrp = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      *(uint4*)(ygrp + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
       if (q == 0) ((int8_t*)(plane + p.yexp))[(int64_t)s * (p.ldy / 64) + col0 / 64] = (int8_t)sx;
     }
   }
@@ -1440,19 +1445,22 @@ hipError_t launch_gemm1_tail_finish(int mode, int ks, int block_m, const float* 
 // order j = 0..k-1 (with K pieces: plane by plane, slots in order within
 // each), for h < cols (a column chunk of the output).  Each y value is
 // decoded exactly, q * 2^s (int16 q, the exponent of its 64-column group).
-// 8 columns per thread (one 16-byte non-temporal load per slot: y is read
-// once); the 8 bf16 results go out as one 16-byte store when the row stride
-// allows it.  Columns h .. h+7 lie in one 64-column group and inside the y
-// rows GEMM2 wrote (the chunk width is a multiple of 256, or all Hp); only
-// those below `cols` are stored.
+// 8 stored values per thread (one 16-byte non-temporal load per slot: y is
+// read once): positions p .. p+7 of a 64-column group, which hold output
+// columns y_group_col(p) .. +3 and 16 further .. +3; each four bf16 results
+// go out as one 8-byte store when the row stride allows it.  The group lies
+// inside the y rows GEMM2 wrote (the chunk width is a multiple of 256, or all
+// Hp); only columns below `cols` are stored.
 template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict__ y, int64_t yexp, int k, int cols,
                                                       int64_t ldy, int nplanes, int64_t plane,
                                                       uint16_t* __restrict__ out, int64_t ld_out, int vec_store) {
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
   const int t = blockIdx.y;
+  // stored positions h .. h+7 of a row: output columns c and c + 16 (4 each)
   const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (h >= cols) return;
+  if ((h & ~63) >= cols) return;
+  const int c = y_group_col(h);
   const int64_t lde = ldy / 64;
   float a[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   // plane by plane (K pieces of GEMM2); in a plane every slot's loads are
@@ -1482,16 +1490,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint8_t* __restrict_
       }
     }
   }
-  uint16_t* o = out + (int64_t)t * ld_out + h;
-  if (vec_store && h + 8 <= cols) {
-    uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(a[2 * i]) | ((uint32_t)f32_to_bf16(a[2 * i + 1]) << 16);
-    *(uint4*)o = make_uint4(w[0], w[1], w[2], w[3]);
-  } else {
+  for (int half = 0; half < 2; ++half) {
+    const int c0 = c + 16 * half;
+    uint16_t* o = out + (int64_t)t * ld_out + c0;
+    const float* av = a + 4 * half;
+    if (vec_store && c0 + 4 <= cols) {
+      *(uint2*)o = make_uint2((uint32_t)f32_to_bf16(av[0]) | ((uint32_t)f32_to_bf16(av[1]) << 16),
+                              (uint32_t)f32_to_bf16(av[2]) | ((uint32_t)f32_to_bf16(av[3]) << 16));
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (h + i < cols) o[i] = f32_to_bf16(a[i]);
+      for (int i = 0; i < 4; ++i)
+        if (c0 + i < cols) o[i] = f32_to_bf16(av[i]);
+    }
   }
 }
 
@@ -1499,8 +1510,8 @@ hipError_t launch_combine(const uint8_t* y, int64_t yexp, int T, int k, int c0, 
                           int64_t plane, uint16_t* out, int64_t ld_out, hipStream_t s) {
   if (T <= 0 || cols <= 0) return hipSuccess;
   uint16_t* o = out + c0;
-  // 16-byte stores need every row start 16-byte aligned
-  const int vec = ((uintptr_t)o % 16 == 0) && (ld_out % 8 == 0);
+  // 8-byte stores need every row start 8-byte aligned
+  const int vec = ((uintptr_t)o % 8 == 0) && (ld_out % 4 == 0);
   dim3 grid((unsigned)((cols + 2047) / 2048), (unsigned)T), block(256);
   if (k <= 2)
     hipLaunchKernelGGL(combine_kernel<2>, grid, block, 0, s, y, yexp, k, cols, ldy, nplanes, plane, o, ld_out, vec);

@@ -166,7 +166,13 @@ hipError_t launch_swiglu_requant(int mode, const float* part, int ks, int P, int
 // differs from v by at most 2^(s-1) (2^-15 of the group's largest |v|), or
 // 2^s where the largest value rounds to 2^15 and saturates.  The combine
 // decodes exactly and sums in fp32.  Half the bytes of fp32 rows, for the
-// two passes over them.
+// two passes over them.  Within each 64-column group the values are stored
+// in GEMM2's lane order: position 16q + 4j + i holds column 16j + 4q + i
+// (y_group_col), so each lane of GEMM2 writes 32 contiguous bytes.
+__host__ __device__ inline int y_group_col(int pos) {
+  const int u = pos & 63;
+  return (pos & ~63) + 16 * ((u >> 2) & 3) + 4 * (u >> 4) + (u & 3);
+}
 inline int64_t y_values_bytes(int64_t pairs, int64_t cols) { return (pairs * cols * 2 + 255) / 256 * 256; }
 inline int64_t y_plane_bytes(int64_t pairs, int64_t cols) {
   return y_values_bytes(pairs, cols) + (pairs * (cols / 64) + 255) / 256 * 256;
