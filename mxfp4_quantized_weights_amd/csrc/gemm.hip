@@ -1323,8 +1323,10 @@ hipError_t launch_swiglu_requant(int mode, const float* part, int ks, int P, int
 // rounds, the numbering of the GEMM kernel): per row, the KS pieces' fp32
 // partial sums added in piece order, then the clamped SwiGLU and the
 // re-quantisation of epilogue_gemm1_s for the N tile's 128 intermediate
-// columns; pad rows get zero codes and scales.  32 threads per row (4
-// columns each), 8 rows at a time.
+// columns; pad rows get zero codes and scales.  Workgroup (r, c) takes rows
+// 16c .. 16c+15 of the block: 32 threads per row (4 columns each), 8 rows at
+// a time (one workgroup per 16 rows, so that a large block's partial sums
+// are read by many compute units).
 template <int QMODE, int KS, int BM>
 __global__ __launch_bounds__(256) void gemm1_tail_finish_kernel(const float* __restrict__ part,
                                                                 const int32_t* __restrict__ sorted_ids,
@@ -1337,7 +1339,8 @@ __global__ __launch_bounds__(256) void gemm1_tail_finish_kernel(const float* __r
   if (!tail_split_on(items, W) || r >= items - F * W) return;
   const int g = F * W + r, m = g / n_tiles, nt = g % n_tiles;
   const int c = (threadIdx.x & 31) * 4;  // intermediate column within the N tile
-  for (int t = threadIdx.x >> 5; t < BM; t += 8) {
+  const int t_end = min(BM, 16 * ((int)blockIdx.y + 1));
+  for (int t = 16 * blockIdx.y + (threadIdx.x >> 5); t < t_end; t += 8) {
     const int64_t row = (int64_t)m * BM + t;
     const bool real = sorted_ids[row] < P;
     float a[4];
@@ -1398,7 +1401,7 @@ __global__ __launch_bounds__(256) void gemm1_tail_finish_kernel(const float* __r
 template <int QMODE, int BM>
 static void launch_tail_finish_bm(int ks, const float* part, const int32_t* sorted, const int32_t* npp, int n_tiles,
                                   int W, int P, int Ip, float limit, uint8_t* aq, void* as, hipStream_t s) {
-  const dim3 grid((unsigned)W), block(256);
+  const dim3 grid((unsigned)W, (unsigned)((BM + 15) / 16)), block(256);
   switch (ks) {
     case 2:
       hipLaunchKernelGGL((gemm1_tail_finish_kernel<QMODE, 2, BM>), grid, block, 0, s, part, sorted, npp, n_tiles, W,
