@@ -18,7 +18,9 @@ the same kernels, called through the stage entry points) with the attainable
 ceiling min(peak, intensity x HBM bandwidth), the CPU oracle's throughput on
 a bounded sample of the same workload, and (unless --no-extras) the decode
 (T = 64) and MXFP4 (T = 4096) layers measured the same way, plus the decode
-layer at T = 1 .. 64 replayed from a HIP graph, as extra keys.
+layer at T = 1 .. 64 replayed from a HIP graph, as extra keys, and what the
+part itself delivers beside the published peaks (a read stream's and a device
+copy's GB/s, each MFMA instruction's TFLOP/s: `box_measured`).
 """
 from __future__ import annotations
 
@@ -72,6 +74,46 @@ def copy_calibration(mib: int):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_dispatch": n * 4}), flush=True)
+
+
+def box_measured(M):
+    """What this part delivers beside the published peaks: a 2 GiB read with the
+    GEMMs' kind of load (the library's stream diagnostic), a 1 GiB device copy
+    (read + write bytes over its time; medians of 5) and each matrix-core
+    instruction the GEMMs use, from the library's rate diagnostic (8
+    independent accumulator chains per wave, 4 waves per SIMD, no memory
+    traffic; median of 3 launches of ~3 ms)."""
+    import torch
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+
+    def med_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    copy_gbs = 2 * n * 4 / (med_ms(lambda: b.copy_(a), 5) * 1e-3) / 1e9
+    del b
+    big = torch.ones(2 * n, dtype=torch.float32, device="cuda")   # 2 GiB, read once per launch
+    read_gbs = big.numel() * 4 / (med_ms(lambda: M.moe_diag_stream_read(big), 5) * 1e-3) / 1e9
+    del a, big
+    sink = torch.empty(M.DIAG_MFMA_RATE_WORKGROUPS * 256, dtype=torch.float32, device="cuda")
+    tflops = {}
+    for kind, name, iters in ((0, "f16_16x16x32", 12000), (1, "fp8_16x16x128", 6000), (2, "fp4_16x16x128", 12000)):
+        flop = M.DIAG_MFMA_RATE_WORKGROUPS * 4 * iters * 8 * M.DIAG_MFMA_RATE_FLOP[kind]
+        ms = med_ms(lambda: M.moe_diag_mfma_rate(kind, iters, sink), 3)
+        tflops[name] = round(flop / (ms * 1e-3) / 1e12, 1)
+    return {"read_gbs": round(read_gbs, 1), "copy_gbs": round(copy_gbs, 1), "mfma_tflops": tflops,
+            "spec": {"hbm_gbs": HBM_PEAK_GBS, "f16_tflops": 2500.0, "fp8_tflops": 5000.0, "fp4_tflops": 10100.0}}
 
 
 def algorithmic_bytes(wl, ids, M):
@@ -460,6 +502,7 @@ def main():
         m, _, _, _ = measure(M, W.WORKLOADS["prefill_mxfp4"], args, breakdown=not args.no_breakdown, block_m=0)
         extras["prefill_mxfp4"] = m
         res["extra"] = extras
+        res["box_measured"] = box_measured(M)
     print(json.dumps(res), flush=True)
 
 

@@ -384,6 +384,33 @@ moe_status_t moe_forward(const moe_cfg_t* cfg, int32_t T, const void* x_bf16, in
  * the two matrix-core sums with an exact one. */
 moe_status_t moe_diag_mfma_tile(int32_t kind, const void* a, const void* b, float* out, void* stream);
 
+/* Diagnostic (not part of the layer): the matrix-core throughput of one
+ * instruction, for pricing the GEMMs against what the part delivers beside
+ * its published peak.  One launch of MOE_DIAG_MFMA_RATE_WORKGROUPS workgroups
+ * of 4 waves (4 per CU on a 256-CU MI355X), each wave running `iters` rounds
+ * of 8 independent accumulator chains with no memory traffic:
+ *   kind 0: 16x16x32 f16 MFMA (16384 FLOP each; GEMM1's block-FP8 path),
+ *   kind 1: 16x16x128 FP8 MFMA (65536 FLOP; GEMM2),
+ *   kind 2: 16x16x128 FP4 MFMA (65536 FLOP; the MXFP4 GEMMs).
+ * FLOPs per launch = WORKGROUPS * 4 * iters * 8 * (FLOP each); the caller
+ * times the launch on `stream`.  out: device f32 [WORKGROUPS * 256], written
+ * (a sink for the accumulators).  MOE_ERR_UNSUPPORTED for another kind or
+ * iters < 1, MOE_ERR_NULL for out == NULL. */
+#define MOE_DIAG_MFMA_RATE_WORKGROUPS 1024
+moe_status_t moe_diag_mfma_rate(int32_t kind, int32_t iters, float* out, void* stream);
+
+/* Diagnostic (not part of the layer): the HBM read rate this part reaches
+ * with the GEMMs' kind of load (16-byte non-temporal loads, coalesced, four in
+ * flight per lane, a contiguous share per workgroup), for pricing their weight
+ * streams beside the published peak.  One launch of MOE_DIAG_STREAM_WORKGROUPS
+ * workgroups of 512 threads reads `bytes` bytes of device memory at src
+ * (16-byte aligned, a multiple of 16) once; the caller times it on `stream`.
+ * sink: device u32 [WORKGROUPS * 512], written with a checksum of the data.
+ * MOE_ERR_NULL, MOE_ERR_SHAPE (bytes < 0) and MOE_ERR_ALIGN before any
+ * launch. */
+#define MOE_DIAG_STREAM_WORKGROUPS 256
+moe_status_t moe_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Size of the scratch that moe_forward_noalloc keeps in a static device
  * array: 128 MiB, held on every GPU the library runs on until the process
  * ends.  It covers moe_workspace_bytes(cfg, T) for decode batches, e.g. up to

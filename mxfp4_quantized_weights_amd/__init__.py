@@ -98,6 +98,8 @@ _SIGS = {
                                                         _I32, _P, _SZ, _P]),
     "moe_forward_noalloc": (ctypes.c_int, [_CFGP, _I32, _P, _I64, _P, _P, _P, _P, _P, _P, _I64, _P]),
     "moe_diag_mfma_tile": (ctypes.c_int, [_I32, _P, _P, _P, _P]),
+    "moe_diag_mfma_rate": (ctypes.c_int, [_I32, _I32, _P, _P]),
+    "moe_diag_stream_read": (ctypes.c_int, [_P, _I64, _P, _P]),
     "moe_decode_supported": (_I32, [_CFGP, _I32]),
     "moe_decode_gemm1_swiglu": (ctypes.c_int, [_CFGP, _I32, _P, _P, _P, _P, _P, _P, _P]),
     "moe_decode_gemm2_combine": (ctypes.c_int, [_CFGP, _I32, _P, _P, _P, _P, _P, _P, _I64, _P, _P, _P]),
@@ -459,6 +461,37 @@ def moe_diag_mfma_tile(kind: int, a: torch.Tensor, b: torch.Tensor, stream=None)
     _check(_lib.moe_diag_mfma_tile(kind, _dev(a, torch.uint8, "a"), _dev(b, torch.uint8, "b"), out.data_ptr(),
                                    _stream(stream)), "moe_diag_mfma_tile")
     return out
+
+
+# moe_diag_mfma_rate: workgroups of 4 waves per launch (MOE_DIAG_MFMA_RATE_WORKGROUPS)
+# and FLOP per instruction of each kind (f16 16x16x32, FP8 and FP4 16x16x128)
+DIAG_MFMA_RATE_WORKGROUPS = 1024
+DIAG_MFMA_RATE_FLOP = (16384, 65536, 65536)
+
+
+def moe_diag_mfma_rate(kind: int, iters: int, sink: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Diagnostic: one launch of the matrix-core rate loop (kind 0 f16, 1 FP8,
+    2 FP4; ``iters`` rounds of 8 MFMAs per wave) on ``stream``; the caller times
+    it.  FLOPs per launch: DIAG_MFMA_RATE_WORKGROUPS * 4 * iters * 8 *
+    DIAG_MFMA_RATE_FLOP[kind].  -> the f32 sink the kernel writes."""
+    if sink is None:
+        sink = torch.empty(DIAG_MFMA_RATE_WORKGROUPS * 256, dtype=torch.float32, device="cuda")
+    _check(_lib.moe_diag_mfma_rate(kind, iters, sink.data_ptr(), _stream(stream)), "moe_diag_mfma_rate")
+    return sink
+
+
+DIAG_STREAM_WORKGROUPS = 256    # of 512 threads
+
+
+def moe_diag_stream_read(src: torch.Tensor, sink: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Diagnostic: one launch that reads every byte of ``src`` (contiguous device
+    memory, 16-byte aligned, a multiple of 16 bytes) with the GEMMs' kind of
+    load, on ``stream``; the caller times it.  -> the u32 checksum sink (int32)."""
+    if sink is None:
+        sink = torch.empty(DIAG_STREAM_WORKGROUPS * 512, dtype=torch.int32, device=src.device)
+    _check(_lib.moe_diag_stream_read(_dev(src, None, "src"), src.numel() * src.element_size(), sink.data_ptr(),
+                                     _stream(stream)), "moe_diag_stream_read")
+    return sink
 
 
 class ExpertWeights:

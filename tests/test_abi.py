@@ -466,3 +466,22 @@ def test_mfma_results_read_after_their_wait_states(tmp_path):
                         break                         # an MFMA in between outlasts the wait
                     ws += 1
     assert checked > 100
+
+
+def test_mfma_rate_diagnostic_rejects_bad_arguments_before_any_launch():
+    lib = M.lib()
+    sink = ctypes.c_void_p(16)  # never dereferenced: the checks come first
+    assert lib.moe_diag_mfma_rate(3, 1, sink, None) == UNSUP
+    assert lib.moe_diag_mfma_rate(-1, 1, sink, None) == UNSUP
+    assert lib.moe_diag_mfma_rate(0, 0, sink, None) == UNSUP
+    assert lib.moe_diag_mfma_rate(0, 1, None, None) == NULL
+
+
+def test_stream_diagnostic_rejects_bad_arguments_before_any_launch():
+    lib = M.lib()
+    p16 = ctypes.c_void_p(256)  # never dereferenced: the checks come first
+    assert lib.moe_diag_stream_read(None, 16, p16, None) == NULL
+    assert lib.moe_diag_stream_read(p16, 16, None, None) == NULL
+    assert lib.moe_diag_stream_read(p16, -16, p16, None) == SHAPE
+    assert lib.moe_diag_stream_read(ctypes.c_void_p(264), 16, p16, None) == ALIGN
+    assert lib.moe_diag_stream_read(p16, 24, p16, None) == ALIGN

@@ -86,3 +86,30 @@ def test_random_tiles_error_statistics():
     log(f"  over 24 tiles: f16 path max {worst16 / U32:.2f} u of sum|ab|; FP8 MFMA max {worst8 / U32:.1f} u, "
         f"median {np.median(med8) / U32:.1f} u")
     assert worst16 <= 4 * U32
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2])
+def test_mfma_rate_diagnostic_runs(kind):
+    # the rate loop of each instruction runs to completion and leaves finite
+    # sums in its sink (its timing is bench.py's business)
+    sink = M.moe_diag_mfma_rate(kind, 16)
+    torch.cuda.synchronize()
+    s = sink.cpu().numpy()
+    assert s.shape == (M.DIAG_MFMA_RATE_WORKGROUPS * 256,)
+    assert np.isfinite(s).all()
+    log(f"mfma rate kind {kind}: sink sum {float(s.sum()):.4g}")
+
+
+@pytest.mark.parametrize("words", [4, 4 * 1001, 4 * (256 * 4 * 512 * 3 + 12345)])
+def test_stream_diagnostic_reads_every_word_once(words):
+    # the XOR of the per-thread checksums is the XOR of every 32-bit word of
+    # the buffer exactly when each 16-byte word is read once (one word; fewer
+    # words than workgroups; several unrolled rounds per workgroup with a
+    # ragged tail)
+    rng = np.random.default_rng(words)
+    host = rng.integers(-2**31, 2**31, size=words, dtype=np.int64).astype(np.int32)
+    src = torch.from_numpy(host).cuda()
+    sink = M.moe_diag_stream_read(src)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy())
+    assert got == np.bitwise_xor.reduce(host)
