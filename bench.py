@@ -502,7 +502,17 @@ def main():
         m, _, _, _ = measure(M, W.WORKLOADS["prefill_mxfp4"], args, breakdown=not args.no_breakdown, block_m=0)
         extras["prefill_mxfp4"] = m
         res["extra"] = extras
-        res["box_measured"] = box_measured(M)
+        box = res["box_measured"] = box_measured(M)
+        # each roofline's fraction of what this part measurably reaches: the
+        # read stream for HBM-bound kernels, the rate of the MFMA instruction
+        # the kernel runs (f16 for block FP8, FP4 for MXFP4) for MFMA-bound ones
+        for r in (res, extras["decode_fp8"], extras["prefill_mxfp4"]):
+            roof = r["roofline"]
+            if roof["bound"] == "hbm":
+                roof["frac_of_box_read"] = round(roof["achieved"] / box["read_gbs"], 4)
+            else:
+                inst = "fp4_16x16x128" if r["config"]["quant"] == "mxfp4" else "f16_16x16x32"
+                roof["frac_of_box_mfma"] = round(roof["achieved_tflops"] / box["mfma_tflops"][inst], 4)
     print(json.dumps(res), flush=True)
 
 
