@@ -414,8 +414,8 @@ moe_status_t moe_diag_stream_read(const void* src, int64_t bytes, uint32_t* sink
 /* Size of the scratch that moe_forward_noalloc keeps in a static device
  * array: 128 MiB, held on every GPU the library runs on until the process
  * ends.  It covers moe_workspace_bytes(cfg, T) for decode batches, e.g. up to
- * 730 tokens of the 288-expert top-8 block-FP8 layer with H = 4096, I = 1024
- * (block_m 16/32). */
+ * 793 tokens (block_m 16) or 731 (block_m 32) of the 288-expert top-8
+ * block-FP8 layer with H = 4096, I = 1024. */
 #define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
 
 /* moe_forward for callers that cannot allocate device memory: code under

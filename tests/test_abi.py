@@ -485,3 +485,13 @@ def test_stream_diagnostic_rejects_bad_arguments_before_any_launch():
     assert lib.moe_diag_stream_read(p16, -16, p16, None) == SHAPE
     assert lib.moe_diag_stream_read(ctypes.c_void_p(264), 16, p16, None) == ALIGN
     assert lib.moe_diag_stream_read(p16, 24, p16, None) == ALIGN
+
+
+def test_noalloc_scratch_covers_the_documented_decode_batches():
+    # the header's figures: 793 tokens at block_m 16 and 731 at block_m 32 of
+    # the 288-expert top-8 H = 4096, I = 1024 block-FP8 layer fit the static
+    # scratch, one more token does not
+    lim = 128 << 20
+    for bm, T in ((16, 793), (32, 731)):
+        c = M.make_cfg(288, 8, "fp8", 4096, 1024, block_m=bm)
+        assert M.workspace_bytes(c, T) <= lim < M.workspace_bytes(c, T + 1)
